@@ -1,0 +1,102 @@
+/*
+ * wc_oracle.h -- plain CPU oracle of the chunked byte-plane + rANS weight codec.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the slow, obviously-correct
+ * definition that the GPU path is checked against.  Only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it; the
+ * product path never does.  It shares no code, header, table or constant with
+ * the HIP library: every constant below is restated here on purpose.
+ *
+ * Sources (titles of the pages the method comes from):
+ *   - "SMEF -- blog companion code" README, file table: pass 3 splits each
+ *     tensor into sign / exponent / mantissa byte streams; pass 4 codes a
+ *     stream with a vectorised rANS coder.
+ *   - "weight-compression" README (Split12): BF16 is byte-split, the high byte
+ *     is reconstructed from a codebook, the low byte is kept raw, and the
+ *     bar is a bit-for-bit round trip.
+ *   - "PTWM" README, "How it works": exponent-plane separation by byte split;
+ *     "Configuration": large tensors coded as independently decodable chunks.
+ * The pages name rANS but fix none of its parameters.  This format fixes them
+ * (one reading of the pages, stated in full in wc_oracle.c).
+ *
+ * All functions are synchronous, single-purpose and take host pointers.
+ */
+#ifndef WC_ORACLE_H
+#define WC_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype codes */
+#define WCO_BF16 0
+#define WCO_FP32 1
+
+/* status codes */
+#define WCO_OK 0
+#define WCO_ERR_ARG 1
+#define WCO_ERR_CAPACITY 2
+#define WCO_ERR_CORRUPT 3
+
+/* corruption detail bits (OR-ed) */
+#define WCO_EF_BAD_TABLE 1u       /* frequency table does not sum to 4096 */
+#define WCO_EF_WORD_OVERRUN 2u    /* decoder wanted a word past the chunk payload */
+#define WCO_EF_BAD_FINAL_STATE 4u /* a lane did not end at the initial state */
+#define WCO_EF_BAD_TAIL 8u        /* unconsumed words or a non-zero pad word */
+#define WCO_EF_BAD_SEEK 16u       /* seek entries out of order, out of range or misaligned */
+
+typedef struct {
+    uint64_t n;                /* elements */
+    uint64_t num_chunks;       /* ceil(n / 65536) */
+    uint64_t raw_bytes;        /* bytes of the raw (uncoded) planes */
+    uint64_t table_bytes;      /* 512 per chunk */
+    uint64_t seek_bytes;       /* 8 * (chunks + 1) */
+    uint64_t payload_capacity; /* worst-case payload bytes */
+} wco_layout;
+
+int wco_query_layout(int dtype, uint64_t n, wco_layout *out);
+
+/* Plane split / merge (byte-plane transform). */
+void wco_split_bf16(const uint16_t *v, uint64_t n, uint8_t *hi, uint8_t *lo);
+void wco_merge_bf16(const uint8_t *hi, const uint8_t *lo, uint64_t n, uint16_t *v);
+/* FP32: exp coded; raw = sign bits (LSB-first, ceil(n/8) B) | m0 | m1 | m2. */
+void wco_split_fp32(const uint32_t *u, uint64_t n, uint8_t *exp, uint8_t *raw);
+void wco_merge_fp32(const uint8_t *exp, const uint8_t *raw, uint64_t n, uint32_t *u);
+
+/* One chunk. */
+void wco_histogram(const uint8_t *sym, uint32_t n, uint32_t counts[256]);
+void wco_normalize(const uint32_t counts[256], uint32_t total, uint16_t freq[256]);
+/* Encodes n (1..65536) symbols with table freq into out (capacity >= 128 +
+ * 2*n + 2).  Returns the chunk payload size in bytes. */
+uint32_t wco_encode_chunk(const uint8_t *sym, uint32_t n, const uint16_t freq[256], uint8_t *out);
+/* Decodes; returns 0 or WCO_EF_* bits.  Never reads outside p[0, size). */
+uint32_t wco_decode_chunk(const uint8_t *p, uint64_t size, const uint16_t freq[256], uint32_t n,
+                          uint8_t *sym);
+
+/* Whole tensor.  threads <= 1 runs on the calling thread; otherwise chunks
+ * are split into contiguous ranges over that many POSIX threads. */
+int wco_encode(int dtype, const void *in, uint64_t n, uint8_t *raw, uint16_t *tables,
+               uint64_t *seek, uint8_t *payload, uint64_t payload_capacity, int threads);
+int wco_decode(int dtype, const uint8_t *raw, const uint16_t *tables, const uint64_t *seek,
+               const uint8_t *payload, uint64_t payload_bytes, uint64_t n, void *out, int threads,
+               uint32_t *err_bits);
+
+/* Batches: tensor i is coded on its own; its chunks follow the previous
+ * tensor's in the tables, seek table and payload, and its raw planes start at
+ * raw_base[i] = previous raw_base + previous raw bytes, rounded up to 256. */
+int wco_plan_batch(int dtype, const uint64_t *n, uint32_t count, uint64_t *chunk_base,
+                   uint64_t *raw_base, wco_layout *total);
+int wco_encode_batch(int dtype, const void *const *in, const uint64_t *n, uint32_t count,
+                     uint8_t *raw, uint16_t *tables, uint64_t *seek, uint8_t *payload,
+                     uint64_t payload_capacity, int threads);
+int wco_decode_batch(int dtype, void *const *out, const uint64_t *n, uint32_t count,
+                     const uint8_t *raw, const uint16_t *tables, const uint64_t *seek,
+                     const uint8_t *payload, uint64_t payload_bytes, int threads,
+                     uint32_t *err_bits);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
