@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the lossless BF16 weight codec on one MI355X.
+
+One step = the whole hot path over one synthetic weight set already resident
+in HBM: batched encode (plane split + histogram + 12-bit table, chunked rANS
+encode, seek-table scan, compaction) followed by batched fused decode back to
+BF16.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "gpt2-small-bf16"
+STAGES = ["split_hist", "rans_encode", "scan", "compact"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU work for the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-check", action="store_true", help="skip the round-trip check before timing")
+    return p.parse_args()
+
+
+def cpu_baseline(w, xs, target_s):
+    """The oracle, as it stands, on a bounded sample of the same set."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    # calibrate on one tensor-sized piece
+    probe = xs[0][: min(xs[0].size, 4 * 65536)]
+    t = time.perf_counter()
+    e = oracle.encode(probe, w.dtype, threads=threads)
+    oracle.decode(e, threads=threads)
+    rate = probe.size / max(time.perf_counter() - t, 1e-6)  # elements / s, round trip
+    want = max(int(rate * target_s), 1)
+    sample, count = [], 0
+    for x in xs:
+        if count >= want and sample:
+            break
+        take = x if count + x.size <= 2 * want else x[: max(want - count, 65536)]
+        sample.append(take)
+        count += take.size
+    t_enc = t_dec = 0.0
+    nbytes = 0
+    for x in sample:
+        t = time.perf_counter()
+        e = oracle.encode(x, w.dtype, threads=threads)
+        t_enc += time.perf_counter() - t
+        t = time.perf_counter()
+        y, _ = oracle.decode(e, threads=threads)
+        t_dec += time.perf_counter() - t
+        assert np.array_equal(y, x)
+        nbytes += x.size * w.elem_bytes
+    total = t_enc + t_dec
+    return {
+        "value": nbytes / total / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {len(sample)} tensor(s) of {w.name}, {count} elements "
+                  f"({nbytes / 1e6:.1f} MB), encode + decode, {threads} threads",
+        "encode_GBps": nbytes / t_enc / 1e9,
+        "decode_GBps": nbytes / t_dec / 1e9,
+        "seconds": total,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the codec shards by "
+              "whole tensors with no exchange on decode, and no multi-GPU path is built here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lossless_weight_compression_bf16_amd as wc
+    from lossless_weight_compression_bf16_amd import _binding as B, codec, synthetic as S
+
+    wc.lib()
+    dev = torch.device("cuda:0")
+    w = S.workload(args.workload)
+    log(f"[bench] generating {w.name}: {len(w.shapes)} tensors, {w.n} elements")
+    t0 = time.perf_counter()
+    xs = S.set_bits(w)
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading")
+    ity = torch.int16 if w.dtype == "bf16" else torch.int32
+    nty = np.int16 if w.dtype == "bf16" else np.int32
+    ins = [torch.from_numpy(x.view(nty)).to(dev) for x in xs]
+    outs = [torch.empty_like(t) for t in ins]
+    ns = [t.numel() for t in ins]
+
+    h_in, tot = B.wc_plan_batch(w.dtype, ns)
+    h_out, _ = B.wc_plan_batch(w.dtype, ns)
+    for i in range(len(ins)):
+        h_in[i].ptr = ins[i].data_ptr()
+        h_out[i].ptr = outs[i].data_ptr()
+    d_in = codec.segments_to_device(h_in, len(ins), dev)
+    d_out = codec.segments_to_device(h_out, len(ins), dev)
+    raw = torch.empty(tot.raw_bytes, dtype=torch.uint8, device=dev)
+    tables = torch.empty(tot.num_chunks * 256, dtype=torch.int16, device=dev)
+    seek = torch.empty(tot.num_chunks + 1, dtype=torch.int64, device=dev)
+    payload = torch.empty(tot.payload_capacity, dtype=torch.uint8, device=dev)
+    scratch = torch.empty(tot.scratch_bytes, dtype=torch.uint8, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    enc_bufs = B.make_buffers(raw, tables, seek, payload, tot.payload_capacity)
+    stream = torch.cuda.current_stream()
+    C = int(tot.num_chunks)
+    n = int(tot.n)
+    raw_in_bytes = n * w.elem_bytes
+
+    K, W = args.steps, args.warmup
+    # per step: 5 stage events recorded inside wc_encode_batch, 2 around the decode
+    evs = [B.HipEvents(7) for _ in range(max(K, 1))]
+
+    def step(i=None):
+        sev = evs[i] if i is not None else None
+        B.wc_encode_batch(w.dtype, h_in, d_in, len(ins), enc_bufs, scratch, scratch.numel(), err,
+                          stream, sev)
+        if sev is not None:
+            sev.record(5, stream)
+        dec_bufs = B.make_buffers(raw, tables, seek, payload, payload_bytes)
+        B.wc_decode_batch(w.dtype, h_out, d_out, len(outs), dec_bufs, err, stream)
+        if sev is not None:
+            sev.record(6, stream)
+
+    payload_bytes = tot.payload_capacity
+    step()
+    torch.cuda.synchronize()
+    payload_bytes = int(seek[-1].item())
+    for _ in range(max(W - 1, 0)):
+        step()
+    torch.cuda.synchronize()
+    if int(err.item()):
+        raise RuntimeError(f"device error bits {int(err.item()):#x}")
+    if not args.no_check:
+        for a, b in zip(ins, outs):
+            if not torch.equal(a, b):
+                raise RuntimeError("round trip is not bit-exact")
+        log("[bench] round trip bit-exact")
+    compressed = int(raw.numel() + tables.numel() * 2 + seek.numel() * 8 + payload_bytes)
+    ratio = compressed / raw_in_bytes
+
+    # timed region
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / K
+    if int(err.item()):
+        raise RuntimeError(f"device error bits {int(err.item()):#x}")
+
+    stage_ms = {s: 0.0 for s in STAGES}
+    dec_ms = 0.0
+    for i in range(K):
+        for j, s in enumerate(STAGES):
+            stage_ms[s] += evs[i].elapsed_ms(j, j + 1) / K
+        dec_ms += evs[i].elapsed_ms(5, 6) / K
+    enc_ms = sum(stage_ms.values())
+
+    # algorithmic bytes (the minimum the method moves), per launch
+    side = payload_bytes + 512 * C + 8 * (C + 1)
+    raw_plane = int(tot.raw_bytes)
+    alg = {
+        "rans_decode": side + raw_plane + raw_in_bytes,           # read compressed + raw plane, write BF16
+        "encode_total": raw_in_bytes + raw_plane + side,          # read BF16, write raw plane + compressed
+        "split_hist": raw_in_bytes + raw_plane + 512 * C,
+        "rans_encode": raw_in_bytes + 512 * C + payload_bytes,
+        "compact": 2 * payload_bytes,
+    }
+    times = {"split_hist": stage_ms["split_hist"], "rans_encode": stage_ms["rans_encode"],
+             "scan": stage_ms["scan"], "compact": stage_ms["compact"], "rans_decode": dec_ms}
+    dominant = max(times, key=times.get)
+    dom_bytes = alg.get(dominant, 0)
+    dom_ms = times[dominant]
+    achieved = dom_bytes / (dom_ms / 1e3) / 1e9 if dom_ms > 0 else 0.0
+
+    kernels = {}
+    for k, t in times.items():
+        entry = {"ms": round(t, 5)}
+        if k in alg and t > 0:
+            entry["alg_GBps"] = round(alg[k] / (t / 1e3) / 1e9, 2)
+            entry["hbm_frac"] = round(alg[k] / (t / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)
+        kernels[k] = entry
+
+    result = {
+        "metric": "rANS decode/encode GB/s of BF16 weights + % HBM roofline; compression ratio",
+        "value": round(raw_in_bytes / (ms_step / 1e3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tensors": len(w.shapes), "elements": n,
+                   "raw_bytes": raw_in_bytes, "chunks": C, "weights": w.dtype},
+        "ratio": round(ratio, 5),
+        "encode_GBps": round(raw_in_bytes / (enc_ms / 1e3) / 1e9, 3),
+        "decode_GBps": round(raw_in_bytes / (dec_ms / 1e3) / 1e9, 3),
+        "decode_hbm_frac": round(alg["rans_decode"] / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "encode_hbm_frac": round(alg["encode_total"] / (enc_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernels": kernels,
+        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on host cores")
+        result["cpu_baseline"] = cpu_baseline(w, xs, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

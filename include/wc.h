@@ -1,0 +1,162 @@
+/*
+ * wc.h -- C ABI of the MI355X (gfx950) lossless weight codec.
+ *
+ * What it computes
+ * ----------------
+ * Lossless compression of BF16 / FP32 weight tensors by byte-plane split and
+ * rANS coding of the skewed plane:
+ *   - BF16 (weight-compression / Split12 README: "byte-split BF16, high byte
+ *     reconstructed from a codebook, low byte kept raw"): the high byte
+ *     (sign + exponent bits 7..1) is rANS coded; the low byte (exponent bit 0
+ *     + 7 mantissa bits) is stored raw.
+ *   - FP32 (SMEF README, pass 3: sign / exponent / mantissa byte streams):
+ *     the exponent byte is rANS coded; raw = sign bits packed LSB-first
+ *     (ceil(n/8) bytes), then mantissa bytes m0 = bits 0-7, m1 = bits 8-15,
+ *     m2 = bits 16-22, one byte per element each.
+ *   - The coded plane is cut into chunks of 65536 symbols that decode on their
+ *     own (PTWM README, "Configuration": independently decodable chunks).
+ *     Each chunk has a 256-entry 12-bit frequency table (sum 4096, largest-
+ *     remainder rounding, zero counts stay zero) and 32 interleaved 32-bit
+ *     rANS states (symbol j -> lane j mod 32), L = 2^16, 16-bit
+ *     renormalisation words stored in decode order.
+ *   - Chunk payload = 32 final states (u32 LE) + words (u16 LE) + one zero
+ *     word if the word count is odd.  seek[0] = 0, seek[k+1] = seek[k] +
+ *     payload size of chunk k (u64).  tables = 256 u16 per chunk.
+ * The result is bit-exact: decode(encode(x)) reproduces every bit pattern,
+ * NaN payloads, infinities, subnormals and -0 included (Split12 README: the
+ * bar is an exact round trip).
+ *
+ * Conventions
+ * -----------
+ * - Pointers named d_* are device pointers (HBM of the current device);
+ *   everything else is host memory.  The library allocates nothing, frees
+ *   nothing, and never synchronises: every call only validates its arguments
+ *   on the host and enqueues kernels on `stream`.  Calls on different streams
+ *   may run concurrently if their buffers do not overlap.
+ * - Alignment: tensors, raw planes, tables and payload 16 bytes; seek 8
+ *   bytes; scratch 256 bytes.  (torch allocations are 256-byte aligned.)
+ * - Sizes are in elements unless the name says bytes.  n <= 2^40.
+ * - Return codes report argument and launch errors only.  Data errors found
+ *   on the device (a corrupt stream, a payload buffer that is too small) are
+ *   OR-ed as WC_EF_* bits into *d_err, which the caller zeroes beforehand and
+ *   reads after the stream has synchronised.  d_err may be NULL, in which
+ *   case such errors are not reported.
+ * - For any input bytes, decode reads only inside the buffers it is given
+ *   (payload[seek[k], seek[k+1]) within payload_bytes, the tables and raw
+ *   planes of its own chunks) and writes only the output elements of its own
+ *   chunks.
+ */
+#ifndef WC_H
+#define WC_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { WC_BF16 = 0, WC_FP32 = 1 } wc_dtype;
+
+typedef enum {
+    WC_OK = 0,
+    WC_ERR_ARG = 1,      /* null / misaligned pointer, bad dtype, size out of range */
+    WC_ERR_CAPACITY = 2, /* a buffer is smaller than the layout requires */
+    WC_ERR_CORRUPT = 3,  /* (reserved for host-side checks) */
+    WC_ERR_HIP = 4       /* a kernel launch failed */
+} wc_status;
+
+/* Device error bits (OR-ed into *d_err). */
+#define WC_EF_BAD_TABLE 1u       /* a chunk's table does not sum to 4096 */
+#define WC_EF_WORD_OVERRUN 2u    /* decoding wanted more words than the chunk holds */
+#define WC_EF_BAD_FINAL_STATE 4u /* a lane did not return to the initial state */
+#define WC_EF_BAD_TAIL 8u        /* words left over, or a non-zero pad word */
+#define WC_EF_BAD_SEEK 16u       /* seek entries out of order, misaligned or past payload_bytes */
+#define WC_EF_CAPACITY 32u       /* encode: the payload did not fit payload_bytes */
+
+#define WC_CHUNK 65536u
+
+/* Sizes of every buffer for one tensor (or, from wc_plan_batch, a batch). */
+typedef struct {
+    uint64_t n;                /* elements */
+    uint64_t num_chunks;       /* ceil(n / 65536) (summed over a batch) */
+    uint64_t raw_bytes;        /* raw planes */
+    uint64_t table_bytes;      /* 512 * num_chunks */
+    uint64_t seek_bytes;       /* 8 * (num_chunks + 1) */
+    uint64_t payload_capacity; /* worst-case payload: 128 + 2 * (len + len % 2) per chunk */
+    uint64_t scratch_bytes;    /* encoder scratch */
+} wc_layout;
+
+/* Device buffers of one encoding.  For encode, payload_bytes is the payload
+ * buffer's capacity; for decode, the number of valid payload bytes
+ * (seek[num_chunks]). */
+typedef struct {
+    uint8_t *raw;
+    uint16_t *tables;
+    uint64_t *seek;
+    uint8_t *payload;
+    uint64_t payload_bytes;
+} wc_buffers;
+
+/* One tensor of a batch.  `ptr` is the device address of the tensor (input
+ * of encode, output of decode).  chunk_base / raw_base are filled by
+ * wc_plan_batch: tensor i's chunks follow tensor i-1's in the tables, seek
+ * table and payload; its raw planes start at raw_base (the previous tensor's
+ * raw end rounded up to 256 bytes). */
+typedef struct {
+    uint64_t ptr;
+    uint64_t n;
+    uint64_t chunk_base;
+    uint64_t raw_base;
+} wc_segment;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int wc_version(void);
+
+/* Human-readable name of a status code. */
+const char *wc_status_string(wc_status s);
+
+/* Layout of one tensor of n elements.  Pure host function. */
+wc_status wc_query_layout(wc_dtype dtype, uint64_t n, wc_layout *out);
+
+/* Fills chunk_base and raw_base of segs[0..nseg) (host array; ptr and n are
+ * read) and the batch's total layout.  Pure host function. */
+wc_status wc_plan_batch(wc_dtype dtype, wc_segment *segs, uint32_t nseg, wc_layout *total);
+
+/* Encode one tensor of n elements at d_in (BF16 as u16 patterns, FP32 as
+ * u32 patterns).  Writes out->raw (layout.raw_bytes), out->tables,
+ * out->seek and out->payload (at most out->payload_bytes; layout's
+ * payload_capacity always suffices).  d_scratch must hold
+ * layout.scratch_bytes.  stage_events may be NULL or point to 5 events that
+ * are recorded on `stream` before the split, after the split, after the rANS
+ * kernel, after the scan and after the compaction. */
+wc_status wc_encode(wc_dtype dtype, const void *d_in, uint64_t n, const wc_buffers *out,
+                    void *d_scratch, uint64_t scratch_bytes, uint32_t *d_err,
+                    hipStream_t stream, hipEvent_t *stage_events);
+
+/* Decode one tensor of n elements into d_out (u16 / u32 bit patterns). */
+wc_status wc_decode(wc_dtype dtype, const wc_buffers *in, uint64_t n, void *d_out,
+                    uint32_t *d_err, hipStream_t stream);
+
+/* Batched forms: one launch sequence over all chunks of all tensors.
+ * h_segs is the host copy of the planned segment array (for validation);
+ * d_segs holds the same bytes in device memory (read by the kernels).
+ * The scratch size is the batch layout's scratch_bytes. */
+wc_status wc_encode_batch(wc_dtype dtype, const wc_segment *h_segs, const wc_segment *d_segs,
+                          uint32_t nseg, const wc_buffers *out, void *d_scratch,
+                          uint64_t scratch_bytes, uint32_t *d_err, hipStream_t stream,
+                          hipEvent_t *stage_events);
+wc_status wc_decode_batch(wc_dtype dtype, const wc_segment *h_segs, const wc_segment *d_segs,
+                          uint32_t nseg, const wc_buffers *in, uint32_t *d_err,
+                          hipStream_t stream);
+
+/* Host-side self check of the exact division by reciprocal that the encoder
+ * kernel uses (same inline code, compiled for the CPU): every divisor
+ * 1..4096 against boundary and sampled dividends below 2^32.  Returns the
+ * number of wrong quotients (0 expected). */
+uint64_t wc_check_division(uint32_t samples_per_divisor);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

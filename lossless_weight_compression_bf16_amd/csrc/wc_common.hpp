@@ -1,0 +1,122 @@
+// wc_common.hpp -- constants and small device helpers of the gfx950 codec.
+//
+// Format constants (the pages name rANS but fix none of its parameters; these
+// are the format's own choices, restated in the public header wc.h):
+//   chunk = 65536 symbols, 32 interleaved u32 states per chunk, 12-bit
+//   frequency tables (M = 4096), state lower bound L = 2^16, 16-bit
+//   renormalisation words.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wc.h"
+
+namespace wc {
+
+constexpr uint32_t kChunk = 65536;
+constexpr uint32_t kLanes = 32;
+constexpr uint32_t kScaleBits = 12;
+constexpr uint32_t kM = 1u << kScaleBits;
+constexpr uint32_t kL = 1u << 16;
+constexpr uint32_t kMaxWords = kChunk;                  // at most one word per symbol
+constexpr uint64_t kSlotBytes = 128 + 2ull * kMaxWords;   // encoder scratch per chunk
+constexpr uint64_t kMaxElems = 1ull << 40;
+
+inline __host__ __device__ uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+inline __host__ __device__ uint64_t raw_bytes_of(int dtype, uint64_t n)
+{
+    return dtype == WC_BF16 ? n : (n + 7) / 8 + 3 * n;
+}
+
+// Device addresses held as integers (segment tables) are always global
+// memory; saying so lets the compiler emit global_* instead of flat_*
+// accesses, whose completion would otherwise also count against LDS waits.
+#define WC_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ inline WC_GLOBAL T *gptr(uint64_t a)
+{
+    return reinterpret_cast<WC_GLOBAL T *>(a);
+}
+template <typename T>
+__device__ inline WC_GLOBAL T *gptr(T *p)
+{
+    return reinterpret_cast<WC_GLOBAL T *>(reinterpret_cast<uint64_t>(p));
+}
+
+// Segment view handed to every kernel: either one inline tensor (nseg == 0)
+// or a device array of planned segments.
+struct SegTable {
+    const wc_segment *segs;
+    uint32_t nseg;
+    wc_segment single;
+};
+
+// The segment that owns global chunk k: the last one whose chunk_base <= k
+// (empty segments share their chunk_base with the next one and are skipped).
+__device__ inline wc_segment find_segment(const SegTable &st, uint64_t k)
+{
+    if (st.nseg == 0) return st.single;
+    uint32_t lo = 0, hi = st.nseg;
+    while (hi - lo > 1) {
+        uint32_t mid = (lo + hi) >> 1;
+        if (st.segs[mid].chunk_base <= k) lo = mid; else hi = mid;
+    }
+    return st.segs[lo];
+}
+
+// ---------------------------------------------------------------------------
+// Exact unsigned division by an invariant divisor d in [1, 4096] for any
+// 32-bit dividend: Granlund & Montgomery, "Division by Invariant Integers
+// using Multiplication" (PLDI 1994), the round-up method with an N+1-bit
+// multiplier (their Figure 4.1): l = ceil(log2 d),
+// m' = floor(2^32 (2^l - d) / d) + 1, sh1 = min(l, 1), sh2 = max(l - 1, 0),
+// q = (t1 + ((x - t1) >> sh1)) >> sh2 with t1 = mulhi(m', x).
+// gfx950 has no integer divide instruction; this is one mul_hi, a subtract,
+// an add and two shifts.
+// ---------------------------------------------------------------------------
+struct DivConst {
+    uint32_t mp;
+    uint32_t sh1;
+    uint32_t sh2;
+};
+
+inline __host__ __device__ DivConst div_const(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((1u << l) < d) l++;
+    DivConst c;
+    c.mp = (uint32_t)((((uint64_t)((1u << l) - d)) << 32) / d) + 1u;
+    c.sh1 = l < 1 ? l : 1;
+    c.sh2 = l > 1 ? l - 1 : 0;
+    return c;
+}
+
+inline __host__ __device__ uint32_t mulhi32(uint32_t a, uint32_t b)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __umulhi(a, b);
+#else
+    return (uint32_t)(((uint64_t)a * b) >> 32);
+#endif
+}
+
+inline __host__ __device__ uint32_t div_exact(uint32_t x, uint32_t mp, uint32_t sh1, uint32_t sh2)
+{
+    uint32_t t1 = mulhi32(mp, x);
+    return (t1 + ((x - t1) >> sh1)) >> sh2;
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront helpers (wave64).
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+__device__ inline uint32_t wave_sum(uint32_t v)
+{
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace wc

@@ -1,0 +1,396 @@
+// wc_encode.hpp -- encoder kernels for gfx950.
+//
+//   k_split_hist  one 256-thread block per chunk: coalesced 16-byte loads of
+//                 the tensor, raw planes written back with vector stores, the
+//                 coded plane counted into LDS sub-histograms, then the
+//                 chunk's 12-bit table built with integer arithmetic only.
+//   k_encode      one wavefront per two chunks (one chunk per 32-lane half):
+//                 32 interleaved rANS states, reverse order, words written
+//                 downwards into the chunk's scratch slot.
+//   k_scan        exclusive scan of the chunk sizes into the seek table.
+//   k_compact     moves every chunk's payload from its slot to its offset.
+#pragma once
+
+#include "wc_common.hpp"
+
+namespace wc {
+
+// ------------------------------------------------------------ block helpers
+// (256 threads = 4 wavefronts)
+
+__device__ inline uint32_t block_sum256(uint32_t v, uint32_t *red)
+{
+    const uint32_t w = threadIdx.x >> 6;
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    uint32_t r = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return r;
+}
+
+// Exclusive prefix count of a predicate over the block, in thread order.
+__device__ inline uint32_t block_rank256(bool p, uint32_t *red, uint32_t *total)
+{
+    const uint32_t w = threadIdx.x >> 6;
+    uint64_t m = __ballot(p);
+    uint32_t in_wave = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if ((threadIdx.x & 63) == 0) red[w] = (uint32_t)__popcll(m);
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+    for (uint32_t i = 0; i < 4; i++) {
+        uint32_t c = red[i];
+        off += i < w ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return off + in_wave;
+}
+
+// Normalises the chunk's counts to a 12-bit table.  Thread s holds count c
+// of symbol s; T is the chunk length.  Integer largest-remainder rounding:
+// f = floor(4096 c / T), at least 1 when c > 0; a positive shortfall D goes
+// +1 to the D regular symbols with the largest remainders (smaller symbol
+// first on ties); an excess E = -D is removed the way "take 1 from the
+// largest f, smaller symbol on ties" repeated E times would remove it,
+// computed in closed form: every f is cut to a level v+1 and the smallest
+// symbols at that level drop to v, where v is the largest level whose cut
+// removes at least E.
+__device__ inline uint32_t normalize256(uint32_t c, uint32_t T, uint32_t *red, uint32_t *keys)
+{
+    const uint32_t s = threadIdx.x;
+    const uint32_t scaled = c * kM;  // <= 2^28
+    const uint32_t q = scaled / T;
+    const uint32_t r = scaled - q * T;
+    const bool regular = q >= 1;
+    uint32_t f = c ? (regular ? q : 1u) : 0u;
+    const int32_t d = (int32_t)kM - (int32_t)block_sum256(f, red);
+
+    if (d > 0) {
+        uint32_t m;
+        uint32_t pos = block_rank256(regular, red, &m);
+        const uint32_t key = r * 256u + (255u - s);  // r < 65536: unique, fits 24 bits
+        if (regular) keys[pos] = key;
+        __syncthreads();
+        if (regular) {
+            uint32_t rank = 0;
+            for (uint32_t i = 0; i < m; i++) rank += keys[i] > key ? 1u : 0u;
+            if (rank < (uint32_t)d) f += 1;
+        }
+        __syncthreads();
+    } else if (d < 0) {
+        const uint32_t e = (uint32_t)(-d);
+        // cost(v) = sum max(f - v, 0) is non-increasing; cost(1) >= e and
+        // cost(4096) = 0 < e, so the largest v with cost(v) >= e is in [1, 4096).
+        uint32_t lo = 1, hi = kM;
+        while (hi - lo > 1) {
+            uint32_t mid = (lo + hi) >> 1;
+            uint32_t cost = block_sum256(f > mid ? f - mid : 0u, red);
+            if (cost >= e) lo = mid; else hi = mid;
+        }
+        const uint32_t v = lo;
+        const uint32_t cut = block_sum256(f > v + 1 ? f - (v + 1) : 0u, red);
+        const uint32_t left = e - cut;
+        const bool at = f >= v + 1;
+        uint32_t m;
+        uint32_t pos = block_rank256(at, red, &m);
+        if (at) f = pos < left ? v : v + 1;
+    }
+    return f;
+}
+
+// ------------------------------------------------------------ split + table
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__restrict__ raw,
+                                                    uint16_t *__restrict__ tables)
+{
+    constexpr int kCopies = 8;             // one sub-histogram per 32 threads
+    constexpr int kStride = 257;           // pad: copies land on different banks
+    __shared__ uint32_t hist[kCopies * kStride];
+    __shared__ uint32_t red[4];
+    __shared__ uint32_t keys[256];
+
+    const uint64_t k = blockIdx.x;
+    const wc_segment sg = find_segment(st, k);
+    const uint64_t start = (k - sg.chunk_base) * kChunk;
+    const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
+    const uint32_t tid = threadIdx.x;
+
+    for (uint32_t i = tid; i < kCopies * kStride; i += 256) hist[i] = 0;
+    __syncthreads();
+    uint32_t *my = hist + (tid >> 5) * kStride;
+
+    if constexpr (DT == WC_BF16) {
+        const uint16_t *in = reinterpret_cast<const uint16_t *>(sg.ptr) + start;
+        uint8_t *lo = raw + sg.raw_base + start;
+        const uint32_t ng = len / 8;
+        for (uint32_t g = tid; g < ng; g += 256) {
+            const uint4 v = reinterpret_cast<const uint4 *>(in)[g];
+            uint2 l;
+            l.x = __builtin_amdgcn_perm(v.y, v.x, 0x06040200u);
+            l.y = __builtin_amdgcn_perm(v.w, v.z, 0x06040200u);
+            reinterpret_cast<uint2 *>(lo)[g] = l;
+            const uint32_t h0 = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
+            const uint32_t h1 = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
+            atomicAdd(&my[h0 & 0xFF], 1u);
+            atomicAdd(&my[(h0 >> 8) & 0xFF], 1u);
+            atomicAdd(&my[(h0 >> 16) & 0xFF], 1u);
+            atomicAdd(&my[h0 >> 24], 1u);
+            atomicAdd(&my[h1 & 0xFF], 1u);
+            atomicAdd(&my[(h1 >> 8) & 0xFF], 1u);
+            atomicAdd(&my[(h1 >> 16) & 0xFF], 1u);
+            atomicAdd(&my[h1 >> 24], 1u);
+        }
+        for (uint32_t i = ng * 8 + tid; i < len; i += 256) {
+            const uint16_t e = in[i];
+            lo[i] = (uint8_t)(e & 0xFF);
+            atomicAdd(&my[e >> 8], 1u);
+        }
+    } else {
+        // FP32: exponent counted; raw = sign bits | m0 | m1 | m2 (plane bases
+        // follow the segment's element count).
+        const uint32_t *in = reinterpret_cast<const uint32_t *>(sg.ptr) + start;
+        const uint64_t sb = (sg.n + 7) / 8;
+        uint8_t *sign = raw + sg.raw_base + start / 8;
+        uint8_t *m0 = raw + sg.raw_base + sb + start;
+        uint8_t *m1 = m0 + sg.n;
+        uint8_t *m2 = m1 + sg.n;
+        const uint32_t ng = (len + 7) / 8;  // groups of 8 elements = one sign byte
+        for (uint32_t g = tid; g < ng; g += 256) {
+            uint32_t sbyte = 0;
+            for (uint32_t i = 0; i < 8; i++) {
+                const uint32_t j = 8 * g + i;
+                if (j >= len) break;
+                const uint32_t u = in[j];
+                atomicAdd(&my[(u >> 23) & 0xFF], 1u);
+                sbyte |= (u >> 31) << i;
+                m0[j] = (uint8_t)(u & 0xFF);
+                m1[j] = (uint8_t)((u >> 8) & 0xFF);
+                m2[j] = (uint8_t)((u >> 16) & 0x7F);
+            }
+            sign[g] = (uint8_t)sbyte;
+        }
+    }
+    __syncthreads();
+
+    uint32_t c = 0;
+    for (int i = 0; i < kCopies; i++) c += hist[i * kStride + tid];
+    const uint32_t f = normalize256(c, len, red, keys);
+    tables[k * 256 + tid] = (uint16_t)f;
+}
+
+// ------------------------------------------------------------------ encoder
+
+// Per-symbol encoder constants: reciprocal, renormalisation threshold,
+// (4096 - f) and the two shifts, cumulative start b.
+struct EncSym {
+    uint32_t mp;
+    uint32_t th;     // x > th  <=>  x >= f * 2^20 (renormalise first)
+    uint32_t fm_sh;  // (4096 - f) | sh1 << 16 | sh2 << 24
+    uint32_t b;
+};
+
+template <int DT>
+__device__ inline uint32_t load_elem(const void *base, uint64_t i)
+{
+    if constexpr (DT == WC_BF16) return reinterpret_cast<const uint16_t *>(base)[i];
+    else return reinterpret_cast<const uint32_t *>(base)[i];
+}
+
+template <int DT>
+__device__ inline uint32_t symbol_of(uint32_t e)
+{
+    if constexpr (DT == WC_BF16) return e >> 8;
+    else return (e >> 23) & 0xFF;
+}
+
+// One encode step for one lane: renormalise (emit the low 16 bits into the
+// word list, which grows downwards from index p) and push symbol s.
+template <bool CHECK>
+__device__ inline void enc_step(uint32_t &x, uint32_t &p, bool active, const EncSym &e,
+                                uint16_t *words, uint32_t h)
+{
+    const bool emit = (!CHECK || active) && x > e.th;
+    const uint64_t m = __ballot(emit);
+    const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(ml, 0u));
+    const uint32_t cl = __popc(ml), ch = __popc(mh);
+    p -= h ? ch : cl;
+    const uint32_t rank = below - (h ? cl : 0u);
+    if (emit) {
+        words[p + rank] = (uint16_t)(x & 0xFFFF);
+        x >>= 16;
+    }
+    if (!CHECK || active) {
+        const uint32_t q = div_exact(x, e.mp, (e.fm_sh >> 16) & 0xFF, e.fm_sh >> 24);
+        x = x + __umul24(q, e.fm_sh & 0xFFFF) + e.b;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__restrict__ tables,
+                                               uint8_t *__restrict__ slots, uint2 *__restrict__ meta,
+                                               uint64_t total_chunks)
+{
+    __shared__ EncSym enc[2][256];
+    const uint32_t lane = threadIdx.x & 31, h = threadIdx.x >> 5;
+    const uint64_t k = 2ull * blockIdx.x + h;
+    const bool valid = k < total_chunks;
+
+    wc_segment sg{0, 0, 0, 0};
+    uint64_t start = 0;
+    uint32_t len = 0;
+    if (valid) {
+        sg = find_segment(st, k);
+        start = (k - sg.chunk_base) * kChunk;
+        len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
+        // table: 8 symbols per lane, cumulative start by a scan over the half
+        const uint4 fv = reinterpret_cast<const uint4 *>(tables + k * 256)[lane];
+        uint32_t f[8] = {fv.x & 0xFFFF, fv.x >> 16, fv.y & 0xFFFF, fv.y >> 16,
+                         fv.z & 0xFFFF, fv.z >> 16, fv.w & 0xFFFF, fv.w >> 16};
+        uint32_t local = 0;
+        for (int i = 0; i < 8; i++) local += f[i];
+        uint32_t incl = local;
+        for (int o = 1; o < 32; o <<= 1) {
+            uint32_t v = __shfl_up(incl, o, 32);
+            if (lane >= (uint32_t)o) incl += v;
+        }
+        uint32_t b = incl - local;
+        for (int i = 0; i < 8; i++) {
+            EncSym e;
+            const uint32_t fi = f[i] ? f[i] : 1u;  // absent symbols are never encoded
+            const DivConst dc = div_const(fi);
+            e.mp = dc.mp;
+            e.th = (fi << 20) - 1u;  // wraps to 0xFFFFFFFF at f = 4096: never renormalise
+            e.fm_sh = (kM - fi) | (dc.sh1 << 16) | (dc.sh2 << 24);
+            e.b = b;
+            enc[h][8 * lane + i] = e;
+            b += f[i];
+        }
+    }
+    __syncthreads();
+
+    uint16_t *words = reinterpret_cast<uint16_t *>(slots + (valid ? k : 0) * kSlotBytes + 128);
+    const void *in = reinterpret_cast<const void *>(sg.ptr);
+    uint32_t x = kL;
+    uint32_t p = kMaxWords;
+
+    // the other half of the wavefront (chunk k ^ 1) decides whether the
+    // unchecked loop may run
+    const uint32_t other_len = __shfl_xor(len, 32, 64);
+    const bool full = len == kChunk && other_len == kChunk;
+    if (full) {
+        constexpr uint32_t G = 16;  // steps per group; symbols prefetched one group ahead
+        const uint64_t base = start + lane;
+        uint32_t cur[G], nxt[G];
+        uint32_t t0 = kChunk / kLanes - G;
+#pragma unroll
+        for (uint32_t i = 0; i < G; i++) cur[i] = load_elem<DT>(in, base + 32ull * (t0 + i));
+        for (;;) {
+            const bool more = t0 > 0;
+            if (more) {
+#pragma unroll
+                for (uint32_t i = 0; i < G; i++) nxt[i] = load_elem<DT>(in, base + 32ull * (t0 - G + i));
+            }
+#pragma unroll
+            for (int i = G - 1; i >= 0; i--) {
+                const EncSym e = enc[h][symbol_of<DT>(cur[i])];
+                enc_step<false>(x, p, true, e, words, h);
+            }
+            if (!more) break;
+            t0 -= G;
+#pragma unroll
+            for (uint32_t i = 0; i < G; i++) cur[i] = nxt[i];
+        }
+    } else {
+        const uint32_t steps = (len + kLanes - 1) / kLanes;
+        const uint32_t other = __shfl_xor(steps, 32, 64);
+        const uint32_t smax = steps > other ? steps : other;
+        for (uint32_t t = smax; t-- > 0;) {
+            const uint32_t j = t * kLanes + lane;
+            const bool active = valid && j < len;
+            const uint32_t s = active ? symbol_of<DT>(load_elem<DT>(in, start + j)) : 0u;
+            const EncSym e = enc[h][s];
+            enc_step<true>(x, p, active, e, words, h);
+        }
+    }
+
+    if (valid) {
+        reinterpret_cast<uint32_t *>(slots + k * kSlotBytes)[lane] = x;
+        if (lane == 0) {
+            const uint32_t nw = kMaxWords - p;
+            meta[k] = make_uint2(128u + 2u * nw + 2u * (nw & 1u), p);
+        }
+    }
+}
+
+// --------------------------------------------------------------------- scan
+
+__global__ __launch_bounds__(1024) void k_scan(const uint2 *__restrict__ meta, uint64_t total_chunks,
+                                               uint64_t *__restrict__ seek, uint64_t capacity,
+                                               uint32_t *err)
+{
+    __shared__ uint64_t wsum[16];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const uint64_t per = (total_chunks + 1023) / 1024;
+    const uint64_t b = min(total_chunks, per * tid), e = min(total_chunks, b + per);
+    uint64_t local = 0;
+    for (uint64_t i = b; i < e; i++) local += meta[i].x;
+    // inclusive scan in the wavefront, then across the 16 wavefronts
+    uint64_t incl = local;
+    for (int o = 1; o < 64; o <<= 1) {
+        uint64_t v = __shfl_up(incl, o, 64);
+        if (lane >= (uint32_t)o) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    uint64_t off = 0;
+    for (uint32_t i = 0; i < w; i++) off += wsum[i];
+    uint64_t run = off + incl - local;
+    if (tid == 0) seek[0] = 0;
+    for (uint64_t i = b; i < e; i++) {
+        run += meta[i].x;
+        seek[i + 1] = run;
+    }
+    if (tid == 1023) {
+        uint64_t total = 0;
+        for (int i = 0; i < 16; i++) total += wsum[i];
+        if (total > capacity && err) atomicOr(err, WC_EF_CAPACITY);
+    }
+}
+
+// ------------------------------------------------------------------ compact
+
+__global__ __launch_bounds__(256) void k_compact(const uint8_t *__restrict__ slots,
+                                                 const uint2 *__restrict__ meta,
+                                                 const uint64_t *__restrict__ seek,
+                                                 uint8_t *__restrict__ payload, uint64_t capacity)
+{
+    const uint64_t k = blockIdx.x;
+    const uint2 mk = meta[k];
+    const uint64_t dst_off = seek[k];
+    if (dst_off + mk.x > capacity) return;  // reported by the scan
+    const uint32_t p = mk.y, nw = kMaxWords - p, ndw = (nw + 1) / 2;
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(slots + k * kSlotBytes);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(payload + dst_off);
+    const uint32_t tid = threadIdx.x;
+    if (tid < 32) dst[tid] = src[tid];
+    const uint32_t *ws = src + 32;  // word area as dwords: word j is half (j & 1) of dword j / 2
+    for (uint32_t i = tid; i < ndw; i += 256) {
+        const uint32_t j = p + 2 * i;  // word that lands in the low half
+        uint32_t v;
+        if ((p & 1) == 0) {
+            v = ws[j >> 1];
+        } else {
+            v = ws[j >> 1] >> 16;
+            if (j + 1 < kMaxWords) v |= ws[(j + 1) >> 1] << 16;
+        }
+        if (2 * i + 1 >= nw) v &= 0xFFFFu;  // odd count: zero pad word
+        dst[32 + i] = v;
+    }
+}
+
+}  // namespace wc

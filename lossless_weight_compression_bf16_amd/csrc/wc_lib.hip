@@ -1,0 +1,254 @@
+// wc_lib.hip -- C ABI of the gfx950 lossless weight codec (see include/wc.h).
+//
+// Host side: argument validation, buffer layout, and the launch sequence
+//   encode: k_split_hist -> k_encode -> k_scan -> k_compact
+//   decode: k_decode
+// on the caller's stream.  No allocation, no synchronisation, no global state.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "wc.h"
+#include "wc_common.hpp"
+#include "wc_decode.hpp"
+#include "wc_encode.hpp"
+
+using namespace wc;
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+uint64_t chunk_capacity(uint64_t len) { return 128 + 2 * (len + (len & 1)); }
+
+void layout_of(int dtype, uint64_t n, wc_layout *out)
+{
+    const uint64_t c = (n + kChunk - 1) / kChunk;
+    out->n = n;
+    out->num_chunks = c;
+    out->raw_bytes = raw_bytes_of(dtype, n);
+    out->table_bytes = 512 * c;
+    out->seek_bytes = 8 * (c + 1);
+    out->payload_capacity = 0;
+    if (c) out->payload_capacity = (c - 1) * chunk_capacity(kChunk) + chunk_capacity(n - (c - 1) * kChunk);
+    out->scratch_bytes = 0;
+}
+
+uint64_t scratch_bytes_for(uint64_t chunks)
+{
+    return chunks ? align_up(8 * chunks, 256) + chunks * kSlotBytes : 0;
+}
+
+bool valid_dtype(int d) { return d == WC_BF16 || d == WC_FP32; }
+
+// Checks a batch's host segment array against the planning rule.
+wc_status check_plan(int dtype, const wc_segment *segs, uint32_t nseg, wc_layout *total, bool need_ptrs = true)
+{
+    uint64_t chunks = 0, raw = 0, cap = 0, elems = 0;
+    for (uint32_t i = 0; i < nseg; i++) {
+        const wc_segment &s = segs[i];
+        if (s.n > kMaxElems) return WC_ERR_ARG;
+        if (s.chunk_base != chunks || s.raw_base != raw) return WC_ERR_ARG;
+        if (need_ptrs && s.n && (s.ptr == 0 || (s.ptr % 16) != 0)) return WC_ERR_ARG;
+        wc_layout one;
+        layout_of(dtype, s.n, &one);
+        chunks += one.num_chunks;
+        raw += one.raw_bytes;
+        if (i + 1 < nseg) raw = align_up(raw, 256);
+        cap += one.payload_capacity;
+        elems += s.n;
+    }
+    total->n = elems;
+    total->num_chunks = chunks;
+    total->raw_bytes = raw;
+    total->table_bytes = 512 * chunks;
+    total->seek_bytes = 8 * (chunks + 1);
+    total->payload_capacity = cap;
+    total->scratch_bytes = scratch_bytes_for(chunks);
+    return WC_OK;
+}
+
+wc_status check_buffers(const wc_buffers *b, uint64_t chunks, uint64_t raw_bytes)
+{
+    if (!b || !b->seek || !aligned(b->seek, 8)) return WC_ERR_ARG;
+    if (chunks == 0) return WC_OK;
+    if (!b->tables || !aligned(b->tables, 16)) return WC_ERR_ARG;
+    if (!b->payload || !aligned(b->payload, 16)) return WC_ERR_ARG;
+    if (raw_bytes && (!b->raw || !aligned(b->raw, 16))) return WC_ERR_ARG;
+    return WC_OK;
+}
+
+template <int DT>
+wc_status encode_impl(const SegTable &st, uint64_t chunks, const wc_buffers *out, void *d_scratch,
+                      uint32_t *d_err, hipStream_t stream, hipEvent_t *ev)
+{
+    uint2 *meta = reinterpret_cast<uint2 *>(d_scratch);
+    uint8_t *slots = reinterpret_cast<uint8_t *>(d_scratch) + align_up(8 * chunks, 256);
+    if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return WC_ERR_HIP;
+    if (chunks) {
+        hipLaunchKernelGGL(k_split_hist<DT>, dim3((uint32_t)chunks), dim3(256), 0, stream, st, out->raw,
+                           out->tables);
+    }
+    if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return WC_ERR_HIP;
+    if (chunks) {
+        hipLaunchKernelGGL(k_encode<DT>, dim3((uint32_t)((chunks + 1) / 2)), dim3(64), 0, stream, st,
+                           out->tables, slots, meta, chunks);
+    }
+    if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return WC_ERR_HIP;
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, meta, chunks, out->seek, out->payload_bytes,
+                       d_err);
+    if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return WC_ERR_HIP;
+    if (chunks) {
+        hipLaunchKernelGGL(k_compact, dim3((uint32_t)chunks), dim3(256), 0, stream, slots, meta, out->seek,
+                           out->payload, out->payload_bytes);
+    }
+    if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return WC_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
+}
+
+template <int DT>
+wc_status decode_impl(const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err,
+                      hipStream_t stream)
+{
+    if (chunks == 0) return WC_OK;
+    hipLaunchKernelGGL(k_decode<DT>, dim3((uint32_t)((chunks + 1) / 2)), dim3(64), 0, stream, st, in->raw,
+                       in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err);
+    return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wc_version(void) { return kVersion; }
+
+const char *wc_status_string(wc_status s)
+{
+    switch (s) {
+    case WC_OK: return "ok";
+    case WC_ERR_ARG: return "invalid argument";
+    case WC_ERR_CAPACITY: return "buffer too small";
+    case WC_ERR_CORRUPT: return "corrupt stream";
+    case WC_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+wc_status wc_query_layout(wc_dtype dtype, uint64_t n, wc_layout *out)
+{
+    if (!out || !valid_dtype(dtype) || n > kMaxElems) return WC_ERR_ARG;
+    layout_of(dtype, n, out);
+    out->scratch_bytes = scratch_bytes_for(out->num_chunks);
+    return WC_OK;
+}
+
+wc_status wc_plan_batch(wc_dtype dtype, wc_segment *segs, uint32_t nseg, wc_layout *total)
+{
+    if (!valid_dtype(dtype) || (nseg && !segs) || !total) return WC_ERR_ARG;
+    uint64_t chunks = 0, raw = 0;
+    for (uint32_t i = 0; i < nseg; i++) {
+        if (segs[i].n > kMaxElems) return WC_ERR_ARG;
+        segs[i].chunk_base = chunks;
+        segs[i].raw_base = raw;
+        chunks += (segs[i].n + kChunk - 1) / kChunk;
+        raw += raw_bytes_of(dtype, segs[i].n);
+        if (i + 1 < nseg) raw = align_up(raw, 256);
+    }
+    return check_plan(dtype, segs, nseg, total, false);
+}
+
+wc_status wc_encode(wc_dtype dtype, const void *d_in, uint64_t n, const wc_buffers *out, void *d_scratch,
+                    uint64_t scratch_bytes, uint32_t *d_err, hipStream_t stream, hipEvent_t *stage_events)
+{
+    if (!valid_dtype(dtype) || n > kMaxElems) return WC_ERR_ARG;
+    wc_layout lay;
+    wc_query_layout(dtype, n, &lay);
+    wc_status s = check_buffers(out, lay.num_chunks, lay.raw_bytes);
+    if (s != WC_OK) return s;
+    if (n && (!d_in || !aligned(d_in, 16))) return WC_ERR_ARG;
+    if (lay.num_chunks && (!d_scratch || !aligned(d_scratch, 256))) return WC_ERR_ARG;
+    if (scratch_bytes < lay.scratch_bytes) return WC_ERR_CAPACITY;
+    if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
+    SegTable st{nullptr, 0, {reinterpret_cast<uint64_t>(d_in), n, 0, 0}};
+    return dtype == WC_BF16 ? encode_impl<WC_BF16>(st, lay.num_chunks, out, d_scratch, d_err, stream, stage_events)
+                            : encode_impl<WC_FP32>(st, lay.num_chunks, out, d_scratch, d_err, stream, stage_events);
+}
+
+wc_status wc_decode(wc_dtype dtype, const wc_buffers *in, uint64_t n, void *d_out, uint32_t *d_err,
+                    hipStream_t stream)
+{
+    if (!valid_dtype(dtype) || n > kMaxElems) return WC_ERR_ARG;
+    wc_layout lay;
+    wc_query_layout(dtype, n, &lay);
+    wc_status s = check_buffers(in, lay.num_chunks, lay.raw_bytes);
+    if (s != WC_OK) return s;
+    if (n && (!d_out || !aligned(d_out, 16))) return WC_ERR_ARG;
+    if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
+    SegTable st{nullptr, 0, {reinterpret_cast<uint64_t>(d_out), n, 0, 0}};
+    return dtype == WC_BF16 ? decode_impl<WC_BF16>(st, lay.num_chunks, in, d_err, stream)
+                            : decode_impl<WC_FP32>(st, lay.num_chunks, in, d_err, stream);
+}
+
+wc_status wc_encode_batch(wc_dtype dtype, const wc_segment *h_segs, const wc_segment *d_segs, uint32_t nseg,
+                          const wc_buffers *out, void *d_scratch, uint64_t scratch_bytes, uint32_t *d_err,
+                          hipStream_t stream, hipEvent_t *stage_events)
+{
+    if (!valid_dtype(dtype) || nseg == 0 || !h_segs || !d_segs || !aligned(d_segs, 8)) return WC_ERR_ARG;
+    wc_layout tot;
+    wc_status s = check_plan(dtype, h_segs, nseg, &tot);
+    if (s != WC_OK) return s;
+    s = check_buffers(out, tot.num_chunks, tot.raw_bytes);
+    if (s != WC_OK) return s;
+    if (tot.num_chunks && (!d_scratch || !aligned(d_scratch, 256))) return WC_ERR_ARG;
+    if (scratch_bytes < tot.scratch_bytes) return WC_ERR_CAPACITY;
+    if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
+    SegTable st{d_segs, nseg, {0, 0, 0, 0}};
+    return dtype == WC_BF16 ? encode_impl<WC_BF16>(st, tot.num_chunks, out, d_scratch, d_err, stream, stage_events)
+                            : encode_impl<WC_FP32>(st, tot.num_chunks, out, d_scratch, d_err, stream, stage_events);
+}
+
+wc_status wc_decode_batch(wc_dtype dtype, const wc_segment *h_segs, const wc_segment *d_segs, uint32_t nseg,
+                          const wc_buffers *in, uint32_t *d_err, hipStream_t stream)
+{
+    if (!valid_dtype(dtype) || nseg == 0 || !h_segs || !d_segs || !aligned(d_segs, 8)) return WC_ERR_ARG;
+    wc_layout tot;
+    wc_status s = check_plan(dtype, h_segs, nseg, &tot);
+    if (s != WC_OK) return s;
+    s = check_buffers(in, tot.num_chunks, tot.raw_bytes);
+    if (s != WC_OK) return s;
+    if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
+    SegTable st{d_segs, nseg, {0, 0, 0, 0}};
+    return dtype == WC_BF16 ? decode_impl<WC_BF16>(st, tot.num_chunks, in, d_err, stream)
+                            : decode_impl<WC_FP32>(st, tot.num_chunks, in, d_err, stream);
+}
+
+uint64_t wc_check_division(uint32_t samples_per_divisor)
+{
+    uint64_t bad = 0;
+    uint64_t rng = 0x9E3779B97F4A7C15ull;
+    for (uint32_t d = 1; d <= kM; d++) {
+        const DivConst c = div_const(d);
+        auto check = [&](uint32_t x) {
+            if (div_exact(x, c.mp, c.sh1, c.sh2) != x / d) bad++;
+        };
+        const uint32_t qmax = 0xFFFFFFFFu / d;
+        const uint32_t fixed[] = {0u, 1u, d - 1, d, d + 1, 0xFFFFFFFFu, 0xFFFFFFFFu - d, 0x7FFFFFFFu,
+                                  0x80000000u, (d << 20) - 1, qmax * d, qmax * d - 1, qmax * d + (d - 1)};
+        for (uint32_t x : fixed) check(x);
+        for (uint32_t i = 0; i < samples_per_divisor; i++) {
+            rng = rng * 6364136223846793005ull + 1442695040888963407ull;
+            const uint32_t q = (uint32_t)((rng >> 32) % ((uint64_t)qmax + 1));
+            const uint32_t r = (uint32_t)(rng >> 8) % d;
+            const uint64_t x = (uint64_t)q * d + r;
+            if (x <= 0xFFFFFFFFu) check((uint32_t)x);
+            check(q * d);
+            if (q) check(q * d - 1);
+        }
+    }
+    return bad;
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+"""The C-ABI library, without a GPU: it loads, exports every function that
+include/wc.h declares, and its host-side logic (layout, batch planning,
+argument checks, the encoder's reciprocal division) agrees with the oracle
+and with arithmetic."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import lossless_weight_compression_bf16_amd as wc
+from lossless_weight_compression_bf16_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from lossless_weight_compression_bf16_amd import build
+        build.build()
+    return wc.lib()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "wc.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:wc_status|int|const char \*|uint64_t)\s*\*?\s*(wc_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def test_version_and_strings(L):
+    assert wc.wc_version() >= 10000
+    assert L.wc_status_string(1) == b"invalid argument"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("n", [0, 1, 7, 65535, 65536, 65537, 3 * 65536 + 5, 8029995008])
+def test_layout_matches_oracle(L, oracle_lib, dtype, n):
+    a = wc.wc_query_layout(dtype, n).as_dict()
+    b = oracle_lib.query_layout(dtype, n)
+    for k in ("n", "num_chunks", "raw_bytes", "table_bytes", "seek_bytes", "payload_capacity"):
+        assert a[k] == getattr(b, k), k
+    c = a["num_chunks"]
+    assert a["scratch_bytes"] == (0 if c == 0 else ((8 * c + 255) // 256) * 256 + c * 131200)
+
+
+def test_plan_batch_matches_oracle(L, oracle_lib):
+    ns = [65536 * 2 + 5, 1, 0, 70000, 300, 50257 * 768]
+    for dtype in ("bf16", "fp32"):
+        segs, tot = wc.wc_plan_batch(dtype, ns)
+        cb, rb, otot = oracle_lib.plan_batch(dtype, ns)
+        assert [segs[i].chunk_base for i in range(len(ns))] == list(cb)
+        assert [segs[i].raw_base for i in range(len(ns))] == list(rb)
+        assert tot.num_chunks == otot.num_chunks and tot.raw_bytes == otot.raw_bytes
+        assert tot.payload_capacity == otot.payload_capacity
+
+
+def test_division_by_reciprocal(L):
+    # every divisor 1..4096, boundary and sampled dividends below 2^32
+    assert wc.wc_check_division(512) == 0
+
+
+def test_argument_errors_without_launch(L):
+    bufs = B.wc_buffers(0, 0, 0, 0, 0)
+    # bad dtype, null buffers, misaligned input: rejected on the host
+    assert L.wc_encode(7, None, 10, ctypes.byref(bufs), None, 0, None, None, None) == B.WC_ERR_ARG
+    assert L.wc_encode(0, None, 10, ctypes.byref(bufs), None, 0, None, None, None) == B.WC_ERR_ARG
+    good = B.wc_buffers(256, 256, 256, 256, 1 << 20)
+    assert L.wc_encode(0, 0x1002, 10, ctypes.byref(good), 256, 1 << 30, None, None, None) == B.WC_ERR_ARG
+    assert L.wc_encode(0, 0x1000, 10, ctypes.byref(good), 256, 10, None, None, None) == B.WC_ERR_CAPACITY
+    assert L.wc_decode(0, ctypes.byref(bufs), 10, 0x1000, None, None) == B.WC_ERR_ARG
+    assert L.wc_decode(0, ctypes.byref(good), 1 << 41, 0x1000, None, None) == B.WC_ERR_ARG
+    segs, _ = wc.wc_plan_batch("bf16", [100, 200])
+    segs[0].ptr, segs[1].ptr = 0x1000, 0x2000
+    segs[1].chunk_base = 5  # not what the plan says
+    assert L.wc_decode_batch(0, ctypes.cast(segs, ctypes.c_void_p), 0x3000, 2, ctypes.byref(good),
+                             None, None) == B.WC_ERR_ARG
