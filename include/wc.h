@@ -102,7 +102,7 @@ typedef struct {
  * of encode, output of decode).  chunk_base / raw_base are filled by
  * wc_plan_batch: tensor i's chunks follow tensor i-1's in the tables, seek
  * table and payload; its raw planes start at raw_base (the previous tensor's
- * raw end rounded up to 256 bytes). */
+ * raw end rounded up to 256 bytes; encode writes zeros into the gap). */
 typedef struct {
     uint64_t ptr;
     uint64_t n;

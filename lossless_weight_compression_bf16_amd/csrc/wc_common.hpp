@@ -45,6 +45,9 @@ __device__ inline WC_GLOBAL T *gptr(T *p)
     return reinterpret_cast<WC_GLOBAL T *>(reinterpret_cast<uint64_t>(p));
 }
 
+// Native 16-byte vector (loads as one global_load_dwordx4).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Segment view handed to every kernel: either one inline tensor (nseg == 0)
 // or a device array of planned segments.
 struct SegTable {

@@ -11,6 +11,8 @@
 //   k_compact     moves every chunk's payload from its slot to its offset.
 #pragma once
 
+#include <type_traits>
+
 #include "wc_common.hpp"
 
 namespace wc {
@@ -105,7 +107,7 @@ __device__ inline uint32_t normalize256(uint32_t c, uint32_t T, uint32_t *red, u
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__restrict__ raw,
-                                                    uint16_t *__restrict__ tables)
+                                                    uint16_t *__restrict__ tables, uint64_t raw_total)
 {
     constexpr int kCopies = 8;             // one sub-histogram per 32 threads
     constexpr int kStride = 257;           // pad: copies land on different banks
@@ -120,15 +122,21 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
     const uint32_t tid = threadIdx.x;
 
     for (uint32_t i = tid; i < kCopies * kStride; i += 256) hist[i] = 0;
+    // the segment's last chunk zeroes the alignment gap after its raw planes
+    if (start + len == sg.n) {
+        const uint64_t end = sg.raw_base + raw_bytes_of(DT, sg.n);
+        const uint64_t pad_end = min(align_up(end, 256), raw_total);
+        if (end + tid < pad_end) raw[end + tid] = 0;
+    }
     __syncthreads();
     uint32_t *my = hist + (tid >> 5) * kStride;
 
     if constexpr (DT == WC_BF16) {
-        const uint16_t *in = reinterpret_cast<const uint16_t *>(sg.ptr) + start;
+        const WC_GLOBAL uint16_t *in = gptr<uint16_t>(sg.ptr) + start;
         uint8_t *lo = raw + sg.raw_base + start;
         const uint32_t ng = len / 8;
         for (uint32_t g = tid; g < ng; g += 256) {
-            const uint4 v = reinterpret_cast<const uint4 *>(in)[g];
+            const u32x4 v = reinterpret_cast<const WC_GLOBAL u32x4 *>(in)[g];
             uint2 l;
             l.x = __builtin_amdgcn_perm(v.y, v.x, 0x06040200u);
             l.y = __builtin_amdgcn_perm(v.w, v.z, 0x06040200u);
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
     } else {
         // FP32: exponent counted; raw = sign bits | m0 | m1 | m2 (plane bases
         // follow the segment's element count).
-        const uint32_t *in = reinterpret_cast<const uint32_t *>(sg.ptr) + start;
+        const WC_GLOBAL uint32_t *in = gptr<uint32_t>(sg.ptr) + start;
         const uint64_t sb = (sg.n + 7) / 8;
         uint8_t *sign = raw + sg.raw_base + start / 8;
         uint8_t *m0 = raw + sg.raw_base + sb + start;
@@ -194,10 +202,10 @@ struct EncSym {
 };
 
 template <int DT>
-__device__ inline uint32_t load_elem(const void *base, uint64_t i)
+__device__ inline uint32_t load_elem(uint64_t base, uint64_t i)
 {
-    if constexpr (DT == WC_BF16) return reinterpret_cast<const uint16_t *>(base)[i];
-    else return reinterpret_cast<const uint32_t *>(base)[i];
+    if constexpr (DT == WC_BF16) return gptr<const uint16_t>(base)[i];
+    else return gptr<const uint32_t>(base)[i];
 }
 
 template <int DT>
@@ -274,9 +282,9 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     __syncthreads();
 
     uint16_t *words = reinterpret_cast<uint16_t *>(slots + (valid ? k : 0) * kSlotBytes + 128);
-    const void *in = reinterpret_cast<const void *>(sg.ptr);
+    const uint64_t in = sg.ptr;
     uint32_t x = kL;
-    uint32_t p = kMaxWords;
+    uint32_t p_w = kMaxWords;  // words are written downwards from here
 
     // the other half of the wavefront (chunk k ^ 1) decides whether the
     // unchecked loop may run
@@ -284,23 +292,29 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     const bool full = len == kChunk && other_len == kChunk;
     if (full) {
         constexpr uint32_t G = 16;  // steps per group; symbols prefetched one group ahead
-        const uint64_t base = start + lane;
+        using Elem = typename std::conditional<DT == WC_BF16, uint16_t, uint32_t>::type;
+        // element of lane `lane` at step t: p[32 t]; one base pointer per group,
+        // so the group's loads use immediate offsets
+        const WC_GLOBAL Elem *p = gptr<const Elem>(in) + start + lane;
         uint32_t cur[G], nxt[G];
         uint32_t t0 = kChunk / kLanes - G;
+        {
+            const WC_GLOBAL Elem *g = p + 32u * t0;
 #pragma unroll
-        for (uint32_t i = 0; i < G; i++) cur[i] = load_elem<DT>(in, base + 32ull * (t0 + i));
+            for (uint32_t i = 0; i < G; i++) cur[i] = g[32 * i];
+        }
         for (;;) {
-            const bool more = t0 > 0;
-            if (more) {
+            // next (lower) group; the last group re-reads itself instead of branching
+            const uint32_t tn = t0 >= G ? t0 - G : t0;
+            const WC_GLOBAL Elem *g = p + 32u * tn;
 #pragma unroll
-                for (uint32_t i = 0; i < G; i++) nxt[i] = load_elem<DT>(in, base + 32ull * (t0 - G + i));
-            }
+            for (uint32_t i = 0; i < G; i++) nxt[i] = g[32 * i];
 #pragma unroll
             for (int i = G - 1; i >= 0; i--) {
                 const EncSym e = enc[h][symbol_of<DT>(cur[i])];
-                enc_step<false>(x, p, true, e, words, h);
+                enc_step<false>(x, p_w, true, e, words, h);
             }
-            if (!more) break;
+            if (t0 == 0) break;
             t0 -= G;
 #pragma unroll
             for (uint32_t i = 0; i < G; i++) cur[i] = nxt[i];
@@ -314,15 +328,15 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
             const bool active = valid && j < len;
             const uint32_t s = active ? symbol_of<DT>(load_elem<DT>(in, start + j)) : 0u;
             const EncSym e = enc[h][s];
-            enc_step<true>(x, p, active, e, words, h);
+            enc_step<true>(x, p_w, active, e, words, h);
         }
     }
 
     if (valid) {
         reinterpret_cast<uint32_t *>(slots + k * kSlotBytes)[lane] = x;
         if (lane == 0) {
-            const uint32_t nw = kMaxWords - p;
-            meta[k] = make_uint2(128u + 2u * nw + 2u * (nw & 1u), p);
+            const uint32_t nw = kMaxWords - p_w;
+            meta[k] = make_uint2(128u + 2u * nw + 2u * (nw & 1u), p_w);
         }
     }
 }

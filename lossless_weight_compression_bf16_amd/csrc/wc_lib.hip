@@ -82,15 +82,15 @@ wc_status check_buffers(const wc_buffers *b, uint64_t chunks, uint64_t raw_bytes
 }
 
 template <int DT>
-wc_status encode_impl(const SegTable &st, uint64_t chunks, const wc_buffers *out, void *d_scratch,
-                      uint32_t *d_err, hipStream_t stream, hipEvent_t *ev)
+wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, const wc_buffers *out,
+                      void *d_scratch, uint32_t *d_err, hipStream_t stream, hipEvent_t *ev)
 {
     uint2 *meta = reinterpret_cast<uint2 *>(d_scratch);
     uint8_t *slots = reinterpret_cast<uint8_t *>(d_scratch) + align_up(8 * chunks, 256);
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return WC_ERR_HIP;
     if (chunks) {
         hipLaunchKernelGGL(k_split_hist<DT>, dim3((uint32_t)chunks), dim3(256), 0, stream, st, out->raw,
-                           out->tables);
+                           out->tables, raw_total);
     }
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return WC_ERR_HIP;
     if (chunks) {
@@ -173,8 +173,8 @@ wc_status wc_encode(wc_dtype dtype, const void *d_in, uint64_t n, const wc_buffe
     if (scratch_bytes < lay.scratch_bytes) return WC_ERR_CAPACITY;
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{nullptr, 0, {reinterpret_cast<uint64_t>(d_in), n, 0, 0}};
-    return dtype == WC_BF16 ? encode_impl<WC_BF16>(st, lay.num_chunks, out, d_scratch, d_err, stream, stage_events)
-                            : encode_impl<WC_FP32>(st, lay.num_chunks, out, d_scratch, d_err, stream, stage_events);
+    return dtype == WC_BF16 ? encode_impl<WC_BF16>(st, lay.num_chunks, lay.raw_bytes, out, d_scratch, d_err, stream, stage_events)
+                            : encode_impl<WC_FP32>(st, lay.num_chunks, lay.raw_bytes, out, d_scratch, d_err, stream, stage_events);
 }
 
 wc_status wc_decode(wc_dtype dtype, const wc_buffers *in, uint64_t n, void *d_out, uint32_t *d_err,
@@ -206,8 +206,8 @@ wc_status wc_encode_batch(wc_dtype dtype, const wc_segment *h_segs, const wc_seg
     if (scratch_bytes < tot.scratch_bytes) return WC_ERR_CAPACITY;
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{d_segs, nseg, {0, 0, 0, 0}};
-    return dtype == WC_BF16 ? encode_impl<WC_BF16>(st, tot.num_chunks, out, d_scratch, d_err, stream, stage_events)
-                            : encode_impl<WC_FP32>(st, tot.num_chunks, out, d_scratch, d_err, stream, stage_events);
+    return dtype == WC_BF16 ? encode_impl<WC_BF16>(st, tot.num_chunks, tot.raw_bytes, out, d_scratch, d_err, stream, stage_events)
+                            : encode_impl<WC_FP32>(st, tot.num_chunks, tot.raw_bytes, out, d_scratch, d_err, stream, stage_events);
 }
 
 wc_status wc_decode_batch(wc_dtype dtype, const wc_segment *h_segs, const wc_segment *d_segs, uint32_t nseg,
