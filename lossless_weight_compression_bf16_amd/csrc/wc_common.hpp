@@ -96,6 +96,27 @@ inline __host__ __device__ DivConst div_const(uint32_t d)
     return c;
 }
 
+// The constants for every divisor 1..4096, built at compile time (the encoder
+// looks them up per symbol instead of dividing 64-bit numbers on the GPU).
+struct DivTable {
+    uint32_t mp[kM + 1];
+    uint8_t l[kM + 1];  // ceil(log2 d); sh1 = min(l, 1), sh2 = max(l - 1, 0)
+};
+
+constexpr DivTable make_div_table()
+{
+    DivTable t{};
+    for (uint32_t d = 1; d <= kM; d++) {
+        uint32_t l = 0;
+        while ((1u << l) < d) l++;
+        t.mp[d] = (uint32_t)((((uint64_t)((1u << l) - d)) << 32) / d) + 1u;
+        t.l[d] = (uint8_t)l;
+    }
+    return t;
+}
+
+__device__ const DivTable kDivTable = make_div_table();
+
 inline __host__ __device__ uint32_t mulhi32(uint32_t a, uint32_t b)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -121,5 +142,11 @@ __device__ inline uint32_t wave_sum(uint32_t v)
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
+
+// LDS requests of one wavefront are served in issue order, so data that one
+// lane writes to LDS is visible to a later read by another lane of the same
+// wavefront; only the compiler has to be kept from moving LDS accesses
+// across these points.
+__device__ inline void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
 }  // namespace wc

@@ -2,98 +2,69 @@
 //
 // One wavefront decodes two chunks, one per 32-lane half, so every VALU
 // instruction of the serial rANS loop carries 64 useful lanes.  Per half the
-// LDS holds the chunk's slot -> symbol table (4096 bytes), its per-symbol
-// (f, b) pairs (256 u32) and a 1024-word ring of the compressed stream that
-// is refilled 256 words at a time, one group of 8 steps ahead, so the word
-// fetch of a step is an LDS read instead of a dependent HBM load.  Each step
-// of a half decodes 32 consecutive elements; the decoded byte is joined with
-// the raw plane (BF16: the low byte) and written straight to the output
-// tensor, 64 contiguous bytes per half per step.
+// LDS holds
+//   - the chunk's slot lookup table, in one of two forms:
+//       wide  (kL1 = true):  one u32 per slot = symbol | (f-1) << 8 |
+//                            (slot-b) << 20; one LDS read per step.  16 KiB
+//                            per chunk, so 4 wavefronts per CU: used when
+//                            there are few chunks and the run is bound by
+//                            the serial latency of each chunk;
+//       narrow (kL1 = false): slot -> symbol bytes (4 KiB) plus per-symbol
+//                            b | (f-4096) << 16 (1 KiB); two LDS reads per
+//                            step but 3x the wavefronts per CU, used when
+//                            there are enough chunks to fill the machine;
+//   - a 1024-word ring of the compressed stream, refilled 256 words at a
+//     time: a refill is loaded at the start of a group of 8 steps and
+//     written to the ring at the start of the next group, so the word fetch
+//     of a step is an LDS read and never waits for HBM;
+//   - the 256 decoded bytes of the current group.
+// At the end of a group each lane joins 8 consecutive decoded bytes with 8
+// raw bytes (loaded with one 8-byte load issued two groups earlier) and
+// writes 8 BF16 values with one 16-byte store: the output is written once,
+// coalesced, straight to HBM.
 #pragma once
+
+#include <type_traits>
 
 #include "wc_common.hpp"
 
 namespace wc {
 
-constexpr uint32_t kRingWords = 1024;     // per half
-constexpr uint32_t kRefillWords = 256;    // one refill: 32 lanes x 16 bytes
-constexpr uint32_t kGroup = 8;            // steps between refill decisions
+constexpr uint32_t kGroup = 8;                     // steps per group
+constexpr uint32_t kBlk = kLanes * kGroup;         // words per refill (max consumed per group)
+constexpr uint32_t kRingWords = 4 * kBlk;          // live words stay below 3 kBlk
+constexpr uint32_t kStageBytes = kLanes * kGroup;  // decoded bytes per group per half
 
-struct DecShared {
-    uint32_t sym[2][kM / 4];              // slot -> symbol, 4 slots per word (LDS offset 0)
-    uint32_t ring[2][kRingWords / 2];     // compressed words, 2 per u32
-    uint32_t fb[2][256];                  // b | (f - 4096) << 16
+struct DecSharedL1 {
+    uint32_t tab[2][kM];                    // per slot: sym | (f-1) << 8 | (slot-b) << 20
+    uint32_t ring[2][kRingWords / 2];
+    uint32_t stage[2][kStageBytes / 4];
 };
 
-// Raw-plane bytes one lane needs for one element, and the output write.
-template <int DT>
-struct RawView;
-
-template <>
-struct RawView<WC_BF16> {
-    const WC_GLOBAL uint8_t *lo;
-    WC_GLOBAL uint16_t *out;
-    __device__ void init(const uint8_t *raw, const wc_segment &sg, uint64_t start)
-    {
-        lo = gptr(raw) + sg.raw_base + start;
-        out = gptr<uint16_t>(sg.ptr) + start;
-    }
-    struct Pre {
-        uint32_t v;
-    };
-    __device__ Pre fetch(uint32_t j) const { return Pre{lo[j]}; }
-    __device__ void put(uint32_t j, uint32_t s, const Pre &p) const { out[j] = (uint16_t)((s << 8) | p.v); }
+struct DecSharedL2 {
+    uint32_t sym[2][kM / 4];                // slot -> symbol, 4 slots per word
+    uint32_t fb[2][256];                    // b | (f - 4096) << 16
+    uint32_t ring[2][kRingWords / 2];
+    uint32_t stage[2][kStageBytes / 4];
 };
 
-template <>
-struct RawView<WC_FP32> {
-    const WC_GLOBAL uint8_t *sign, *m0, *m1, *m2;
-    WC_GLOBAL uint32_t *out;
-    __device__ void init(const uint8_t *raw, const wc_segment &sg, uint64_t start)
-    {
-        const uint64_t sb = (sg.n + 7) / 8;
-        sign = gptr(raw) + sg.raw_base + start / 8;
-        m0 = gptr(raw) + sg.raw_base + sb + start;
-        m1 = m0 + sg.n;
-        m2 = m1 + sg.n;
-        out = gptr<uint32_t>(sg.ptr) + start;
-    }
-    struct Pre {
-        uint32_t v;
-    };
-    __device__ Pre fetch(uint32_t j) const
-    {
-        const uint32_t sbit = (sign[j >> 3] >> (j & 7)) & 1u;
-        return Pre{(sbit << 31) | ((uint32_t)m2[j] << 16) | ((uint32_t)m1[j] << 8) | m0[j]};
-    }
-    __device__ void put(uint32_t j, uint32_t s, const Pre &p) const { out[j] = p.v | (s << 23); }
-};
-
-// The ring is written and read by lanes of the same wavefront.  LDS requests
-// of one wavefront are served in issue order, so only the compiler has to be
-// kept from moving the reads of the next group above the refill's writes.
-__device__ inline void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
-
-// Per-half stream cursor.  All values are uniform within a half.
+// Per-half stream cursor (values uniform within a half).
 struct Stream {
-    const uint32_t *words;  // payload + seek[k] + 128, as dwords
-    uint32_t nw;            // words in the chunk (pad included, even)
-    uint32_t ptr;           // next word to consume
-    uint32_t fill;          // words written to the ring so far
+    const WC_GLOBAL uint32_t *words;  // payload + seek[k] + 128, as dwords
+    uint32_t nw;                      // words in the chunk (pad included, even)
+    uint32_t ptr;                     // next word to consume
+    uint32_t fill;                    // words written to the ring
 };
 
-// Starts a refill of 256 words if the ring runs low; returns whether it did.
-__device__ inline bool refill_issue(const Stream &st, uint32_t lane, bool on, uint4 &v)
+// Loads the next 256-word block if the ring runs low (16 bytes per lane).
+__device__ inline bool refill_issue(const Stream &st, uint32_t lane, bool on, u32x4 &v)
 {
-    const bool go = on && st.fill - st.ptr < 2 * kRefillWords && st.fill < st.nw;
+    const bool go = on && st.fill - st.ptr < 2 * kBlk && st.fill < st.nw;
     if (go) {
         const uint32_t d0 = st.fill / 2 + 4 * lane, ndw = st.nw / 2;
-        const WC_GLOBAL uint32_t *w = gptr(st.words) + d0;
+        const WC_GLOBAL uint32_t *w = st.words + d0;
         if (d0 + 4 <= ndw) {
-            v.x = w[0];
-            v.y = w[1];
-            v.z = w[2];
-            v.w = w[3];
+            v = u32x4{w[0], w[1], w[2], w[3]};
         } else {
             v.x = d0 + 0 < ndw ? w[0] : 0u;
             v.y = d0 + 1 < ndw ? w[1] : 0u;
@@ -104,41 +75,206 @@ __device__ inline bool refill_issue(const Stream &st, uint32_t lane, bool on, ui
     return go;
 }
 
-__device__ inline void refill_commit(Stream &st, uint32_t lane, bool go, const uint4 &v, uint32_t *ring)
+__device__ inline void refill_commit(Stream &st, uint32_t lane, bool go, const u32x4 &v, uint32_t *ring)
 {
     if (go) {
         const uint32_t d0 = (st.fill / 2 + 4 * lane) & (kRingWords / 2 - 1);
-        *reinterpret_cast<uint4 *>(ring + d0) = v;
-        st.fill += kRefillWords;
+        *reinterpret_cast<u32x4 *>(ring + d0) = v;
+        st.fill += kBlk;
     }
 }
 
-// One decode step for one lane.  With x = 4096 (x >> 12) + slot,
-// f (x >> 12) + slot - b  ==  x - b + (f - 4096) (x >> 12)  (mod 2^32),
-// one signed 24-bit multiply-add with the table's (f - 4096).
-template <int DT, bool CHECK>
-__device__ inline void dec_step(uint32_t &x, uint32_t &ptr, const DecShared &sh, uint32_t h, bool active,
-                                const RawView<DT> &rv, uint32_t j, const typename RawView<DT>::Pre &pre)
+// ----------------------------------------------------------- raw plane views
+// fetch(): the raw bytes a lane needs for its 8 elements of a group (issued
+// early); flush(): joins them with the 8 decoded bytes and stores.
+
+template <int DT>
+struct RawView;
+
+template <>
+struct RawView<WC_BF16> {
+    const WC_GLOBAL uint8_t *lo;
+    WC_GLOBAL uint16_t *out;
+    struct Pre {
+        uint2 v;
+    };
+    __device__ void init(const uint8_t *raw, const wc_segment &sg, uint64_t start)
+    {
+        lo = gptr(raw) + sg.raw_base + start;
+        out = gptr<uint16_t>(sg.ptr) + start;
+    }
+    // elements [e, e + 8), all inside the chunk, e a multiple of 8
+    __device__ Pre fetch(uint32_t e) const
+    {
+        const WC_GLOBAL uint32_t *p = reinterpret_cast<const WC_GLOBAL uint32_t *>(lo + e);
+        return Pre{make_uint2(p[0], p[1])};
+    }
+    __device__ void flush(uint32_t e, uint2 sym, const Pre &p) const
+    {
+        // out[i] = sym[i] << 8 | lo[i]: interleave the bytes pairwise
+        u32x4 o;
+        o.x = __builtin_amdgcn_perm(sym.x, p.v.x, 0x05010400u);
+        o.y = __builtin_amdgcn_perm(sym.x, p.v.x, 0x07030602u);
+        o.z = __builtin_amdgcn_perm(sym.y, p.v.y, 0x05010400u);
+        o.w = __builtin_amdgcn_perm(sym.y, p.v.y, 0x07030602u);
+        *reinterpret_cast<WC_GLOBAL u32x4 *>(out + e) = o;
+    }
+    // tail chunks: only elements below len exist
+    __device__ Pre fetch_checked(uint32_t e, uint32_t len) const
+    {
+        if (e + 8 <= len) return fetch(e);
+        uint32_t v[2] = {0, 0};
+        for (uint32_t i = 0; i < 8; i++)
+            if (e + i < len) v[i >> 2] |= (uint32_t)lo[e + i] << (8 * (i & 3));
+        return Pre{make_uint2(v[0], v[1])};
+    }
+    __device__ void flush_checked(uint32_t e, uint2 sym, const Pre &p, uint32_t len) const
+    {
+        if (e + 8 <= len) {
+            flush(e, sym, p);
+            return;
+        }
+        for (uint32_t i = 0; i < 8; i++) {
+            if (e + i >= len) break;
+            const uint32_t sh = 8 * (i & 3);
+            const uint32_t sb = ((i < 4 ? sym.x : sym.y) >> sh) & 0xFF;
+            const uint32_t lb = ((i < 4 ? p.v.x : p.v.y) >> sh) & 0xFF;
+            out[e + i] = (uint16_t)((sb << 8) | lb);
+        }
+    }
+};
+
+template <>
+struct RawView<WC_FP32> {
+    const WC_GLOBAL uint8_t *sign, *m0, *m1, *m2;
+    WC_GLOBAL uint32_t *out;
+    struct Pre {
+        uint32_t unused;
+    };
+    __device__ void init(const uint8_t *raw, const wc_segment &sg, uint64_t start)
+    {
+        const uint64_t sb = (sg.n + 7) / 8;
+        sign = gptr(raw) + sg.raw_base + start / 8;
+        m0 = gptr(raw) + sg.raw_base + sb + start;
+        m1 = m0 + sg.n;
+        m2 = m1 + sg.n;
+        out = gptr<uint32_t>(sg.ptr) + start;
+    }
+    // the mantissa planes have no alignment guarantee: they are read with
+    // byte loads when the group is written out
+    __device__ Pre fetch(uint32_t) const { return Pre{0}; }
+    __device__ Pre fetch_checked(uint32_t, uint32_t) const { return Pre{0}; }
+    __device__ void flush_checked(uint32_t e, uint2 sym, const Pre &, uint32_t len) const
+    {
+        const uint32_t sbits = sign[e >> 3];
+        for (uint32_t i = 0; i < 8; i++) {
+            const uint32_t j = e + i;
+            if (j >= len) break;
+            const uint32_t s = ((i < 4 ? sym.x : sym.y) >> (8 * (i & 3))) & 0xFF;
+            out[j] = (((sbits >> i) & 1u) << 31) | (s << 23) | ((uint32_t)m2[j] << 16) |
+                     ((uint32_t)m1[j] << 8) | m0[j];
+        }
+    }
+    __device__ void flush(uint32_t e, uint2 sym, const Pre &p) const { flush_checked(e, sym, p, e + 8); }
+};
+
+// -------------------------------------------------------------- table lookup
+
+template <bool kL1>
+struct Lookup;
+
+// One LDS read: xd = f (x >> 12) + slot - b = (f-1) q + q + (slot-b).
+template <>
+struct Lookup<true> {
+    __device__ static inline uint32_t step(const DecSharedL1 &sh, uint32_t h, uint32_t x, uint32_t &s)
+    {
+        const uint32_t e = sh.tab[h][x & (kM - 1)];
+        const uint32_t q = x >> kScaleBits;
+        s = e & 0xFF;
+        return __umul24((e >> 8) & 0xFFF, q) + (q + (e >> 20));
+    }
+};
+
+// Two LDS reads: with x = 4096 q + slot,
+// f q + slot - b == x - b + (f - 4096) q  (mod 2^32), one signed 24-bit mad.
+template <>
+struct Lookup<false> {
+    __device__ static inline uint32_t step(const DecSharedL2 &sh, uint32_t h, uint32_t x, uint32_t &s)
+    {
+        const uint8_t *sym = reinterpret_cast<const uint8_t *>(&sh.sym[0][0]);
+        s = sym[(x & (kM - 1)) | (h << 12)];
+        const uint32_t fb = sh.fb[h][s];
+        return (uint32_t)__mul24((int32_t)fb >> 16, (int32_t)(x >> kScaleBits)) + (x - (fb & 0xFFFF));
+    }
+};
+
+// One decode step of one lane: table lookup, renormalisation from the ring
+// (rank among the half's renormalising lanes via ballot + mbcnt), decoded
+// byte into the group's stage.
+template <bool kL1, bool CHECK, typename Sh>
+__device__ inline void dec_step(uint32_t &x, uint32_t &ptr, Sh &sh, uint32_t h, uint32_t lane, bool active,
+                                uint32_t i)
 {
-    const uint8_t *sym = reinterpret_cast<const uint8_t *>(&sh.sym[0][0]);
-    const uint32_t s = sym[(x & (kM - 1)) | (h << 12)];
-    const uint32_t fb = sh.fb[h][s];
-    const uint32_t xd = (uint32_t)__mul24((int32_t)fb >> 16, (int32_t)(x >> kScaleBits)) + (x - (fb & 0xFFFF));
+    uint32_t s;
+    const uint32_t xd = Lookup<kL1>::step(sh, h, x, s);
     const bool need = (!CHECK || active) && xd < kL;
     const uint64_t m = __ballot(need);
     const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
-    // rank among the half's renormalising lanes, added to the half's cursor
     const uint32_t widx = __builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(h ? 0u : ml, ptr));
     const uint16_t *ring = reinterpret_cast<const uint16_t *>(&sh.ring[0][0]);
     const uint32_t w = ring[(widx & (kRingWords - 1)) | (h << 10)];
     ptr += __popc(h ? mh : ml);
-    if (!CHECK || active) {
-        x = need ? (xd << 16) | w : xd;
-        rv.put(j, s, pre);
+    if (!CHECK || active) x = need ? (xd << 16) | w : xd;
+    reinterpret_cast<uint8_t *>(&sh.stage[h][0])[kLanes * i + lane] = (uint8_t)s;
+}
+
+// Builds the slot table of half h from the lane's 8 frequencies f[] (symbols
+// 8 lane .. 8 lane + 7) and their cumulative start b0.  The owner of a slot
+// is the last symbol whose start b is <= slot; each lane fills 128 slots by a
+// binary search for its first slot and a forward walk.
+template <bool kL1, typename Sh>
+__device__ inline void build_table(Sh &sh, uint32_t h, uint32_t lane, const uint32_t f[8], uint32_t b0,
+                                   uint32_t *fbtmp)
+{
+    {
+        uint32_t b = b0;
+        for (int i = 0; i < 8; i++) {
+            fbtmp[8 * lane + i] = (b & 0xFFFF) | ((f[i] - kM) << 16);
+            b += f[i];
+        }
+    }
+    wave_lds_order();
+    auto bstart = [&](uint32_t t) -> uint32_t { return fbtmp[t] & 0xFFFF; };
+    const uint32_t s0 = 128 * lane;
+    uint32_t lo = 0, hi = 256;
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (bstart(mid) <= s0) lo = mid; else hi = mid;
+    }
+    uint32_t s = lo;
+    uint32_t bs = bstart(s);
+    uint32_t nb = s < 255 ? bstart(s + 1) : kM;
+    for (uint32_t q = 0; q < 32; q++) {
+        uint32_t word = 0;
+        for (uint32_t i = 0; i < 4; i++) {
+            const uint32_t slot = s0 + 4 * q + i;
+            while (slot >= nb) {
+                s++;
+                bs = nb;
+                nb = s < 255 ? bstart(s + 1) : kM;
+            }
+            if constexpr (kL1) {
+                const uint32_t fm1 = nb - bs - 1;  // f - 1 of the owner
+                reinterpret_cast<DecSharedL1 &>(sh).tab[h][slot] = s | (fm1 << 8) | ((slot - bs) << 20);
+            } else {
+                word |= s << (8 * i);
+            }
+        }
+        if constexpr (!kL1) reinterpret_cast<DecSharedL2 &>(sh).sym[h][32 * lane + q] = word;
     }
 }
 
-template <int DT>
+template <int DT, bool kL1>
 __global__ __launch_bounds__(64) void k_decode(SegTable st, const uint8_t *__restrict__ raw,
                                                const uint16_t *__restrict__ tables,
                                                const uint64_t *__restrict__ seek,
@@ -146,7 +282,8 @@ __global__ __launch_bounds__(64) void k_decode(SegTable st, const uint8_t *__res
                                                uint64_t payload_bytes, uint64_t total_chunks,
                                                uint32_t *err)
 {
-    __shared__ DecShared sh;
+    using Sh = typename std::conditional<kL1, DecSharedL1, DecSharedL2>::type;
+    __shared__ Sh sh;
     const uint32_t lane = threadIdx.x & 31, h = threadIdx.x >> 5;
     const uint64_t k = 2ull * blockIdx.x + h;
     bool ok = k < total_chunks;
@@ -166,15 +303,15 @@ __global__ __launch_bounds__(64) void k_decode(SegTable st, const uint8_t *__res
             bits |= WC_EF_BAD_SEEK;
             ok = false;
         } else {
-            cs.words = reinterpret_cast<const uint32_t *>(payload + a + 128);
+            cs.words = gptr(reinterpret_cast<const uint32_t *>(payload + a + 128));
             cs.nw = (uint32_t)min<uint64_t>((b - a - 128) / 2, 2ull * kMaxWords + 2);
-            x = reinterpret_cast<const uint32_t *>(payload + a)[lane];
+            x = gptr(reinterpret_cast<const uint32_t *>(payload + a))[lane];
         }
     }
     // table: 8 symbols per lane, validated (sum 4096) before it is used
     uint32_t f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (ok) {
-        const uint4 fv = reinterpret_cast<const uint4 *>(tables + k * 256)[lane];
+        const u32x4 fv = gptr(reinterpret_cast<const u32x4 *>(tables + k * 256))[lane];
         f[0] = fv.x & 0xFFFF; f[1] = fv.x >> 16; f[2] = fv.y & 0xFFFF; f[3] = fv.y >> 16;
         f[4] = fv.z & 0xFFFF; f[5] = fv.z >> 16; f[6] = fv.w & 0xFFFF; f[7] = fv.w >> 16;
     }
@@ -182,7 +319,7 @@ __global__ __launch_bounds__(64) void k_decode(SegTable st, const uint8_t *__res
     for (int i = 0; i < 8; i++) local += f[i];
     uint32_t incl = local;
     for (int o = 1; o < 32; o <<= 1) {
-        uint32_t v = __shfl_up(incl, o, 32);
+        const uint32_t v = __shfl_up(incl, o, 32);
         if (lane >= (uint32_t)o) incl += v;
     }
     const uint32_t fsum = __shfl(incl, 31, 32);
@@ -191,42 +328,16 @@ __global__ __launch_bounds__(64) void k_decode(SegTable st, const uint8_t *__res
         ok = false;
     }
     if (ok) {
-        uint32_t b = incl - local;
-        for (int i = 0; i < 8; i++) {
-            sh.fb[h][8 * lane + i] = (b & 0xFFFF) | ((f[i] - kM) << 16);
-            b += f[i];
-        }
+        // the wide table needs (b, f) only while it is built: borrow the ring
+        uint32_t *fbtmp;
+        if constexpr (kL1) fbtmp = &sh.ring[h][0];
+        else fbtmp = &sh.fb[h][0];
+        build_table<kL1>(sh, h, lane, f, incl - local, fbtmp);
     }
     __syncthreads();
-    if (ok) {
-        // slots [128 lane, 128 lane + 128): owner of a slot = the last symbol
-        // whose start b is <= slot; walk forward from a binary search.
-        const uint32_t s0 = 128 * lane;
-        uint32_t lo = 0, hi = 256;
-        // b of symbol t from the packed table (b <= 4096 fits 16 bits)
-        auto bstart = [&](uint32_t t) -> uint32_t { return sh.fb[h][t] & 0xFFFF; };
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (bstart(mid) <= s0) lo = mid; else hi = mid;
-        }
-        uint32_t s = lo;
-        uint32_t nb = s < 255 ? bstart(s + 1) : kM;
-        for (uint32_t q = 0; q < 32; q++) {
-            uint32_t word = 0;
-            for (uint32_t i = 0; i < 4; i++) {
-                const uint32_t slot = s0 + 4 * q + i;
-                while (slot >= nb) {
-                    s++;
-                    nb = s < 255 ? bstart(s + 1) : kM;
-                }
-                word |= s << (8 * i);
-            }
-            sh.sym[h][32 * lane + q] = word;
-        }
-    }
-    // initial ring fill: two refills
+    // prefill the ring with two blocks
     for (int r = 0; r < 2; r++) {
-        uint4 v;
+        u32x4 v;
         const bool go = refill_issue(cs, lane, ok, v);
         refill_commit(cs, lane, go, v, sh.ring[h]);
     }
@@ -234,48 +345,58 @@ __global__ __launch_bounds__(64) void k_decode(SegTable st, const uint8_t *__res
 
     RawView<DT> rv;
     if (ok) rv.init(raw, sg, start);
+    const uint2 *stage = reinterpret_cast<const uint2 *>(&sh.stage[h][0]);
 
-    const uint32_t other_len = __shfl_xor(ok ? len : 0u, 32, 64);
-    const bool full = ok && len == kChunk && other_len == kChunk;
+    // Groups of 8 steps; both halves run the same number of groups (the
+    // shorter or missing chunk idles).  Full chunks take the unchecked path.
+    const uint32_t steps = ok ? (len + kLanes - 1) / kLanes : 0;
+    const uint32_t steps_other = __shfl_xor(steps, 32, 64);
+    const uint32_t ngroups = ((steps > steps_other ? steps : steps_other) + kGroup - 1) / kGroup;
+    const uint32_t mine_full = (ok && len == kChunk) ? 1u : 0u;
+    const uint32_t other_full = __shfl_xor(mine_full, 32, 64);
+    const bool full = mine_full && other_full;
     using Pre = typename RawView<DT>::Pre;
-    if (full) {
-        constexpr uint32_t kSteps = kChunk / kLanes;
-        Pre cur[kGroup], nxt[kGroup];
-#pragma unroll
-        for (uint32_t i = 0; i < kGroup; i++) cur[i] = rv.fetch(32 * i + lane);
-        for (uint32_t t0 = 0; t0 < kSteps; t0 += kGroup) {
-            uint4 v;
-            const bool go = refill_issue(cs, lane, true, v);
-            // next group's raw bytes (the last group re-reads its own: no branch)
-            const uint32_t tn = t0 + kGroup < kSteps ? t0 + kGroup : t0;
-#pragma unroll
-            for (uint32_t i = 0; i < kGroup; i++) nxt[i] = rv.fetch(32 * (tn + i) + lane);
-#pragma unroll
-            for (uint32_t i = 0; i < kGroup; i++)
-                dec_step<DT, false>(x, cs.ptr, sh, h, true, rv, 32 * (t0 + i) + lane, cur[i]);
-            refill_commit(cs, lane, go, v, sh.ring[h]);
+    auto run = [&](auto check_tag, uint32_t ng) {
+        constexpr bool CHECK = decltype(check_tag)::value;
+        auto fetch = [&](uint32_t gg) -> Pre {
+            const uint32_t e = kBlk * gg + 8 * lane;
+            if constexpr (CHECK) return ok ? rv.fetch_checked(e, len) : Pre{};
+            else return rv.fetch(e);
+        };
+        // raw bytes of group g are loaded two groups ahead into one of three
+        // register sets; the loop is unrolled by three so the sets are fixed
+        Pre pa = fetch(0);
+        Pre pb = fetch(ng > 1 ? 1 : 0);
+        Pre pc;
+        u32x4 pend = u32x4{0, 0, 0, 0};
+        bool pgo = false;
+        auto group = [&](uint32_t gg, const Pre &cur, Pre &ahead) {
+            refill_commit(cs, lane, pgo, pend, sh.ring[h]);
+            pgo = refill_issue(cs, lane, ok, pend);
+            ahead = fetch(gg + 2 < ng ? gg + 2 : gg);  // the last groups re-load themselves
             wave_lds_order();
 #pragma unroll
-            for (uint32_t i = 0; i < kGroup; i++) cur[i] = nxt[i];
-        }
-    } else {
-        const uint32_t steps = ok ? (len + kLanes - 1) / kLanes : 0;
-        const uint32_t other = __shfl_xor(steps, 32, 64);
-        const uint32_t smax = steps > other ? steps : other;
-        for (uint32_t t0 = 0; t0 < smax; t0 += kGroup) {
-            uint4 v;
-            const bool go = refill_issue(cs, lane, ok, v);
             for (uint32_t i = 0; i < kGroup; i++) {
-                const uint32_t j = 32 * (t0 + i) + lane;
-                const bool active = ok && j < len;
-                Pre pre{0};
-                if (active) pre = rv.fetch(j);
-                dec_step<DT, true>(x, cs.ptr, sh, h, active, rv, j, pre);
+                const bool active = !CHECK || (ok && kLanes * (kGroup * gg + i) + lane < len);
+                dec_step<kL1, CHECK>(x, cs.ptr, sh, h, lane, active, i);
             }
-            refill_commit(cs, lane, go, v, sh.ring[h]);
             wave_lds_order();
+            if constexpr (CHECK) {
+                if (ok) rv.flush_checked(kBlk * gg + 8 * lane, stage[lane], cur, len);
+            } else {
+                rv.flush(kBlk * gg + 8 * lane, stage[lane], cur);
+            }
+            wave_lds_order();
+        };
+#pragma unroll 1
+        for (uint32_t g = 0; g < ng; g += 3) {
+            group(g, pa, pc);
+            if (g + 1 < ng) group(g + 1, pb, pa);
+            if (g + 2 < ng) group(g + 2, pc, pb);
         }
-    }
+    };
+    if (full) run(std::false_type{}, kChunk / kBlk);
+    else run(std::true_type{}, ngroups);
 
     if (ok) {
         if (cs.ptr > cs.nw) {

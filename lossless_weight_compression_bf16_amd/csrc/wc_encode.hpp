@@ -201,41 +201,85 @@ struct EncSym {
     uint32_t b;
 };
 
-template <int DT>
-__device__ inline uint32_t load_elem(uint64_t base, uint64_t i)
-{
-    if constexpr (DT == WC_BF16) return gptr<const uint16_t>(base)[i];
-    else return gptr<const uint32_t>(base)[i];
-}
+constexpr uint32_t kEncGroup = 8;                  // steps per group: 256 symbols per half
 
-template <int DT>
-__device__ inline uint32_t symbol_of(uint32_t e)
-{
-    if constexpr (DT == WC_BF16) return e >> 8;
-    else return (e >> 23) & 0xFF;
-}
+struct EncShared {
+    EncSym enc[2][256];
+    uint32_t stage[2][kLanes * kEncGroup / 4];    // the group's symbols, element order
+};
 
-// One encode step for one lane: renormalise (emit the low 16 bits into the
-// word list, which grows downwards from index p) and push symbol s.
+// Coded-plane bytes of 8 consecutive elements [e, e + 8), loaded with wide
+// loads two groups ahead and unpacked into the group's stage.
+template <int DT>
+struct SymView;
+
+template <>
+struct SymView<WC_BF16> {
+    const WC_GLOBAL uint16_t *in;
+    struct Pre {
+        u32x4 v;
+    };
+    __device__ Pre fetch(uint32_t e) const { return Pre{*reinterpret_cast<const WC_GLOBAL u32x4 *>(in + e)}; }
+    __device__ uint2 bytes(const Pre &p) const
+    {
+        return make_uint2(__builtin_amdgcn_perm(p.v.y, p.v.x, 0x07050301u),
+                          __builtin_amdgcn_perm(p.v.w, p.v.z, 0x07050301u));
+    }
+    __device__ Pre fetch_checked(uint32_t e, uint32_t len) const
+    {
+        if (e + 8 <= len) return fetch(e);
+        uint32_t v[4] = {0, 0, 0, 0};
+        for (uint32_t i = 0; i < 8; i++)
+            if (e + i < len) v[i >> 1] |= (uint32_t)in[e + i] << (16 * (i & 1));
+        return Pre{u32x4{v[0], v[1], v[2], v[3]}};
+    }
+};
+
+template <>
+struct SymView<WC_FP32> {
+    const WC_GLOBAL uint32_t *in;
+    struct Pre {
+        u32x4 a, b;
+    };
+    __device__ Pre fetch(uint32_t e) const
+    {
+        const WC_GLOBAL u32x4 *p = reinterpret_cast<const WC_GLOBAL u32x4 *>(in + e);
+        return Pre{p[0], p[1]};
+    }
+    // exponent byte of u: bits 23..30
+    __device__ static uint32_t ex(uint32_t u) { return (u >> 23) & 0xFF; }
+    __device__ uint2 bytes(const Pre &p) const
+    {
+        return make_uint2(ex(p.a.x) | ex(p.a.y) << 8 | ex(p.a.z) << 16 | ex(p.a.w) << 24,
+                          ex(p.b.x) | ex(p.b.y) << 8 | ex(p.b.z) << 16 | ex(p.b.w) << 24);
+    }
+    __device__ Pre fetch_checked(uint32_t e, uint32_t len) const
+    {
+        if (e + 8 <= len) return fetch(e);
+        uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (uint32_t i = 0; i < 8; i++)
+            if (e + i < len) v[i] = in[e + i];
+        return Pre{u32x4{v[0], v[1], v[2], v[3]}, u32x4{v[4], v[5], v[6], v[7]}};
+    }
+};
+
+// One encode step for one lane: renormalise (the low 16 bits go to the word
+// list, which grows downwards from index p; the lane's rank among the half's
+// emitting lanes orders words within a step) and push the symbol.
 template <bool CHECK>
 __device__ inline void enc_step(uint32_t &x, uint32_t &p, bool active, const EncSym &e,
-                                uint16_t *words, uint32_t h)
+                                WC_GLOBAL uint16_t *words, uint32_t h)
 {
     const bool emit = (!CHECK || active) && x > e.th;
     const uint64_t m = __ballot(emit);
     const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(ml, 0u));
-    const uint32_t cl = __popc(ml), ch = __popc(mh);
-    p -= h ? ch : cl;
-    const uint32_t rank = below - (h ? cl : 0u);
-    if (emit) {
-        words[p + rank] = (uint16_t)(x & 0xFFFF);
-        x >>= 16;
-    }
-    if (!CHECK || active) {
-        const uint32_t q = div_exact(x, e.mp, (e.fm_sh >> 16) & 0xFF, e.fm_sh >> 24);
-        x = x + __umul24(q, e.fm_sh & 0xFFFF) + e.b;
-    }
+    p -= __popc(h ? mh : ml);
+    const uint32_t slot = __builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(h ? 0u : ml, p));
+    if (emit) words[slot] = (uint16_t)(x & 0xFFFF);
+    const uint32_t xr = emit ? x >> 16 : x;
+    const uint32_t q = div_exact(xr, e.mp, (e.fm_sh >> 16) & 0xFF, e.fm_sh >> 24);
+    const uint32_t xn = xr + __umul24(q, e.fm_sh & 0xFFFF) + e.b;
+    if (!CHECK || active) x = xn;
 }
 
 template <int DT>
@@ -243,7 +287,7 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
                                                uint8_t *__restrict__ slots, uint2 *__restrict__ meta,
                                                uint64_t total_chunks)
 {
-    __shared__ EncSym enc[2][256];
+    __shared__ EncShared sh;
     const uint32_t lane = threadIdx.x & 31, h = threadIdx.x >> 5;
     const uint64_t k = 2ull * blockIdx.x + h;
     const bool valid = k < total_chunks;
@@ -256,7 +300,7 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
         start = (k - sg.chunk_base) * kChunk;
         len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
         // table: 8 symbols per lane, cumulative start by a scan over the half
-        const uint4 fv = reinterpret_cast<const uint4 *>(tables + k * 256)[lane];
+        const u32x4 fv = gptr(reinterpret_cast<const u32x4 *>(tables + k * 256))[lane];
         uint32_t f[8] = {fv.x & 0xFFFF, fv.x >> 16, fv.y & 0xFFFF, fv.y >> 16,
                          fv.z & 0xFFFF, fv.z >> 16, fv.w & 0xFFFF, fv.w >> 16};
         uint32_t local = 0;
@@ -269,71 +313,79 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
         uint32_t b = incl - local;
         for (int i = 0; i < 8; i++) {
             EncSym e;
-            const uint32_t fi = f[i] ? f[i] : 1u;  // absent symbols are never encoded
-            const DivConst dc = div_const(fi);
-            e.mp = dc.mp;
+            // absent symbols are never encoded; f > 4096 only in a corrupt
+            // table, which the normaliser never produces
+            const uint32_t fi = f[i] ? (f[i] <= kM ? f[i] : kM) : 1u;
+            const uint32_t l = kDivTable.l[fi];
+            e.mp = kDivTable.mp[fi];
             e.th = (fi << 20) - 1u;  // wraps to 0xFFFFFFFF at f = 4096: never renormalise
-            e.fm_sh = (kM - fi) | (dc.sh1 << 16) | (dc.sh2 << 24);
+            e.fm_sh = (kM - fi) | ((l < 1 ? l : 1u) << 16) | ((l > 1 ? l - 1 : 0u) << 24);
             e.b = b;
-            enc[h][8 * lane + i] = e;
+            sh.enc[h][8 * lane + i] = e;
             b += f[i];
         }
     }
     __syncthreads();
 
-    uint16_t *words = reinterpret_cast<uint16_t *>(slots + (valid ? k : 0) * kSlotBytes + 128);
-    const uint64_t in = sg.ptr;
+    WC_GLOBAL uint8_t *slot = gptr(slots) + (valid ? k : 0) * kSlotBytes;
+    WC_GLOBAL uint16_t *words = reinterpret_cast<WC_GLOBAL uint16_t *>(slot + 128);
+    SymView<DT> sv;
+    using Elem = typename std::conditional<DT == WC_BF16, uint16_t, uint32_t>::type;
+    sv.in = gptr<const Elem>(sg.ptr) + start;
     uint32_t x = kL;
     uint32_t p_w = kMaxWords;  // words are written downwards from here
+    const uint8_t *stage = reinterpret_cast<const uint8_t *>(&sh.stage[h][0]);
 
-    // the other half of the wavefront (chunk k ^ 1) decides whether the
-    // unchecked loop may run
-    const uint32_t other_len = __shfl_xor(len, 32, 64);
-    const bool full = len == kChunk && other_len == kChunk;
-    if (full) {
-        constexpr uint32_t G = 16;  // steps per group; symbols prefetched one group ahead
-        using Elem = typename std::conditional<DT == WC_BF16, uint16_t, uint32_t>::type;
-        // element of lane `lane` at step t: p[32 t]; one base pointer per group,
-        // so the group's loads use immediate offsets
-        const WC_GLOBAL Elem *p = gptr<const Elem>(in) + start + lane;
-        uint32_t cur[G], nxt[G];
-        uint32_t t0 = kChunk / kLanes - G;
-        {
-            const WC_GLOBAL Elem *g = p + 32u * t0;
+    // Groups of 8 steps, from the last to the first; both halves run the same
+    // number of groups (the shorter or missing chunk idles).  Full chunks take
+    // the unchecked path.
+    constexpr uint32_t kBlkE = kLanes * kEncGroup;  // 256 symbols per group
+    const uint32_t steps = valid ? (len + kLanes - 1) / kLanes : 0;
+    const uint32_t steps_other = __shfl_xor(steps, 32, 64);
+    const uint32_t ngroups = ((steps > steps_other ? steps : steps_other) + kEncGroup - 1) / kEncGroup;
+    const uint32_t mine_full = (valid && len == kChunk) ? 1u : 0u;
+    const uint32_t other_full = __shfl_xor(mine_full, 32, 64);
+    const bool full = mine_full && other_full;
+    using Pre = typename SymView<DT>::Pre;
+    auto run = [&](auto check_tag, uint32_t ng) {
+        constexpr bool CHECK = decltype(check_tag)::value;
+        auto fetch = [&](uint32_t g) -> Pre {
+            const uint32_t e = kBlkE * g + 8 * lane;
+            if constexpr (CHECK) return valid ? sv.fetch_checked(e, len) : Pre{};
+            else return sv.fetch(e);
+        };
+        // a group's input is loaded two groups ahead into one of three
+        // register sets (fixed by unrolling the loop by three)
+        Pre pa = fetch(ng - 1);
+        Pre pb = fetch(ng > 1 ? ng - 2 : ng - 1);
+        Pre pc;
+        auto group = [&](uint32_t gj, const Pre &cur, Pre &ahead) {
+            const uint32_t g = ng - 1 - gj;
+            ahead = fetch(g >= 2 ? g - 2 : g);  // the last groups re-load themselves
+            reinterpret_cast<uint2 *>(&sh.stage[h][0])[lane] = sv.bytes(cur);
+            wave_lds_order();
 #pragma unroll
-            for (uint32_t i = 0; i < G; i++) cur[i] = g[32 * i];
-        }
-        for (;;) {
-            // next (lower) group; the last group re-reads itself instead of branching
-            const uint32_t tn = t0 >= G ? t0 - G : t0;
-            const WC_GLOBAL Elem *g = p + 32u * tn;
-#pragma unroll
-            for (uint32_t i = 0; i < G; i++) nxt[i] = g[32 * i];
-#pragma unroll
-            for (int i = G - 1; i >= 0; i--) {
-                const EncSym e = enc[h][symbol_of<DT>(cur[i])];
-                enc_step<false>(x, p_w, true, e, words, h);
+            for (int i = kEncGroup - 1; i >= 0; i--) {
+                const bool active = !CHECK || (valid && kLanes * (kEncGroup * g + i) + lane < len);
+                const EncSym e = sh.enc[h][stage[kLanes * i + lane]];
+                enc_step<CHECK>(x, p_w, active, e, words, h);
             }
-            if (t0 == 0) break;
-            t0 -= G;
-#pragma unroll
-            for (uint32_t i = 0; i < G; i++) cur[i] = nxt[i];
+            wave_lds_order();
+        };
+#pragma unroll 1
+        for (uint32_t gj = 0; gj < ng; gj += 3) {
+            group(gj, pa, pc);
+            if (gj + 1 < ng) group(gj + 1, pb, pa);
+            if (gj + 2 < ng) group(gj + 2, pc, pb);
         }
-    } else {
-        const uint32_t steps = (len + kLanes - 1) / kLanes;
-        const uint32_t other = __shfl_xor(steps, 32, 64);
-        const uint32_t smax = steps > other ? steps : other;
-        for (uint32_t t = smax; t-- > 0;) {
-            const uint32_t j = t * kLanes + lane;
-            const bool active = valid && j < len;
-            const uint32_t s = active ? symbol_of<DT>(load_elem<DT>(in, start + j)) : 0u;
-            const EncSym e = enc[h][s];
-            enc_step<true>(x, p_w, active, e, words, h);
-        }
+    };
+    if (ngroups) {
+        if (full) run(std::false_type{}, kChunk / kBlkE);
+        else run(std::true_type{}, ngroups);
     }
 
     if (valid) {
-        reinterpret_cast<uint32_t *>(slots + k * kSlotBytes)[lane] = x;
+        reinterpret_cast<WC_GLOBAL uint32_t *>(slot)[lane] = x;
         if (lane == 0) {
             const uint32_t nw = kMaxWords - p_w;
             meta[k] = make_uint2(128u + 2u * nw + 2u * (nw & 1u), p_w);

@@ -109,13 +109,31 @@ wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, c
     return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 
+// Decoder variant: when every wavefront fits on the machine at the wide
+// table's occupancy (4 per CU), the run is bound by the serial latency of a
+// chunk and the one-read wide table is faster; with more chunks the narrow
+// table's higher occupancy wins.
+bool use_wide_table(uint64_t waves)
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+    return waves <= 4ull * (uint64_t)cus;
+}
+
 template <int DT>
 wc_status decode_impl(const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err,
                       hipStream_t stream)
 {
     if (chunks == 0) return WC_OK;
-    hipLaunchKernelGGL(k_decode<DT>, dim3((uint32_t)((chunks + 1) / 2)), dim3(64), 0, stream, st, in->raw,
-                       in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err);
+    const uint64_t waves = (chunks + 1) / 2;
+    if (use_wide_table(waves)) {
+        hipLaunchKernelGGL((k_decode<DT, true>), dim3((uint32_t)waves), dim3(64), 0, stream, st, in->raw,
+                           in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err);
+    } else {
+        hipLaunchKernelGGL((k_decode<DT, false>), dim3((uint32_t)waves), dim3(64), 0, stream, st, in->raw,
+                           in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err);
+    }
     return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 
@@ -229,8 +247,12 @@ uint64_t wc_check_division(uint32_t samples_per_divisor)
 {
     uint64_t bad = 0;
     uint64_t rng = 0x9E3779B97F4A7C15ull;
+    static constexpr DivTable table = make_div_table();
     for (uint32_t d = 1; d <= kM; d++) {
         const DivConst c = div_const(d);
+        // the compile-time table the encoder kernel reads must agree
+        const uint32_t l = table.l[d];
+        if (table.mp[d] != c.mp || (l < 1 ? l : 1u) != c.sh1 || (l > 1 ? l - 1 : 0u) != c.sh2) bad++;
         auto check = [&](uint32_t x) {
             if (div_exact(x, c.mp, c.sh1, c.sh2) != x / d) bad++;
         };
