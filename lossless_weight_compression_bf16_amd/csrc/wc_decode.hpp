@@ -35,17 +35,20 @@ constexpr uint32_t kBlk = kLanes * kGroup;         // words per refill (max cons
 constexpr uint32_t kRingWords = 4 * kBlk;          // live words stay below 3 kBlk
 constexpr uint32_t kStageBytes = kLanes * kGroup;  // decoded bytes per group per half
 
+// H = chunks per wavefront (one per 32-lane half)
+template <int H>
 struct DecSharedL1 {
-    uint32_t tab[2][kM];                    // per slot: sym | (f-1) << 8 | (slot-b) << 20
-    uint32_t ring[2][kRingWords / 2];
-    uint32_t stage[2][kStageBytes / 4];
+    uint32_t tab[H][kM];                    // per slot: sym | (f-1) << 8 | (slot-b) << 20
+    uint32_t ring[H][kRingWords / 2];
+    uint32_t stage[H][kStageBytes / 4];
 };
 
+template <int H>
 struct DecSharedL2 {
-    uint32_t sym[2][kM / 4];                // slot -> symbol, 4 slots per word
-    uint32_t fb[2][256];                    // b | (f - 4096) << 16
-    uint32_t ring[2][kRingWords / 2];
-    uint32_t stage[2][kStageBytes / 4];
+    uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
+    uint32_t fb[H][256];                    // b | (f - 4096) << 16
+    uint32_t ring[H][kRingWords / 2];
+    uint32_t stage[H][kStageBytes / 4];
 };
 
 // Per-half stream cursor (values uniform within a half).
@@ -56,28 +59,38 @@ struct Stream {
     uint32_t fill;                    // words written to the ring
 };
 
-// Loads the next 256-word block if the ring runs low (16 bytes per lane).
-__device__ inline bool refill_issue(const Stream &st, uint32_t lane, bool on, u32x4 &v)
+// A refill moves the next 256-word block into the ring, 16 bytes per lane.
+// The load is issued every group, unconditionally, so the compiler can count
+// outstanding memory operations exactly: when no refill is due it reads the
+// chunk's first 16 bytes, and near the end of the stream it reads the last
+// 16 in-bounds bytes and the commit shifts the lane's words into place.
+struct Refill {
+    u32x4 v;
+    uint32_t shift;  // dwords between the wanted start and the loaded start
+    bool go;
+};
+
+__device__ inline Refill refill_issue(const Stream &st, uint32_t lane, bool on)
 {
-    const bool go = on && st.fill - st.ptr < 2 * kBlk && st.fill < st.nw;
-    if (go) {
-        const uint32_t d0 = st.fill / 2 + 4 * lane, ndw = st.nw / 2;
-        const WC_GLOBAL uint32_t *w = st.words + d0;
-        if (d0 + 4 <= ndw) {
-            v = u32x4{w[0], w[1], w[2], w[3]};
-        } else {
-            v.x = d0 + 0 < ndw ? w[0] : 0u;
-            v.y = d0 + 1 < ndw ? w[1] : 0u;
-            v.z = d0 + 2 < ndw ? w[2] : 0u;
-            v.w = 0u;  // ndw - d0 < 4 here
-        }
-    }
-    return go;
+    Refill r;
+    r.go = on && st.fill - st.ptr < 2 * kBlk && st.fill < st.nw;
+    const int32_t d0 = (int32_t)(st.fill / 2 + 4 * lane), ndw = (int32_t)(st.nw / 2);
+    // [dl, dl + 4) lies in [-32, ndw): the words area or the 128-byte state
+    // area in front of it
+    const int32_t dl = r.go ? (d0 + 4 <= ndw ? d0 : ndw - 4) : -32;
+    r.v = *reinterpret_cast<const WC_GLOBAL u32x4 *>(st.words + dl);
+    r.shift = (uint32_t)(d0 - dl);
+    return r;
 }
 
-__device__ inline void refill_commit(Stream &st, uint32_t lane, bool go, const u32x4 &v, uint32_t *ring)
+__device__ inline void refill_commit(Stream &st, uint32_t lane, const Refill &r, uint32_t *ring)
 {
-    if (go) {
+    if (r.go) {
+        // dwords past the stream end are never consumed by a valid stream
+        u32x4 v = r.v;
+        if (r.shift >= 2) v = u32x4{v.z, v.w, 0u, 0u};
+        if (r.shift & 1) v = u32x4{v.y, v.z, v.w, 0u};
+        if (r.shift >= 4) v = u32x4{0u, 0u, 0u, 0u};
         const uint32_t d0 = (st.fill / 2 + 4 * lane) & (kRingWords / 2 - 1);
         *reinterpret_cast<u32x4 *>(ring + d0) = v;
         st.fill += kBlk;
@@ -186,7 +199,8 @@ struct Lookup;
 // One LDS read: xd = f (x >> 12) + slot - b = (f-1) q + q + (slot-b).
 template <>
 struct Lookup<true> {
-    __device__ static inline uint32_t step(const DecSharedL1 &sh, uint32_t h, uint32_t x, uint32_t &s)
+    template <typename Sh>
+    __device__ static inline uint32_t step(const Sh &sh, uint32_t h, uint32_t x, uint32_t &s)
     {
         const uint32_t e = sh.tab[h][x & (kM - 1)];
         const uint32_t q = x >> kScaleBits;
@@ -199,7 +213,8 @@ struct Lookup<true> {
 // f q + slot - b == x - b + (f - 4096) q  (mod 2^32), one signed 24-bit mad.
 template <>
 struct Lookup<false> {
-    __device__ static inline uint32_t step(const DecSharedL2 &sh, uint32_t h, uint32_t x, uint32_t &s)
+    template <typename Sh>
+    __device__ static inline uint32_t step(const Sh &sh, uint32_t h, uint32_t x, uint32_t &s)
     {
         const uint8_t *sym = reinterpret_cast<const uint8_t *>(&sh.sym[0][0]);
         s = sym[(x & (kM - 1)) | (h << 12)];
@@ -265,39 +280,42 @@ __device__ inline void build_table(Sh &sh, uint32_t h, uint32_t lane, const uint
             }
             if constexpr (kL1) {
                 const uint32_t fm1 = nb - bs - 1;  // f - 1 of the owner
-                reinterpret_cast<DecSharedL1 &>(sh).tab[h][slot] = s | (fm1 << 8) | ((slot - bs) << 20);
+                sh.tab[h][slot] = s | (fm1 << 8) | ((slot - bs) << 20);
             } else {
                 word |= s << (8 * i);
             }
         }
-        if constexpr (!kL1) reinterpret_cast<DecSharedL2 &>(sh).sym[h][32 * lane + q] = word;
+        if constexpr (!kL1) sh.sym[h][32 * lane + q] = word;
     }
 }
 
-template <int DT, bool kL1>
-__global__ __launch_bounds__(64) void k_decode(SegTable st, const uint8_t *__restrict__ raw,
-                                               const uint16_t *__restrict__ tables,
-                                               const uint64_t *__restrict__ seek,
-                                               const uint8_t *__restrict__ payload,
-                                               uint64_t payload_bytes, uint64_t total_chunks,
-                                               uint32_t *err)
+// kH = 1: one chunk per wavefront (32 lanes; the wide table's variant, so
+// a lone wavefront's serial chain has no per-half selects).  kH = 2: two
+// chunks per wavefront; with an odd chunk count the last wavefront's second
+// half shadows the first half's chunk (same unchecked code, nothing stored).
+template <int DT, bool kL1, int kH>
+__global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *__restrict__ raw,
+                                                    const uint16_t *__restrict__ tables,
+                                                    const uint64_t *__restrict__ seek,
+                                                    const uint8_t *__restrict__ payload,
+                                                    uint64_t payload_bytes, uint64_t total_chunks,
+                                                    uint32_t *err)
 {
-    using Sh = typename std::conditional<kL1, DecSharedL1, DecSharedL2>::type;
+    using Sh = typename std::conditional<kL1, DecSharedL1<kH>, DecSharedL2<kH>>::type;
     __shared__ Sh sh;
-    const uint32_t lane = threadIdx.x & 31, h = threadIdx.x >> 5;
-    const uint64_t k = 2ull * blockIdx.x + h;
-    bool ok = k < total_chunks;
+    const uint32_t lane = threadIdx.x & 31, h = kH == 1 ? 0u : threadIdx.x >> 5;
+    const uint64_t k_own = (uint64_t)kH * blockIdx.x + h;
+    const bool real = k_own < total_chunks;
+    const uint64_t k = real ? k_own : k_own - 1;
+    bool ok = true;
     uint32_t bits = 0;
 
-    wc_segment sg{0, 0, 0, 0};
-    uint64_t start = 0;
-    uint32_t len = 0;
+    const wc_segment sg = find_segment(st, k);
+    const uint64_t start = (k - sg.chunk_base) * kChunk;
+    const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
     Stream cs{nullptr, 0, 0, 0};
     uint32_t x = kL;
-    if (ok) {
-        sg = find_segment(st, k);
-        start = (k - sg.chunk_base) * kChunk;
-        len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
+    {
         const uint64_t a = seek[k], b = seek[k + 1];
         if (a > b || b > payload_bytes || b - a < 128 || ((b - a) & 3) || (a & 3)) {
             bits |= WC_EF_BAD_SEEK;
@@ -336,67 +354,69 @@ __global__ __launch_bounds__(64) void k_decode(SegTable st, const uint8_t *__res
     }
     __syncthreads();
     // prefill the ring with two blocks
-    for (int r = 0; r < 2; r++) {
-        u32x4 v;
-        const bool go = refill_issue(cs, lane, ok, v);
-        refill_commit(cs, lane, go, v, sh.ring[h]);
-    }
+    for (int r = 0; r < 2; r++) refill_commit(cs, lane, refill_issue(cs, lane, ok), sh.ring[h]);
     __syncthreads();
 
     RawView<DT> rv;
-    if (ok) rv.init(raw, sg, start);
+    rv.init(raw, sg, start);
     const uint2 *stage = reinterpret_cast<const uint2 *>(&sh.stage[h][0]);
+    const bool put = ok && real;  // this half writes output
 
-    // Groups of 8 steps; both halves run the same number of groups (the
-    // shorter or missing chunk idles).  Full chunks take the unchecked path.
-    const uint32_t steps = ok ? (len + kLanes - 1) / kLanes : 0;
-    const uint32_t steps_other = __shfl_xor(steps, 32, 64);
-    const uint32_t ngroups = ((steps > steps_other ? steps : steps_other) + kGroup - 1) / kGroup;
-    const uint32_t mine_full = (ok && len == kChunk) ? 1u : 0u;
-    const uint32_t other_full = __shfl_xor(mine_full, 32, 64);
-    const bool full = mine_full && other_full;
+    // Groups of 8 steps, first to last.  Groups where every lane of every
+    // half is active (and every table valid) run unchecked; the partial last
+    // group of a shorter chunk runs checked, last.
+    const uint32_t my_len = ok ? len : 0u;
+    const uint32_t other_len = kH == 2 ? __shfl_xor(my_len, 32, 64) : my_len;
+    const uint32_t hi_len = my_len > other_len ? my_len : other_len;
+    const uint32_t lo_len = my_len < other_len ? my_len : other_len;
+    const uint32_t ng = (hi_len + kBlk - 1) / kBlk;
+    const uint32_t nfull = lo_len / kBlk;
     using Pre = typename RawView<DT>::Pre;
-    auto run = [&](auto check_tag, uint32_t ng) {
+    Refill pend{u32x4{0, 0, 0, 0}, 0, false};
+    auto group = [&](auto check_tag, uint32_t gg, uint32_t g_last, const Pre &cur, Pre &ahead) {
         constexpr bool CHECK = decltype(check_tag)::value;
-        auto fetch = [&](uint32_t gg) -> Pre {
-            const uint32_t e = kBlk * gg + 8 * lane;
-            if constexpr (CHECK) return ok ? rv.fetch_checked(e, len) : Pre{};
-            else return rv.fetch(e);
-        };
-        // raw bytes of group g are loaded two groups ahead into one of three
-        // register sets; the loop is unrolled by three so the sets are fixed
-        Pre pa = fetch(0);
-        Pre pb = fetch(ng > 1 ? 1 : 0);
-        Pre pc;
-        u32x4 pend = u32x4{0, 0, 0, 0};
-        bool pgo = false;
-        auto group = [&](uint32_t gg, const Pre &cur, Pre &ahead) {
-            refill_commit(cs, lane, pgo, pend, sh.ring[h]);
-            pgo = refill_issue(cs, lane, ok, pend);
-            ahead = fetch(gg + 2 < ng ? gg + 2 : gg);  // the last groups re-load themselves
-            wave_lds_order();
+        refill_commit(cs, lane, pend, sh.ring[h]);
+        pend = refill_issue(cs, lane, ok);
+        const uint32_t gn = gg + 2 <= g_last ? gg + 2 : gg;  // the last groups re-load themselves
+        if constexpr (CHECK) ahead = put ? rv.fetch_checked(kBlk * gn + 8 * lane, len) : Pre{};
+        else ahead = rv.fetch(kBlk * gn + 8 * lane);
+        wave_lds_order();
 #pragma unroll
-            for (uint32_t i = 0; i < kGroup; i++) {
-                const bool active = !CHECK || (ok && kLanes * (kGroup * gg + i) + lane < len);
-                dec_step<kL1, CHECK>(x, cs.ptr, sh, h, lane, active, i);
-            }
-            wave_lds_order();
-            if constexpr (CHECK) {
-                if (ok) rv.flush_checked(kBlk * gg + 8 * lane, stage[lane], cur, len);
-            } else {
-                rv.flush(kBlk * gg + 8 * lane, stage[lane], cur);
-            }
-            wave_lds_order();
-        };
-#pragma unroll 1
-        for (uint32_t g = 0; g < ng; g += 3) {
-            group(g, pa, pc);
-            if (g + 1 < ng) group(g + 1, pb, pa);
-            if (g + 2 < ng) group(g + 2, pc, pb);
+        for (uint32_t i = 0; i < kGroup; i++) {
+            const bool active = !CHECK || (ok && kLanes * (kGroup * gg + i) + lane < len);
+            dec_step<kL1, CHECK>(x, cs.ptr, sh, h, lane, active, i);
         }
+        wave_lds_order();
+        if constexpr (CHECK) {
+            if (put) rv.flush_checked(kBlk * gg + 8 * lane, stage[lane], cur, len);
+        } else {
+            if (real) rv.flush(kBlk * gg + 8 * lane, stage[lane], cur);
+        }
+        wave_lds_order();
     };
-    if (full) run(std::false_type{}, kChunk / kBlk);
-    else run(std::true_type{}, ngroups);
+    // raw bytes of group g are loaded two groups ahead into one of three
+    // register sets; the hot loop runs whole triples of full groups so the
+    // sets stay in fixed registers
+    const uint32_t n3 = nfull / 3 * 3;
+    if (n3) {
+        const std::false_type u{};
+        Pre pa = rv.fetch(8 * lane);
+        Pre pb = rv.fetch(kBlk + 8 * lane);
+        Pre pc;
+        const uint32_t last = n3 - 1;
+#pragma unroll 1
+        for (uint32_t g = 0; g < n3; g += 3) {
+            group(u, g, last, pa, pc);
+            group(u, g + 1, last, pb, pa);
+            group(u, g + 2, last, pc, pb);
+        }
+    }
+    // what is left (at most two full groups and a partial one) runs checked
+    for (uint32_t g = n3; g < ng; g++) {
+        Pre cur = put ? rv.fetch_checked(kBlk * g + 8 * lane, len) : Pre{};
+        Pre dummy;
+        group(std::true_type{}, g, g, cur, dummy);
+    }
 
     if (ok) {
         if (cs.ptr > cs.nw) {
@@ -409,9 +429,9 @@ __global__ __launch_bounds__(64) void k_decode(SegTable st, const uint8_t *__res
         }
         if (x != kL) bits |= WC_EF_BAD_FINAL_STATE;
     }
-    // OR the half's bits into lane 0 of the half
+    // OR the half's bits into lane 0 of the half; a shadow half reports nothing
     for (int o = 16; o > 0; o >>= 1) bits |= __shfl_xor(bits, o, 32);
-    if (lane == 0 && bits && err) atomicOr(err, bits);
+    if (lane == 0 && bits && real && err) atomicOr(err, bits);
 }
 
 }  // namespace wc

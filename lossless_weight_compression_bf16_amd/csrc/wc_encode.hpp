@@ -202,80 +202,55 @@ struct EncSym {
 };
 
 constexpr uint32_t kEncGroup = 8;                  // steps per group: 256 symbols per half
+constexpr uint32_t kEncBlk = kLanes * kEncGroup;
 
-struct EncShared {
-    EncSym enc[2][256];
-    uint32_t stage[2][kLanes * kEncGroup / 4];    // the group's symbols, element order
-};
-
-// Coded-plane bytes of 8 consecutive elements [e, e + 8), loaded with wide
-// loads two groups ahead and unpacked into the group's stage.
+// The elements a lane encodes in one group: element 32 i + lane of the group
+// for step i, loaded (strided, 64 contiguous bytes per half per load) two
+// groups ahead of use.
 template <int DT>
-struct SymView;
-
-template <>
-struct SymView<WC_BF16> {
-    const WC_GLOBAL uint16_t *in;
+struct SymView {
+    using Elem = typename std::conditional<DT == WC_BF16, uint16_t, uint32_t>::type;
+    const WC_GLOBAL Elem *in;
     struct Pre {
-        u32x4 v;
+        uint32_t e[kEncGroup];
     };
-    __device__ Pre fetch(uint32_t e) const { return Pre{*reinterpret_cast<const WC_GLOBAL u32x4 *>(in + e)}; }
-    __device__ uint2 bytes(const Pre &p) const
+    template <bool CHECK>
+    __device__ Pre fetch(uint32_t g, uint32_t lane, uint32_t len) const
     {
-        return make_uint2(__builtin_amdgcn_perm(p.v.y, p.v.x, 0x07050301u),
-                          __builtin_amdgcn_perm(p.v.w, p.v.z, 0x07050301u));
+        Pre p;
+        const WC_GLOBAL Elem *q = in + kEncBlk * g + lane;
+#pragma unroll
+        for (uint32_t i = 0; i < kEncGroup; i++) {
+            if (CHECK) p.e[i] = kEncBlk * g + kLanes * i + lane < len ? q[kLanes * i] : 0u;
+            else p.e[i] = q[kLanes * i];
+        }
+        return p;
     }
-    __device__ Pre fetch_checked(uint32_t e, uint32_t len) const
+    __device__ static uint32_t symbol(uint32_t e)
     {
-        if (e + 8 <= len) return fetch(e);
-        uint32_t v[4] = {0, 0, 0, 0};
-        for (uint32_t i = 0; i < 8; i++)
-            if (e + i < len) v[i >> 1] |= (uint32_t)in[e + i] << (16 * (i & 1));
-        return Pre{u32x4{v[0], v[1], v[2], v[3]}};
-    }
-};
-
-template <>
-struct SymView<WC_FP32> {
-    const WC_GLOBAL uint32_t *in;
-    struct Pre {
-        u32x4 a, b;
-    };
-    __device__ Pre fetch(uint32_t e) const
-    {
-        const WC_GLOBAL u32x4 *p = reinterpret_cast<const WC_GLOBAL u32x4 *>(in + e);
-        return Pre{p[0], p[1]};
-    }
-    // exponent byte of u: bits 23..30
-    __device__ static uint32_t ex(uint32_t u) { return (u >> 23) & 0xFF; }
-    __device__ uint2 bytes(const Pre &p) const
-    {
-        return make_uint2(ex(p.a.x) | ex(p.a.y) << 8 | ex(p.a.z) << 16 | ex(p.a.w) << 24,
-                          ex(p.b.x) | ex(p.b.y) << 8 | ex(p.b.z) << 16 | ex(p.b.w) << 24);
-    }
-    __device__ Pre fetch_checked(uint32_t e, uint32_t len) const
-    {
-        if (e + 8 <= len) return fetch(e);
-        uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (uint32_t i = 0; i < 8; i++)
-            if (e + i < len) v[i] = in[e + i];
-        return Pre{u32x4{v[0], v[1], v[2], v[3]}, u32x4{v[4], v[5], v[6], v[7]}};
+        if constexpr (DT == WC_BF16) return e >> 8;
+        else return (e >> 23) & 0xFF;
     }
 };
 
 // One encode step for one lane: renormalise (the low 16 bits go to the word
 // list, which grows downwards from index p; the lane's rank among the half's
-// emitting lanes orders words within a step) and push the symbol.
+// emitting lanes orders words within a step) and push the symbol.  `store`
+// is false for a half that only shadows its neighbour's chunk.
+// The store is issued by every lane on every step (the compiler can then count
+// outstanding memory operations exactly); a lane with nothing to emit writes
+// into its own state word, which the final states overwrite.
 template <bool CHECK>
-__device__ inline void enc_step(uint32_t &x, uint32_t &p, bool active, const EncSym &e,
-                                WC_GLOBAL uint16_t *words, uint32_t h)
+__device__ inline void enc_step(uint32_t &x, uint32_t &p, bool active, bool store, const EncSym &e,
+                                WC_GLOBAL uint16_t *words, uint32_t h, uint32_t lane)
 {
     const bool emit = (!CHECK || active) && x > e.th;
     const uint64_t m = __ballot(emit);
     const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
     p -= __popc(h ? mh : ml);
     const uint32_t slot = __builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(h ? 0u : ml, p));
-    if (emit) words[slot] = (uint16_t)(x & 0xFFFF);
+    // words[-64 + 2 lane] is the low half of this lane's state word
+    words[emit && store ? (int32_t)slot : (int32_t)(2 * lane) - 64] = (uint16_t)(x & 0xFFFF);
     const uint32_t xr = emit ? x >> 16 : x;
     const uint32_t q = div_exact(xr, e.mp, (e.fm_sh >> 16) & 0xFF, e.fm_sh >> 24);
     const uint32_t xn = xr + __umul24(q, e.fm_sh & 0xFFFF) + e.b;
@@ -287,18 +262,18 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
                                                uint8_t *__restrict__ slots, uint2 *__restrict__ meta,
                                                uint64_t total_chunks)
 {
-    __shared__ EncShared sh;
+    __shared__ EncSym enc[2][256];
     const uint32_t lane = threadIdx.x & 31, h = threadIdx.x >> 5;
-    const uint64_t k = 2ull * blockIdx.x + h;
-    const bool valid = k < total_chunks;
+    // with an odd chunk count the last wavefront's second half shadows the
+    // first half's chunk: it runs the same unchecked code but stores nothing
+    const uint64_t k_own = 2ull * blockIdx.x + h;
+    const bool real = k_own < total_chunks;
+    const uint64_t k = real ? k_own : k_own - 1;
 
-    wc_segment sg{0, 0, 0, 0};
-    uint64_t start = 0;
-    uint32_t len = 0;
-    if (valid) {
-        sg = find_segment(st, k);
-        start = (k - sg.chunk_base) * kChunk;
-        len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
+    const wc_segment sg = find_segment(st, k);
+    const uint64_t start = (k - sg.chunk_base) * kChunk;
+    const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
+    {
         // table: 8 symbols per lane, cumulative start by a scan over the half
         const u32x4 fv = gptr(reinterpret_cast<const u32x4 *>(tables + k * 256))[lane];
         uint32_t f[8] = {fv.x & 0xFFFF, fv.x >> 16, fv.y & 0xFFFF, fv.y >> 16,
@@ -321,70 +296,65 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
             e.th = (fi << 20) - 1u;  // wraps to 0xFFFFFFFF at f = 4096: never renormalise
             e.fm_sh = (kM - fi) | ((l < 1 ? l : 1u) << 16) | ((l > 1 ? l - 1 : 0u) << 24);
             e.b = b;
-            sh.enc[h][8 * lane + i] = e;
+            enc[h][8 * lane + i] = e;
             b += f[i];
         }
     }
     __syncthreads();
 
-    WC_GLOBAL uint8_t *slot = gptr(slots) + (valid ? k : 0) * kSlotBytes;
+    // a shadow half writes into the spare slot after the last chunk's
+    WC_GLOBAL uint8_t *slot = gptr(slots) + (real ? k : total_chunks) * kSlotBytes;
     WC_GLOBAL uint16_t *words = reinterpret_cast<WC_GLOBAL uint16_t *>(slot + 128);
     SymView<DT> sv;
-    using Elem = typename std::conditional<DT == WC_BF16, uint16_t, uint32_t>::type;
-    sv.in = gptr<const Elem>(sg.ptr) + start;
+    sv.in = gptr<const typename SymView<DT>::Elem>(sg.ptr) + start;
     uint32_t x = kL;
     uint32_t p_w = kMaxWords;  // words are written downwards from here
-    const uint8_t *stage = reinterpret_cast<const uint8_t *>(&sh.stage[h][0]);
 
-    // Groups of 8 steps, from the last to the first; both halves run the same
-    // number of groups (the shorter or missing chunk idles).  Full chunks take
-    // the unchecked path.
-    constexpr uint32_t kBlkE = kLanes * kEncGroup;  // 256 symbols per group
-    const uint32_t steps = valid ? (len + kLanes - 1) / kLanes : 0;
-    const uint32_t steps_other = __shfl_xor(steps, 32, 64);
-    const uint32_t ngroups = ((steps > steps_other ? steps : steps_other) + kEncGroup - 1) / kEncGroup;
-    const uint32_t mine_full = (valid && len == kChunk) ? 1u : 0u;
-    const uint32_t other_full = __shfl_xor(mine_full, 32, 64);
-    const bool full = mine_full && other_full;
+    // Groups of 8 steps run from the last to the first.  Groups where every
+    // lane of both halves is active run unchecked; the partial last group of
+    // a shorter chunk runs checked, first.
+    const uint32_t other_len = __shfl_xor(len, 32, 64);
+    const uint32_t ng = ((len > other_len ? len : other_len) + kEncBlk - 1) / kEncBlk;
+    const uint32_t nfull = (len < other_len ? len : other_len) / kEncBlk;
     using Pre = typename SymView<DT>::Pre;
-    auto run = [&](auto check_tag, uint32_t ng) {
+    auto group = [&](auto check_tag, uint32_t g, uint32_t g_next, const Pre &cur, Pre &ahead) {
         constexpr bool CHECK = decltype(check_tag)::value;
-        auto fetch = [&](uint32_t g) -> Pre {
-            const uint32_t e = kBlkE * g + 8 * lane;
-            if constexpr (CHECK) return valid ? sv.fetch_checked(e, len) : Pre{};
-            else return sv.fetch(e);
-        };
-        // a group's input is loaded two groups ahead into one of three
-        // register sets (fixed by unrolling the loop by three)
-        Pre pa = fetch(ng - 1);
-        Pre pb = fetch(ng > 1 ? ng - 2 : ng - 1);
-        Pre pc;
-        auto group = [&](uint32_t gj, const Pre &cur, Pre &ahead) {
-            const uint32_t g = ng - 1 - gj;
-            ahead = fetch(g >= 2 ? g - 2 : g);  // the last groups re-load themselves
-            reinterpret_cast<uint2 *>(&sh.stage[h][0])[lane] = sv.bytes(cur);
-            wave_lds_order();
+        ahead = sv.template fetch<CHECK>(g_next, lane, len);
+        EncSym es[kEncGroup];
 #pragma unroll
-            for (int i = kEncGroup - 1; i >= 0; i--) {
-                const bool active = !CHECK || (valid && kLanes * (kEncGroup * g + i) + lane < len);
-                const EncSym e = sh.enc[h][stage[kLanes * i + lane]];
-                enc_step<CHECK>(x, p_w, active, e, words, h);
-            }
-            wave_lds_order();
-        };
-#pragma unroll 1
-        for (uint32_t gj = 0; gj < ng; gj += 3) {
-            group(gj, pa, pc);
-            if (gj + 1 < ng) group(gj + 1, pb, pa);
-            if (gj + 2 < ng) group(gj + 2, pc, pb);
+        for (uint32_t i = 0; i < kEncGroup; i++) es[i] = enc[h][SymView<DT>::symbol(cur.e[i])];
+#pragma unroll
+        for (int i = kEncGroup - 1; i >= 0; i--) {
+            const bool active = !CHECK || kEncBlk * g + kLanes * i + lane < len;
+            enc_step<CHECK>(x, p_w, active, real, es[i], words, h, lane);
         }
     };
-    if (ngroups) {
-        if (full) run(std::false_type{}, kChunk / kBlkE);
-        else run(std::true_type{}, ngroups);
+    // Groups run from the last to the first.  The groups above the largest
+    // multiple of three below the shorter chunk's full-group count run checked
+    // first; then whole triples of full groups run unchecked, their input
+    // loaded two groups ahead into three register sets in fixed registers.
+    const uint32_t n3 = nfull / 3 * 3;
+    for (uint32_t g = ng; g-- > n3;) {
+        const Pre cur = sv.template fetch<true>(g, lane, len);
+        Pre dummy;
+        group(std::true_type{}, g, g, cur, dummy);
+    }
+    if (n3) {
+        const std::false_type u{};
+        Pre pa = sv.template fetch<false>(n3 - 1, lane, len);
+        Pre pb = sv.template fetch<false>(n3 - 2, lane, len);
+        Pre pc;
+#pragma unroll 1
+        for (uint32_t g = n3; g > 0; g -= 3) {
+            // groups g-1, g-2, g-3, each loading the group two below it (the
+            // last two re-load themselves)
+            group(u, g - 1, g - 3, pa, pc);
+            group(u, g - 2, g >= 4 ? g - 4 : g - 2, pb, pa);
+            group(u, g - 3, g >= 5 ? g - 5 : g - 3, pc, pb);
+        }
     }
 
-    if (valid) {
+    if (real) {
         reinterpret_cast<WC_GLOBAL uint32_t *>(slot)[lane] = x;
         if (lane == 0) {
             const uint32_t nw = kMaxWords - p_w;

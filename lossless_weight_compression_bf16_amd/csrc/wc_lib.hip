@@ -39,7 +39,9 @@ void layout_of(int dtype, uint64_t n, wc_layout *out)
 
 uint64_t scratch_bytes_for(uint64_t chunks)
 {
-    return chunks ? align_up(8 * chunks, 256) + chunks * kSlotBytes : 0;
+    // one slot per chunk plus a spare one written by the idle half of the
+    // last wavefront when the chunk count is odd
+    return chunks ? align_up(8 * chunks, 256) + (chunks + 1) * kSlotBytes : 0;
 }
 
 bool valid_dtype(int d) { return d == WC_BF16 || d == WC_FP32; }
@@ -109,16 +111,17 @@ wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, c
     return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 
-// Decoder variant: when every wavefront fits on the machine at the wide
-// table's occupancy (4 per CU), the run is bound by the serial latency of a
-// chunk and the one-read wide table is faster; with more chunks the narrow
-// table's higher occupancy wins.
-bool use_wide_table(uint64_t waves)
+// Decoder variant.  While every chunk fits on the machine at once with one
+// chunk per wavefront and the wide table (8 wavefronts per CU), the run is
+// bound by the serial latency of one chunk, and the wide table's single LDS
+// read per step with no per-half selects is fastest.  With more chunks the
+// narrow table's two chunks per wavefront and 10 wavefronts per CU win.
+bool use_wide_table(uint64_t chunks)
 {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-    return waves <= 4ull * (uint64_t)cus;
+    return chunks <= 8ull * (uint64_t)cus;
 }
 
 template <int DT>
@@ -126,13 +129,12 @@ wc_status decode_impl(const SegTable &st, uint64_t chunks, const wc_buffers *in,
                       hipStream_t stream)
 {
     if (chunks == 0) return WC_OK;
-    const uint64_t waves = (chunks + 1) / 2;
-    if (use_wide_table(waves)) {
-        hipLaunchKernelGGL((k_decode<DT, true>), dim3((uint32_t)waves), dim3(64), 0, stream, st, in->raw,
+    if (use_wide_table(chunks)) {
+        hipLaunchKernelGGL((k_decode<DT, true, 1>), dim3((uint32_t)chunks), dim3(32), 0, stream, st, in->raw,
                            in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err);
     } else {
-        hipLaunchKernelGGL((k_decode<DT, false>), dim3((uint32_t)waves), dim3(64), 0, stream, st, in->raw,
-                           in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err);
+        hipLaunchKernelGGL((k_decode<DT, false, 2>), dim3((uint32_t)((chunks + 1) / 2)), dim3(64), 0, stream, st,
+                           in->raw, in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err);
     }
     return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
 }

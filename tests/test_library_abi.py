@@ -50,7 +50,7 @@ def test_layout_matches_oracle(L, oracle_lib, dtype, n):
     for k in ("n", "num_chunks", "raw_bytes", "table_bytes", "seek_bytes", "payload_capacity"):
         assert a[k] == getattr(b, k), k
     c = a["num_chunks"]
-    assert a["scratch_bytes"] == (0 if c == 0 else ((8 * c + 255) // 256) * 256 + c * 131200)
+    assert a["scratch_bytes"] == (0 if c == 0 else ((8 * c + 255) // 256) * 256 + (c + 1) * 131200)
 
 
 def test_plan_batch_matches_oracle(L, oracle_lib):
