@@ -47,6 +47,7 @@ __device__ inline WC_GLOBAL T *gptr(T *p)
 
 // Native 16-byte vector (loads as one global_load_dwordx4).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Segment view handed to every kernel: either one inline tensor (nseg == 0)
 // or a device array of planned segments.

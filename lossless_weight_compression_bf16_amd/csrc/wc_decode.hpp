@@ -33,13 +33,15 @@ namespace wc {
 constexpr uint32_t kGroup = 8;                     // steps per group
 constexpr uint32_t kBlk = kLanes * kGroup;         // words per refill (max consumed per group)
 constexpr uint32_t kRingWords = 4 * kBlk;          // live words stay below 3 kBlk
+constexpr uint32_t kApron = kLanes;                // ring words 0..31 mirrored after the end
+constexpr uint32_t kRingAlloc = kRingWords + kApron;
 constexpr uint32_t kStageBytes = kLanes * kGroup;  // decoded bytes per group per half
 
 // H = chunks per wavefront (one per 32-lane half)
 template <int H>
 struct DecSharedL1 {
     uint32_t tab[H][kM];                    // per slot: sym | (f-1) << 8 | (slot-b) << 20
-    uint32_t ring[H][kRingWords / 2];
+    uint32_t ring[H][kRingAlloc / 2];
     uint32_t stage[H][kStageBytes / 4];
 };
 
@@ -47,7 +49,7 @@ template <int H>
 struct DecSharedL2 {
     uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
     uint32_t fb[H][256];                    // b | (f - 4096) << 16
-    uint32_t ring[H][kRingWords / 2];
+    uint32_t ring[H][kRingAlloc / 2];
     uint32_t stage[H][kStageBytes / 4];
 };
 
@@ -93,6 +95,9 @@ __device__ inline void refill_commit(Stream &st, uint32_t lane, const Refill &r,
         if (r.shift >= 4) v = u32x4{0u, 0u, 0u, 0u};
         const uint32_t d0 = (st.fill / 2 + 4 * lane) & (kRingWords / 2 - 1);
         *reinterpret_cast<u32x4 *>(ring + d0) = v;
+        // a read of 32 words starting anywhere in the ring never wraps: the
+        // first 32 words are repeated after the end
+        if (d0 < kApron / 2) *reinterpret_cast<u32x4 *>(ring + kRingWords / 2 + d0) = v;
         st.fill += kBlk;
     }
 }
@@ -224,22 +229,32 @@ struct Lookup<false> {
 };
 
 // One decode step of one lane: table lookup, renormalisation from the ring
-// (rank among the half's renormalising lanes via ballot + mbcnt), decoded
-// byte into the group's stage.
-template <bool kL1, bool CHECK, typename Sh>
-__device__ inline void dec_step(uint32_t &x, uint32_t &ptr, Sh &sh, uint32_t h, uint32_t lane, bool active,
-                                uint32_t i)
+// (rank among the half's renormalising lanes via ballot + mbcnt, added to
+// the ring position of the half's next word), decoded byte into the group's
+// stage.  rpos is the absolute stream cursor modulo the ring size, kept in a
+// VGPR so the rank needs no extra move on the serial chain.
+template <bool kL1, bool CHECK, int kH, typename Sh>
+__device__ inline void dec_step(uint32_t &x, uint32_t &ptr, uint32_t &rpos, Sh &sh, uint32_t h, uint32_t lane,
+                                bool active, uint32_t i)
 {
     uint32_t s;
     const uint32_t xd = Lookup<kL1>::step(sh, h, x, s);
     const bool need = (!CHECK || active) && xd < kL;
     const uint64_t m = __ballot(need);
     const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
-    const uint32_t widx = __builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(h ? 0u : ml, ptr));
-    const uint16_t *ring = reinterpret_cast<const uint16_t *>(&sh.ring[0][0]);
-    const uint32_t w = ring[(widx & (kRingWords - 1)) | (h << 10)];
-    ptr += __popc(h ? mh : ml);
-    if (!CHECK || active) x = need ? (xd << 16) | w : xd;
+    uint32_t widx;
+    if constexpr (kH == 1) widx = __builtin_amdgcn_mbcnt_lo(ml, rpos);
+    else widx = __builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(h ? 0u : ml, rpos));
+    const uint16_t *ring = reinterpret_cast<const uint16_t *>(&sh.ring[h][0]);
+    const uint32_t w = ring[widx];  // widx < kRingWords + 32: no wrap
+    // x = need ? xd << 16 | w : xd, as one byte permute of (xd, w)
+    const uint32_t sel = need ? 0x05040100u : 0x07060504u;
+    const uint32_t xn = __builtin_amdgcn_perm(xd, w, sel);
+    const uint32_t cnt = __popc(kH == 1 ? ml : (h ? mh : ml));
+    ptr += cnt;
+    rpos = (rpos + cnt) & (kRingWords - 1);
+    asm volatile("" : "+v"(rpos));
+    if (!CHECK || active) x = xn;
     reinterpret_cast<uint8_t *>(&sh.stage[h][0])[kLanes * i + lane] = (uint8_t)s;
 }
 
@@ -373,6 +388,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     const uint32_t nfull = lo_len / kBlk;
     using Pre = typename RawView<DT>::Pre;
     Refill pend{u32x4{0, 0, 0, 0}, 0, false};
+    uint32_t rpos = 0;  // cs.ptr modulo the ring size
     auto group = [&](auto check_tag, uint32_t gg, uint32_t g_last, const Pre &cur, Pre &ahead) {
         constexpr bool CHECK = decltype(check_tag)::value;
         refill_commit(cs, lane, pend, sh.ring[h]);
@@ -384,7 +400,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
 #pragma unroll
         for (uint32_t i = 0; i < kGroup; i++) {
             const bool active = !CHECK || (ok && kLanes * (kGroup * gg + i) + lane < len);
-            dec_step<kL1, CHECK>(x, cs.ptr, sh, h, lane, active, i);
+            dec_step<kL1, CHECK, kH>(x, cs.ptr, rpos, sh, h, lane, active, i);
         }
         wave_lds_order();
         if constexpr (CHECK) {

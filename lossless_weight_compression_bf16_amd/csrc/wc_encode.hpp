@@ -1,9 +1,10 @@
 // wc_encode.hpp -- encoder kernels for gfx950.
 //
 //   k_split_hist  one 256-thread block per chunk: coalesced 16-byte loads of
-//                 the tensor, raw planes written back with vector stores, the
-//                 coded plane counted into LDS sub-histograms, then the
-//                 chunk's 12-bit table built with integer arithmetic only.
+//                 the tensor (four in flight per thread), raw planes written
+//                 back with vector stores, the coded plane counted into
+//                 per-lane LDS sub-histograms, then the chunk's 12-bit table
+//                 built with integer arithmetic only.
 //   k_encode      one wavefront per two chunks (one chunk per 32-lane half):
 //                 32 interleaved rANS states, reverse order, words written
 //                 downwards into the chunk's scratch slot.
@@ -105,13 +106,24 @@ __device__ inline uint32_t normalize256(uint32_t c, uint32_t T, uint32_t *red, u
 
 // ------------------------------------------------------------ split + table
 
+// Per-lane sub-histograms: lane c of every wavefront counts into copy c,
+// two 16-bit counters per word (a copy sees at most 4 x 256 = 1024 symbols
+// of a chunk, so counters never carry into their neighbour).  No two lanes
+// of one LDS atomic ever hit the same word; the odd stride spreads the copies
+// over the banks.
+constexpr uint32_t kHistCopies = 64;
+constexpr uint32_t kHistStride = 129;
+
+__device__ inline void hist_add(uint32_t *my, uint32_t b)
+{
+    atomicAdd(&my[b >> 1], 1u << ((b & 1u) << 4));
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__restrict__ raw,
                                                     uint16_t *__restrict__ tables, uint64_t raw_total)
 {
-    constexpr int kCopies = 8;             // one sub-histogram per 32 threads
-    constexpr int kStride = 257;           // pad: copies land on different banks
-    __shared__ uint32_t hist[kCopies * kStride];
+    __shared__ uint32_t hist[kHistCopies * kHistStride];
     __shared__ uint32_t red[4];
     __shared__ uint32_t keys[256];
 
@@ -121,7 +133,7 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
     const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
     const uint32_t tid = threadIdx.x;
 
-    for (uint32_t i = tid; i < kCopies * kStride; i += 256) hist[i] = 0;
+    for (uint32_t i = tid; i < kHistCopies * kHistStride; i += 256) hist[i] = 0;
     // the segment's last chunk zeroes the alignment gap after its raw planes
     if (start + len == sg.n) {
         const uint64_t end = sg.raw_base + raw_bytes_of(DT, sg.n);
@@ -129,43 +141,57 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
         if (end + tid < pad_end) raw[end + tid] = 0;
     }
     __syncthreads();
-    uint32_t *my = hist + (tid >> 5) * kStride;
+    uint32_t *my = hist + (tid & 63) * kHistStride;
 
     if constexpr (DT == WC_BF16) {
         const WC_GLOBAL uint16_t *in = gptr<uint16_t>(sg.ptr) + start;
-        uint8_t *lo = raw + sg.raw_base + start;
-        const uint32_t ng = len / 8;
-        for (uint32_t g = tid; g < ng; g += 256) {
+        WC_GLOBAL uint8_t *lo = gptr(raw) + sg.raw_base + start;
+        const uint32_t ng = len / 8;  // groups of 8 elements = 16 bytes
+        // four 16-byte loads in flight per thread
+        constexpr uint32_t U = 4;
+        uint32_t g = tid;
+        for (; g + 256 * (U - 1) < ng; g += 256 * U) {
+            u32x4 v[U];
+#pragma unroll
+            for (uint32_t u = 0; u < U; u++) v[u] = reinterpret_cast<const WC_GLOBAL u32x4 *>(in)[g + 256 * u];
+#pragma unroll
+            for (uint32_t u = 0; u < U; u++) {
+                const u32x2 l = u32x2{__builtin_amdgcn_perm(v[u].y, v[u].x, 0x06040200u),
+                                      __builtin_amdgcn_perm(v[u].w, v[u].z, 0x06040200u)};
+                reinterpret_cast<WC_GLOBAL u32x2 *>(lo)[g + 256 * u] = l;
+                const uint32_t h0 = __builtin_amdgcn_perm(v[u].y, v[u].x, 0x07050301u);
+                const uint32_t h1 = __builtin_amdgcn_perm(v[u].w, v[u].z, 0x07050301u);
+#pragma unroll
+                for (uint32_t i = 0; i < 4; i++) hist_add(my, (h0 >> (8 * i)) & 0xFF);
+#pragma unroll
+                for (uint32_t i = 0; i < 4; i++) hist_add(my, (h1 >> (8 * i)) & 0xFF);
+            }
+        }
+        for (; g < ng; g += 256) {
             const u32x4 v = reinterpret_cast<const WC_GLOBAL u32x4 *>(in)[g];
-            uint2 l;
-            l.x = __builtin_amdgcn_perm(v.y, v.x, 0x06040200u);
-            l.y = __builtin_amdgcn_perm(v.w, v.z, 0x06040200u);
-            reinterpret_cast<uint2 *>(lo)[g] = l;
+            const u32x2 l = u32x2{__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
+                                  __builtin_amdgcn_perm(v.w, v.z, 0x06040200u)};
+            reinterpret_cast<WC_GLOBAL u32x2 *>(lo)[g] = l;
             const uint32_t h0 = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
             const uint32_t h1 = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
-            atomicAdd(&my[h0 & 0xFF], 1u);
-            atomicAdd(&my[(h0 >> 8) & 0xFF], 1u);
-            atomicAdd(&my[(h0 >> 16) & 0xFF], 1u);
-            atomicAdd(&my[h0 >> 24], 1u);
-            atomicAdd(&my[h1 & 0xFF], 1u);
-            atomicAdd(&my[(h1 >> 8) & 0xFF], 1u);
-            atomicAdd(&my[(h1 >> 16) & 0xFF], 1u);
-            atomicAdd(&my[h1 >> 24], 1u);
+            for (uint32_t i = 0; i < 4; i++) hist_add(my, (h0 >> (8 * i)) & 0xFF);
+            for (uint32_t i = 0; i < 4; i++) hist_add(my, (h1 >> (8 * i)) & 0xFF);
         }
         for (uint32_t i = ng * 8 + tid; i < len; i += 256) {
-            const uint16_t e = in[i];
+            const uint32_t e = in[i];
             lo[i] = (uint8_t)(e & 0xFF);
-            atomicAdd(&my[e >> 8], 1u);
+            hist_add(my, e >> 8);
         }
     } else {
         // FP32: exponent counted; raw = sign bits | m0 | m1 | m2 (plane bases
-        // follow the segment's element count).
+        // follow the segment's element count, so the mantissa planes have no
+        // alignment guarantee: byte stores)
         const WC_GLOBAL uint32_t *in = gptr<uint32_t>(sg.ptr) + start;
         const uint64_t sb = (sg.n + 7) / 8;
-        uint8_t *sign = raw + sg.raw_base + start / 8;
-        uint8_t *m0 = raw + sg.raw_base + sb + start;
-        uint8_t *m1 = m0 + sg.n;
-        uint8_t *m2 = m1 + sg.n;
+        WC_GLOBAL uint8_t *sign = gptr(raw) + sg.raw_base + start / 8;
+        WC_GLOBAL uint8_t *m0 = gptr(raw) + sg.raw_base + sb + start;
+        WC_GLOBAL uint8_t *m1 = m0 + sg.n;
+        WC_GLOBAL uint8_t *m2 = m1 + sg.n;
         const uint32_t ng = (len + 7) / 8;  // groups of 8 elements = one sign byte
         for (uint32_t g = tid; g < ng; g += 256) {
             uint32_t sbyte = 0;
@@ -173,7 +199,7 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
                 const uint32_t j = 8 * g + i;
                 if (j >= len) break;
                 const uint32_t u = in[j];
-                atomicAdd(&my[(u >> 23) & 0xFF], 1u);
+                hist_add(my, (u >> 23) & 0xFF);
                 sbyte |= (u >> 31) << i;
                 m0[j] = (uint8_t)(u & 0xFF);
                 m1[j] = (uint8_t)((u >> 8) & 0xFF);
@@ -184,8 +210,11 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
     }
     __syncthreads();
 
+    // thread s sums symbol s over the 64 copies
     uint32_t c = 0;
-    for (int i = 0; i < kCopies; i++) c += hist[i * kStride + tid];
+    const uint32_t word = tid >> 1, shift = (tid & 1) << 4;
+#pragma unroll 8
+    for (uint32_t i = 0; i < kHistCopies; i++) c += (hist[i * kHistStride + word] >> shift) & 0xFFFF;
     const uint32_t f = normalize256(c, len, red, keys);
     tables[k * 256 + tid] = (uint16_t)f;
 }
