@@ -1,0 +1,110 @@
+"""Full-size weight sets on the GPU: the whole set is encoded and decoded
+as one batch (the launch configuration the benchmark times), every tensor
+must round-trip bit for bit, and sampled chunks (first, last/tail and
+random ones) are checked byte for byte against the oracle, which regenerates
+each sampled chunk's input on its own from the seeded generator.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import lossless_weight_compression_bf16_amd as wc  # noqa: E402
+from lossless_weight_compression_bf16_amd import codec, synthetic as S  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    wc.lib()
+    return torch.device("cuda:0")
+
+
+def _upload_set(w, dev):
+    t0 = time.time()
+    ts = []
+    ity = np.int16 if w.dtype == "bf16" else np.int32
+    for i in range(len(w.shapes)):
+        x = S.tensor_bits(w, i, threads=16)
+        ts.append(torch.from_numpy(x.view(ity)).to(dev))
+        if i % 64 == 63:
+            _say(f"[full] {w.name}: generated {i + 1}/{len(w.shapes)} tensors ({time.time() - t0:.0f} s)")
+    _say(f"[full] {w.name}: {w.n} elements resident ({time.time() - t0:.0f} s)")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return [t.view(tdt) for t in ts]
+
+
+def _sample_chunks(w, rng, count):
+    numels = w.numels
+    chunks = [(n + 65535) // 65536 for n in numels]
+    picks = {(0, 0), (len(numels) - 1, chunks[-1] - 1)}
+    for i in range(len(numels)):
+        if numels[i] % 65536:
+            picks.add((i, chunks[i] - 1))  # tail chunks
+            if len(picks) > count // 2:
+                break
+    while len(picks) < count:
+        i = int(rng.integers(0, len(numels)))
+        picks.add((i, int(rng.integers(0, chunks[i]))))
+    base = np.concatenate([[0], np.cumsum(chunks)])
+    return sorted((i, k, int(base[i] + k)) for i, k in picks)
+
+
+def _check_set(name, oracle_lib, dev, samples=48):
+    w = S.workload(name)
+    ts = _upload_set(w, dev)
+    e = codec.encode_batch(ts)
+    torch.cuda.synchronize()
+    _say(f"[full] {name}: encoded, ratio {e.ratio:.4f}, payload {e.payload.numel()} B")
+    outs = codec.decode_batch(e)
+    torch.cuda.synchronize()
+    ity = torch.int16 if w.dtype == "bf16" else torch.int32
+    for t, y in zip(ts, outs):
+        assert torch.equal(t.view(ity), y.view(ity))
+    del outs
+    _say(f"[full] {name}: every tensor round-trips")
+    seek = e.seek.cpu().numpy().view("<u8")
+    assert seek[0] == 0 and np.all(np.diff(seek.astype(np.int64)) >= 128)
+    assert np.all(seek % 4 == 0)
+    rng = np.random.default_rng(123)
+    cb, rb, _ = oracle_lib.plan_batch(w.dtype, w.numels)
+    for i, kl, k in _sample_chunks(w, rng, samples):
+        x = S.chunk_bits(w, i, kl)
+        if w.dtype == "bf16":
+            sym, lo = oracle_lib.split_bf16(x)
+            raw_ref = lo
+        else:
+            sym, raw_all = oracle_lib.split_fp32(x)
+            raw_ref = None
+        f = oracle_lib.normalize(oracle_lib.histogram(sym))
+        p = oracle_lib.encode_chunk(sym, f)
+        got_t = e.tables[k].cpu().numpy().view("<u2")
+        assert np.array_equal(got_t, f), (name, i, kl)
+        got_p = e.payload[int(seek[k]): int(seek[k + 1])].cpu().numpy()
+        assert np.array_equal(got_p, p), (name, i, kl)
+        if raw_ref is not None:
+            r0 = int(rb[i]) + 65536 * kl
+            assert np.array_equal(e.raw[r0: r0 + raw_ref.size].cpu().numpy(), raw_ref), (name, i, kl)
+    _say(f"[full] {name}: {samples} sampled chunks match the oracle")
+    return e
+
+
+def test_llama3_8b_set(dev, oracle_lib):
+    e = _check_set("llama3-8b-bf16", oracle_lib, dev)
+    assert 0.66 < e.ratio < 0.69
+
+
+def test_moe_experts_set(dev, oracle_lib):
+    e = _check_set("moe-experts-bf16", oracle_lib, dev)
+    assert 0.66 < e.ratio < 0.70
