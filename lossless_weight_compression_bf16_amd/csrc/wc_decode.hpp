@@ -32,7 +32,10 @@ namespace wc {
 
 constexpr uint32_t kGroup = 8;                     // steps per group
 constexpr uint32_t kBlk = kLanes * kGroup;         // words per refill (max consumed per group)
-constexpr uint32_t kRingWords = 4 * kBlk;          // live words stay below 3 kBlk
+// Ring of three blocks: a refill is issued only while fewer than two blocks
+// are unconsumed and lands one group later, after at most one block more
+// was consumed, so live words plus the landing block never exceed three.
+constexpr uint32_t kRingWords = 3 * kBlk;
 constexpr uint32_t kApron = kLanes;                // ring words 0..31 mirrored after the end
 constexpr uint32_t kRingAlloc = kRingWords + kApron;
 constexpr uint32_t kStageBytes = kLanes * kGroup;  // decoded bytes per group per half
@@ -59,6 +62,7 @@ struct Stream {
     uint32_t nw;                      // words in the chunk (pad included, even)
     uint32_t ptr;                     // next word to consume
     uint32_t fill;                    // words written to the ring
+    uint32_t fpos;                    // fill modulo the ring size
 };
 
 // A refill moves the next 256-word block into the ring, 16 bytes per lane.
@@ -93,12 +97,13 @@ __device__ inline void refill_commit(Stream &st, uint32_t lane, const Refill &r,
         if (r.shift >= 2) v = u32x4{v.z, v.w, 0u, 0u};
         if (r.shift & 1) v = u32x4{v.y, v.z, v.w, 0u};
         if (r.shift >= 4) v = u32x4{0u, 0u, 0u, 0u};
-        const uint32_t d0 = (st.fill / 2 + 4 * lane) & (kRingWords / 2 - 1);
+        const uint32_t d0 = st.fpos / 2 + 4 * lane;
         *reinterpret_cast<u32x4 *>(ring + d0) = v;
         // a read of 32 words starting anywhere in the ring never wraps: the
         // first 32 words are repeated after the end
         if (d0 < kApron / 2) *reinterpret_cast<u32x4 *>(ring + kRingWords / 2 + d0) = v;
         st.fill += kBlk;
+        st.fpos = st.fpos + kBlk < kRingWords ? st.fpos + kBlk : 0u;
     }
 }
 
@@ -205,7 +210,7 @@ struct Lookup;
 template <>
 struct Lookup<true> {
     template <typename Sh>
-    __device__ static inline uint32_t step(const Sh &sh, uint32_t h, uint32_t x, uint32_t &s)
+    __device__ static inline uint32_t step(const Sh &sh, uint32_t h, uint32_t, uint32_t x, uint32_t &s)
     {
         const uint32_t e = sh.tab[h][x & (kM - 1)];
         const uint32_t q = x >> kScaleBits;
@@ -218,12 +223,15 @@ struct Lookup<true> {
 // f q + slot - b == x - b + (f - 4096) q  (mod 2^32), one signed 24-bit mad.
 template <>
 struct Lookup<false> {
+    // sb = 4096 h and fbb = 1024 h: the half's table bases, opaque to the
+    // compiler so each table address is a single and-or / shift-or
     template <typename Sh>
-    __device__ static inline uint32_t step(const Sh &sh, uint32_t h, uint32_t x, uint32_t &s)
+    __device__ static inline uint32_t step(const Sh &sh, uint32_t sb, uint32_t fbb, uint32_t x, uint32_t &s)
     {
         const uint8_t *sym = reinterpret_cast<const uint8_t *>(&sh.sym[0][0]);
-        s = sym[(x & (kM - 1)) | (h << 12)];
-        const uint32_t fb = sh.fb[h][s];
+        s = sym[(x & (kM - 1)) | sb];
+        const uint8_t *fbt = reinterpret_cast<const uint8_t *>(&sh.fb[0][0]);
+        const uint32_t fb = *reinterpret_cast<const uint32_t *>(fbt + ((s << 2) | fbb));
         return (uint32_t)__mul24((int32_t)fb >> 16, (int32_t)(x >> kScaleBits)) + (x - (fb & 0xFFFF));
     }
 };
@@ -238,13 +246,26 @@ __device__ inline void dec_step(uint32_t &x, uint32_t &ptr, uint32_t &rpos, Sh &
                                 bool active, uint32_t i)
 {
     uint32_t s;
-    const uint32_t xd = Lookup<kL1>::step(sh, h, x, s);
+    uint32_t b0 = h, b1 = 0;
+    if constexpr (!kL1) {
+        b0 = h << 12;
+        b1 = h << 10;
+        asm volatile("" : "+v"(b0), "+v"(b1));
+    }
+    const uint32_t xd = Lookup<kL1>::step(sh, b0, b1, x, s);
     const bool need = (!CHECK || active) && xd < kL;
     const uint64_t m = __ballot(need);
     const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
     uint32_t widx;
-    if constexpr (kH == 1) widx = __builtin_amdgcn_mbcnt_lo(ml, rpos);
-    else widx = __builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(h ? 0u : ml, rpos));
+    if constexpr (kH == 1) {
+        widx = __builtin_amdgcn_mbcnt_lo(ml, rpos);
+    } else {
+        // rank within the own half: lanes 0-31 count the low mask, lanes
+        // 32-63 the high one (mbcnt_hi adds nothing below lane 32)
+        const uint32_t lo = __builtin_amdgcn_mbcnt_lo(ml, rpos);
+        const uint32_t hi = __builtin_amdgcn_mbcnt_hi(mh, rpos);
+        widx = h ? hi : lo;
+    }
     const uint16_t *ring = reinterpret_cast<const uint16_t *>(&sh.ring[h][0]);
     const uint32_t w = ring[widx];  // widx < kRingWords + 32: no wrap
     // x = need ? xd << 16 | w : xd, as one byte permute of (xd, w)
@@ -252,7 +273,7 @@ __device__ inline void dec_step(uint32_t &x, uint32_t &ptr, uint32_t &rpos, Sh &
     const uint32_t xn = __builtin_amdgcn_perm(xd, w, sel);
     const uint32_t cnt = __popc(kH == 1 ? ml : (h ? mh : ml));
     ptr += cnt;
-    rpos = (rpos + cnt) & (kRingWords - 1);
+    rpos = rpos + cnt < kRingWords ? rpos + cnt : rpos + cnt - kRingWords;
     asm volatile("" : "+v"(rpos));
     if (!CHECK || active) x = xn;
     reinterpret_cast<uint8_t *>(&sh.stage[h][0])[kLanes * i + lane] = (uint8_t)s;
@@ -328,7 +349,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     const wc_segment sg = find_segment(st, k);
     const uint64_t start = (k - sg.chunk_base) * kChunk;
     const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
-    Stream cs{nullptr, 0, 0, 0};
+    Stream cs{nullptr, 0, 0, 0, 0};
     uint32_t x = kL;
     {
         const uint64_t a = seek[k], b = seek[k + 1];
