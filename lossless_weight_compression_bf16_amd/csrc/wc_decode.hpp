@@ -15,8 +15,10 @@
 //                            there are enough chunks to fill the machine;
 //   - a 1024-word ring of the compressed stream, refilled 256 words at a
 //     time: a refill is loaded at the start of a group of 8 steps and
-//     written to the ring at the start of the next group, so the word fetch
-//     of a step is an LDS read and never waits for HBM;
+//     written to the ring at the start of the group after next, so the
+//     load has two groups to land and the word fetch of a step is an LDS
+//     read that never waits for HBM.  The ring size is a power of two, so a
+//     lane's word address is its stream position masked;
 //   - the 256 decoded bytes of the current group.
 // At the end of a group each lane joins 8 consecutive decoded bytes with 8
 // raw bytes (loaded with one 8-byte load issued two groups earlier) and
@@ -32,19 +34,19 @@ namespace wc {
 
 constexpr uint32_t kGroup = 8;                     // steps per group
 constexpr uint32_t kBlk = kLanes * kGroup;         // words per refill (max consumed per group)
-// Ring of three blocks: a refill is issued only while fewer than two blocks
-// are unconsumed and lands one group later, after at most one block more
-// was consumed, so live words plus the landing block never exceed three.
-constexpr uint32_t kRingWords = 3 * kBlk;
-constexpr uint32_t kApron = kLanes;                // ring words 0..31 mirrored after the end
-constexpr uint32_t kRingAlloc = kRingWords + kApron;
+// Words issued (landed or in flight) run at most three blocks ahead of the
+// read position when a refill is issued; it lands two groups later, when
+// the read position has not moved back, so the landing block never covers
+// an unconsumed word of the four-block ring.  With three blocks prefilled,
+// every group finds the (up to) 256 words it consumes already landed.
+constexpr uint32_t kRingWords = 4 * kBlk;
 constexpr uint32_t kStageBytes = kLanes * kGroup;  // decoded bytes per group per half
 
 // H = chunks per wavefront (one per 32-lane half)
 template <int H>
 struct DecSharedL1 {
     uint32_t tab[H][kM];                    // per slot: sym | (f-1) << 8 | (slot-b) << 20
-    uint32_t ring[H][kRingAlloc / 2];
+    uint32_t ring[H][kRingWords / 2];
     uint32_t stage[H][kStageBytes / 4];
 };
 
@@ -52,7 +54,7 @@ template <int H>
 struct DecSharedL2 {
     uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
     uint32_t fb[H][256];                    // b | (f - 4096) << 16
-    uint32_t ring[H][kRingAlloc / 2];
+    uint32_t ring[H][kRingWords / 2];
     uint32_t stage[H][kStageBytes / 4];
 };
 
@@ -61,8 +63,7 @@ struct Stream {
     const WC_GLOBAL uint32_t *words;  // payload + seek[k] + 128, as dwords
     uint32_t nw;                      // words in the chunk (pad included, even)
     uint32_t ptr;                     // next word to consume
-    uint32_t fill;                    // words written to the ring
-    uint32_t fpos;                    // fill modulo the ring size
+    uint32_t fill;                    // words issued to the ring (landed or in flight)
 };
 
 // A refill moves the next 256-word block into the ring, 16 bytes per lane.
@@ -73,38 +74,43 @@ struct Stream {
 struct Refill {
     u32x4 v;
     uint32_t shift;  // dwords between the wanted start and the loaded start
+    uint32_t pos;    // ring dword offset of the lane's 16 bytes
     bool go;
 };
 
-__device__ inline Refill refill_issue(const Stream &st, uint32_t lane, bool on)
+__device__ inline Refill refill_none()
+{
+    return Refill{u32x4{0u, 0u, 0u, 0u}, 0u, 0u, false};
+}
+
+__device__ inline Refill refill_issue(Stream &st, uint32_t lane, bool on)
 {
     Refill r;
-    r.go = on && st.fill - st.ptr < 2 * kBlk && st.fill < st.nw;
+    r.go = on && st.fill - st.ptr < 3 * kBlk && st.fill < st.nw;
     const int32_t d0 = (int32_t)(st.fill / 2 + 4 * lane), ndw = (int32_t)(st.nw / 2);
     // [dl, dl + 4) lies in [-32, ndw): the words area or the 128-byte state
     // area in front of it
     const int32_t dl = r.go ? (d0 + 4 <= ndw ? d0 : ndw - 4) : -32;
     r.v = *reinterpret_cast<const WC_GLOBAL u32x4 *>(st.words + dl);
     r.shift = (uint32_t)(d0 - dl);
+    r.pos = (st.fill & (kRingWords - 1)) / 2 + 4 * lane;
+    if (r.go) st.fill += kBlk;
     return r;
 }
 
-__device__ inline void refill_commit(Stream &st, uint32_t lane, const Refill &r, uint32_t *ring)
+__device__ inline void refill_commit(const Refill &r, uint32_t *ring)
 {
-    if (r.go) {
-        // dwords past the stream end are never consumed by a valid stream
-        u32x4 v = r.v;
-        if (r.shift >= 2) v = u32x4{v.z, v.w, 0u, 0u};
-        if (r.shift & 1) v = u32x4{v.y, v.z, v.w, 0u};
-        if (r.shift >= 4) v = u32x4{0u, 0u, 0u, 0u};
-        const uint32_t d0 = st.fpos / 2 + 4 * lane;
-        *reinterpret_cast<u32x4 *>(ring + d0) = v;
-        // a read of 32 words starting anywhere in the ring never wraps: the
-        // first 32 words are repeated after the end
-        if (d0 < kApron / 2) *reinterpret_cast<u32x4 *>(ring + kRingWords / 2 + d0) = v;
-        st.fill += kBlk;
-        st.fpos = st.fpos + kBlk < kRingWords ? st.fpos + kBlk : 0u;
+    u32x4 v = r.v;
+    // Lanes at the stream end loaded the last 16 in-bounds bytes: move the
+    // wanted dwords down; what lies past the end is never consumed by a
+    // valid stream and is zeroed.  Once per chunk, so a wave-level branch.
+    if (__ballot(r.go && r.shift != 0)) {
+        const uint32_t sh = r.go ? r.shift : 0u;
+        if (sh & 1) v = u32x4{v.y, v.z, v.w, 0u};
+        if (sh & 2) v = u32x4{v.z, v.w, 0u, 0u};
+        if (sh >= 4) v = u32x4{0u, 0u, 0u, 0u};
     }
+    if (r.go) *reinterpret_cast<u32x4 *>(ring + r.pos) = v;
 }
 
 // ----------------------------------------------------------- raw plane views
@@ -223,8 +229,7 @@ struct Lookup<true> {
 // f q + slot - b == x - b + (f - 4096) q  (mod 2^32), one signed 24-bit mad.
 template <>
 struct Lookup<false> {
-    // sb = 4096 h and fbb = 1024 h: the half's table bases, opaque to the
-    // compiler so each table address is a single and-or / shift-or
+    // sb = 4096 h and fbb = 1024 h: byte offsets of the half's tables
     template <typename Sh>
     __device__ static inline uint32_t step(const Sh &sh, uint32_t sb, uint32_t fbb, uint32_t x, uint32_t &s)
     {
@@ -238,44 +243,40 @@ struct Lookup<false> {
 
 // One decode step of one lane: table lookup, renormalisation from the ring
 // (rank among the half's renormalising lanes via ballot + mbcnt, added to
-// the ring position of the half's next word), decoded byte into the group's
-// stage.  rpos is the absolute stream cursor modulo the ring size, kept in a
-// VGPR so the rank needs no extra move on the serial chain.
+// the stream position of the half's next word), decoded byte into the
+// group's stage.  b0, b1 are the half's table bases and hs = 32 h, all held
+// opaque so every address is one instruction.
 template <bool kL1, bool CHECK, int kH, typename Sh>
-__device__ inline void dec_step(uint32_t &x, uint32_t &ptr, uint32_t &rpos, Sh &sh, uint32_t h, uint32_t lane,
-                                bool active, uint32_t i)
+__device__ inline void dec_step(uint32_t &x, uint32_t &ptr, Sh &sh, uint32_t b0, uint32_t b1, uint32_t hs,
+                                uint32_t h, uint32_t lane, bool active, uint32_t i)
 {
     uint32_t s;
-    uint32_t b0 = h, b1 = 0;
-    if constexpr (!kL1) {
-        b0 = h << 12;
-        b1 = h << 10;
-        asm volatile("" : "+v"(b0), "+v"(b1));
-    }
     const uint32_t xd = Lookup<kL1>::step(sh, b0, b1, x, s);
     const bool need = (!CHECK || active) && xd < kL;
     const uint64_t m = __ballot(need);
     const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
-    uint32_t widx;
+    uint32_t widx, half;
     if constexpr (kH == 1) {
-        widx = __builtin_amdgcn_mbcnt_lo(ml, rpos);
+        widx = __builtin_amdgcn_mbcnt_lo(ml, ptr);
+        half = ml;
     } else {
         // rank within the own half: lanes 0-31 count the low mask, lanes
         // 32-63 the high one (mbcnt_hi adds nothing below lane 32)
-        const uint32_t lo = __builtin_amdgcn_mbcnt_lo(ml, rpos);
-        const uint32_t hi = __builtin_amdgcn_mbcnt_hi(mh, rpos);
+        const uint32_t lo = __builtin_amdgcn_mbcnt_lo(ml, ptr);
+        const uint32_t hi = __builtin_amdgcn_mbcnt_hi(mh, ptr);
         widx = h ? hi : lo;
+        half = (uint32_t)(m >> hs);
     }
     const uint16_t *ring = reinterpret_cast<const uint16_t *>(&sh.ring[h][0]);
-    const uint32_t w = ring[widx];  // widx < kRingWords + 32: no wrap
+    const uint32_t w = ring[widx & (kRingWords - 1)];
     // x = need ? xd << 16 | w : xd, as one byte permute of (xd, w)
     const uint32_t sel = need ? 0x05040100u : 0x07060504u;
     const uint32_t xn = __builtin_amdgcn_perm(xd, w, sel);
-    const uint32_t cnt = __popc(kH == 1 ? ml : (h ? mh : ml));
-    ptr += cnt;
-    rpos = rpos + cnt < kRingWords ? rpos + cnt : rpos + cnt - kRingWords;
-    asm volatile("" : "+v"(rpos));
+    ptr += __popc(half);
     if (!CHECK || active) x = xn;
+    // the byte store must not see the table byte itself: then the symbol
+    // load would be an any-extending one and need a mask
+    asm("" : "+v"(s));
     reinterpret_cast<uint8_t *>(&sh.stage[h][0])[kLanes * i + lane] = (uint8_t)s;
 }
 
@@ -349,7 +350,9 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     const wc_segment sg = find_segment(st, k);
     const uint64_t start = (k - sg.chunk_base) * kChunk;
     const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
-    Stream cs{nullptr, 0, 0, 0, 0};
+    // A half with a bad seek entry still issues its refill loads (never
+    // used): they read 16 bytes at words - 128, here the chunk's own table.
+    Stream cs{gptr(reinterpret_cast<const uint32_t *>(tables + k * 256)) + 32, 0, 0, 0};
     uint32_t x = kL;
     {
         const uint64_t a = seek[k], b = seek[k + 1];
@@ -389,8 +392,8 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         build_table<kL1>(sh, h, lane, f, incl - local, fbtmp);
     }
     __syncthreads();
-    // prefill the ring with two blocks
-    for (int r = 0; r < 2; r++) refill_commit(cs, lane, refill_issue(cs, lane, ok), sh.ring[h]);
+    // prefill the ring with three blocks
+    for (int r = 0; r < 3; r++) refill_commit(refill_issue(cs, lane, ok), sh.ring[h]);
     __syncthreads();
 
     RawView<DT> rv;
@@ -408,20 +411,28 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     const uint32_t ng = (hi_len + kBlk - 1) / kBlk;
     const uint32_t nfull = lo_len / kBlk;
     using Pre = typename RawView<DT>::Pre;
-    Refill pend{u32x4{0, 0, 0, 0}, 0, false};
-    uint32_t rpos = 0;  // cs.ptr modulo the ring size
-    auto group = [&](auto check_tag, uint32_t gg, uint32_t g_last, const Pre &cur, Pre &ahead) {
+    uint32_t b0 = h, b1 = 0, hs = 32 * h;
+    if constexpr (!kL1) {
+        b0 = h << 12;
+        b1 = h << 10;
+    }
+    asm volatile("" : "+v"(b0), "+v"(b1), "+v"(hs));
+    // due: the refill to write into the ring now; next: where this group's
+    // refill goes (may be the same object)
+    auto group = [&](auto check_tag, uint32_t gg, uint32_t g_last, const Pre &cur, Pre &ahead, const Refill &due,
+                     Refill &next) {
         constexpr bool CHECK = decltype(check_tag)::value;
-        refill_commit(cs, lane, pend, sh.ring[h]);
-        pend = refill_issue(cs, lane, ok);
-        const uint32_t gn = gg + 2 <= g_last ? gg + 2 : gg;  // the last groups re-load themselves
+        refill_commit(due, sh.ring[h]);
+        next = refill_issue(cs, lane, ok);
+        // the value loaded for a group past the last is never used
+        const uint32_t gn = gg + 2 <= g_last ? gg + 2 : g_last;
         if constexpr (CHECK) ahead = put ? rv.fetch_checked(kBlk * gn + 8 * lane, len) : Pre{};
         else ahead = rv.fetch(kBlk * gn + 8 * lane);
         wave_lds_order();
 #pragma unroll
         for (uint32_t i = 0; i < kGroup; i++) {
             const bool active = !CHECK || (ok && kLanes * (kGroup * gg + i) + lane < len);
-            dec_step<kL1, CHECK, kH>(x, cs.ptr, rpos, sh, h, lane, active, i);
+            dec_step<kL1, CHECK, kH>(x, cs.ptr, sh, b0, b1, hs, h, lane, active, i);
         }
         wave_lds_order();
         if constexpr (CHECK) {
@@ -431,9 +442,11 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         }
         wave_lds_order();
     };
-    // raw bytes of group g are loaded two groups ahead into one of three
-    // register sets; the hot loop runs whole triples of full groups so the
-    // sets stay in fixed registers
+    // Raw bytes of group g are loaded two groups ahead into one of three
+    // register sets, and the refill issued in group g is committed in group
+    // g + 2, also from one of three sets: the hot loop runs whole triples of
+    // full groups so every set stays in fixed registers.
+    Refill r0 = refill_none(), r1 = refill_none(), r2 = refill_none();
     const uint32_t n3 = nfull / 3 * 3;
     if (n3) {
         const std::false_type u{};
@@ -443,16 +456,21 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         const uint32_t last = n3 - 1;
 #pragma unroll 1
         for (uint32_t g = 0; g < n3; g += 3) {
-            group(u, g, last, pa, pc);
-            group(u, g + 1, last, pb, pa);
-            group(u, g + 2, last, pc, pb);
+            group(u, g, last, pa, pc, r1, r0);
+            group(u, g + 1, last, pb, pa, r2, r1);
+            group(u, g + 2, last, pc, pb, r0, r2);
         }
     }
-    // what is left (at most two full groups and a partial one) runs checked
+    // What is left (at most two full groups and a partial one) runs checked,
+    // with refills committed one group after they are issued: first the two
+    // still in flight land, oldest first.
+    refill_commit(r1, sh.ring[h]);
+    refill_commit(r2, sh.ring[h]);
+    Refill pend = refill_none();
     for (uint32_t g = n3; g < ng; g++) {
         Pre cur = put ? rv.fetch_checked(kBlk * g + 8 * lane, len) : Pre{};
         Pre dummy;
-        group(std::true_type{}, g, g, cur, dummy);
+        group(std::true_type{}, g, g, cur, dummy, pend, pend);
     }
 
     if (ok) {
