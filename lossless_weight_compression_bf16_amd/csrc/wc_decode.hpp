@@ -13,12 +13,19 @@
 //                            b | (f-4096) << 16 (1 KiB); two LDS reads per
 //                            step but 3x the wavefronts per CU, used when
 //                            there are enough chunks to fill the machine;
-//   - a 1024-word ring of the compressed stream, refilled 256 words at a
-//     time: a refill is loaded at the start of a group of 8 steps and
-//     written to the ring at the start of the group after next, so the
-//     load has two groups to land and the word fetch of a step is an LDS
-//     read that never waits for HBM.  The ring size is a power of two, so a
-//     lane's word address is its stream position masked;
+//   - a 320-word ring of the compressed stream (plus its first 32 words
+//     repeated after the end, so a step's 32 reads never wrap), refilled
+//     64 words at a time: a refill is loaded at the start of a group of 8
+//     steps and written to the ring at the start of the group after next,
+//     so the load has two groups to land and the word fetch of a step is
+//     an LDS read.  The ring is sized for one group's worst case (256
+//     words) plus a block, not for the refill latency: a group runs
+//     speculatively on the words landed so far; a chunk in which a group
+//     consumed a word that had not landed is decoded again from the start
+//     with a synchronous fill before every group (rare: it needs more than
+//     64 words per group for many groups in a row, about 2 bits/symbol
+//     above what weights carry).
+//     A small ring keeps 13 wavefronts per CU;
 //   - the 256 decoded bytes of the current group.
 // At the end of a group each lane joins 8 consecutive decoded bytes with 8
 // raw bytes (loaded with one 8-byte load issued two groups earlier) and
@@ -32,21 +39,24 @@
 
 namespace wc {
 
-constexpr uint32_t kGroup = 8;                     // steps per group
-constexpr uint32_t kBlk = kLanes * kGroup;         // words per refill (max consumed per group)
-// Words issued (landed or in flight) run at most three blocks ahead of the
-// read position when a refill is issued; it lands two groups later, when
-// the read position has not moved back, so the landing block never covers
-// an unconsumed word of the four-block ring.  With three blocks prefilled,
-// every group finds the (up to) 256 words it consumes already landed.
-constexpr uint32_t kRingWords = 4 * kBlk;
-constexpr uint32_t kStageBytes = kLanes * kGroup;  // decoded bytes per group per half
+constexpr uint32_t kGroup = 8;                       // steps per group
+constexpr uint32_t kGroupWords = kLanes * kGroup;    // most words one group consumes
+constexpr uint32_t kBlk = 2 * kLanes;                // words per refill block, one dword per lane
+constexpr uint32_t kRingWords = kGroupWords + kBlk;  // 320
+constexpr uint32_t kApron = kLanes;                  // ring words 0..31 repeated after the end
+constexpr uint32_t kRingAlloc = kRingWords + kApron;
+// A block is issued only while fewer than kAhead words are issued and
+// unconsumed; it lands at least one group later, when the read position
+// has not moved back, so it never covers an unconsumed word.
+constexpr uint32_t kAhead = kRingWords - kBlk;
+constexpr uint32_t kStageBytes = kLanes * kGroup;    // decoded bytes per group per half
 
 // H = chunks per wavefront (one per 32-lane half)
 template <int H>
 struct DecSharedL1 {
     uint32_t tab[H][kM];                    // per slot: sym | (f-1) << 8 | (slot-b) << 20
-    uint32_t ring[H][kRingWords / 2];
+    uint32_t fbtmp[H][256];                 // (b, f) while the table is built
+    uint32_t ring[H][kRingAlloc / 2];
     uint32_t stage[H][kStageBytes / 4];
 };
 
@@ -54,7 +64,7 @@ template <int H>
 struct DecSharedL2 {
     uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
     uint32_t fb[H][256];                    // b | (f - 4096) << 16
-    uint32_t ring[H][kRingWords / 2];
+    uint32_t ring[H][kRingAlloc / 2];
     uint32_t stage[H][kStageBytes / 4];
 };
 
@@ -62,55 +72,70 @@ struct DecSharedL2 {
 struct Stream {
     const WC_GLOBAL uint32_t *words;  // payload + seek[k] + 128, as dwords
     uint32_t nw;                      // words in the chunk (pad included, even)
-    uint32_t ptr;                     // next word to consume
+    uint32_t ptr;                     // next word to consume (advanced once per group)
     uint32_t fill;                    // words issued to the ring (landed or in flight)
+    uint32_t land;                    // words landed in the ring
+    uint32_t fpos;                    // fill modulo the ring size
 };
 
-// A refill moves the next 256-word block into the ring, 16 bytes per lane.
-// The load is issued every group, unconditionally, so the compiler can count
-// outstanding memory operations exactly: when no refill is due it reads the
-// chunk's first 16 bytes, and near the end of the stream it reads the last
-// 16 in-bounds bytes and the commit shifts the lane's words into place.
+// A refill moves the next 64-word block into the ring, one dword per lane.
+// Its load is issued unconditionally, so the compiler can count outstanding
+// memory operations exactly: when no refill is due it reads the chunk's
+// first dword, and a lane whose dword lies past the stream end reads the
+// last one in bounds and writes zero.
 struct Refill {
-    u32x4 v;
-    uint32_t shift;  // dwords between the wanted start and the loaded start
-    uint32_t pos;    // ring dword offset of the lane's 16 bytes
+    uint32_t v;
+    uint32_t pos;  // ring dword the lane writes
     bool go;
+    bool in;       // the lane's dword lies inside the stream
 };
 
-__device__ inline Refill refill_none()
+__device__ __forceinline__ Refill refill_none()
 {
-    return Refill{u32x4{0u, 0u, 0u, 0u}, 0u, 0u, false};
+    return Refill{0u, 0u, false, false};
 }
 
-__device__ inline Refill refill_issue(Stream &st, uint32_t lane, bool on)
+__device__ __forceinline__ Refill refill_issue(Stream &st, uint32_t lane, bool on)
 {
     Refill r;
-    r.go = on && st.fill - st.ptr < 3 * kBlk && st.fill < st.nw;
-    const int32_t d0 = (int32_t)(st.fill / 2 + 4 * lane), ndw = (int32_t)(st.nw / 2);
-    // [dl, dl + 4) lies in [-32, ndw): the words area or the 128-byte state
-    // area in front of it
-    const int32_t dl = r.go ? (d0 + 4 <= ndw ? d0 : ndw - 4) : -32;
-    r.v = *reinterpret_cast<const WC_GLOBAL u32x4 *>(st.words + dl);
-    r.shift = (uint32_t)(d0 - dl);
-    r.pos = (st.fill & (kRingWords - 1)) / 2 + 4 * lane;
-    if (r.go) st.fill += kBlk;
+    r.go = on && st.fill - st.ptr < kAhead && st.fill < st.nw;
+    const int32_t d0 = (int32_t)(st.fill / 2 + lane), ndw = (int32_t)(st.nw / 2);
+    r.in = d0 < ndw;
+    // dl lies in [-32, ndw): the words area or the 128-byte state area in
+    // front of it
+    const int32_t dl = r.go ? (r.in ? d0 : ndw - 1) : -32;
+    r.v = st.words[dl];
+    r.pos = st.fpos / 2 + lane;
+    if (r.go) {
+        st.fill += kBlk;
+        st.fpos = st.fpos + kBlk < kRingWords ? st.fpos + kBlk : 0u;
+    }
     return r;
 }
 
-__device__ inline void refill_commit(const Refill &r, uint32_t *ring)
+__device__ __forceinline__ void refill_commit(Stream &st, Refill &r, uint32_t *ring)
 {
-    u32x4 v = r.v;
-    // Lanes at the stream end loaded the last 16 in-bounds bytes: move the
-    // wanted dwords down; what lies past the end is never consumed by a
-    // valid stream and is zeroed.  Once per chunk, so a wave-level branch.
-    if (__ballot(r.go && r.shift != 0)) {
-        const uint32_t sh = r.go ? r.shift : 0u;
-        if (sh & 1) v = u32x4{v.y, v.z, v.w, 0u};
-        if (sh & 2) v = u32x4{v.z, v.w, 0u, 0u};
-        if (sh >= 4) v = u32x4{0u, 0u, 0u, 0u};
+    if (r.go) {
+        const uint32_t v = r.in ? r.v : 0u;
+        ring[r.pos] = v;
+        // a read of 32 words starting anywhere in the ring never wraps
+        if (r.pos < kApron / 2) ring[kRingWords / 2 + r.pos] = v;
+        st.land += kBlk;
+        r.go = false;
     }
-    if (r.go) *reinterpret_cast<u32x4 *>(ring + r.pos) = v;
+}
+
+// Lands what the next group may need (256 words, or the rest of the
+// stream): up to four blocks, loaded together and then written.  Only
+// called with nothing in flight, so issued equals landed.
+__device__ __forceinline__ void refill_sync(Stream &st, uint32_t lane, bool ok, uint32_t *ring)
+{
+    Refill r[kGroupWords / kBlk];
+#pragma unroll
+    for (uint32_t j = 0; j < kGroupWords / kBlk; j++)
+        r[j] = refill_issue(st, lane, ok && st.fill - st.ptr < kGroupWords);
+#pragma unroll
+    for (uint32_t j = 0; j < kGroupWords / kBlk; j++) refill_commit(st, r[j], ring);
 }
 
 // ----------------------------------------------------------- raw plane views
@@ -247,7 +272,7 @@ struct Lookup<false> {
 // group's stage.  b0, b1 are the half's table bases and hs = 32 h, all held
 // opaque so every address is one instruction.
 template <bool kL1, bool CHECK, int kH, typename Sh>
-__device__ inline void dec_step(uint32_t &x, uint32_t &ptr, Sh &sh, uint32_t b0, uint32_t b1, uint32_t hs,
+__device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, uint32_t b0, uint32_t b1, uint32_t hs,
                                 uint32_t h, uint32_t lane, bool active, uint32_t i)
 {
     uint32_t s;
@@ -257,22 +282,24 @@ __device__ inline void dec_step(uint32_t &x, uint32_t &ptr, Sh &sh, uint32_t b0,
     const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
     uint32_t widx, half;
     if constexpr (kH == 1) {
-        widx = __builtin_amdgcn_mbcnt_lo(ml, ptr);
+        widx = __builtin_amdgcn_mbcnt_lo(ml, rpos);
         half = ml;
     } else {
         // rank within the own half: lanes 0-31 count the low mask, lanes
         // 32-63 the high one (mbcnt_hi adds nothing below lane 32)
-        const uint32_t lo = __builtin_amdgcn_mbcnt_lo(ml, ptr);
-        const uint32_t hi = __builtin_amdgcn_mbcnt_hi(mh, ptr);
+        const uint32_t lo = __builtin_amdgcn_mbcnt_lo(ml, rpos);
+        const uint32_t hi = __builtin_amdgcn_mbcnt_hi(mh, rpos);
         widx = h ? hi : lo;
         half = (uint32_t)(m >> hs);
     }
     const uint16_t *ring = reinterpret_cast<const uint16_t *>(&sh.ring[h][0]);
-    const uint32_t w = ring[widx & (kRingWords - 1)];
+    const uint32_t w = ring[widx];  // widx < kRingWords + 32
     // x = need ? xd << 16 | w : xd, as one byte permute of (xd, w)
     const uint32_t sel = need ? 0x05040100u : 0x07060504u;
     const uint32_t xn = __builtin_amdgcn_perm(xd, w, sel);
-    ptr += __popc(half);
+    const uint32_t np = rpos + __popc(half);
+    rpos = np < kRingWords ? np : np - kRingWords;
+    asm volatile("" : "+v"(rpos));
     if (!CHECK || active) x = xn;
     // the byte store must not see the table byte itself: then the symbol
     // load would be an any-extending one and need a mask
@@ -352,7 +379,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
     // A half with a bad seek entry still issues its refill loads (never
     // used): they read 16 bytes at words - 128, here the chunk's own table.
-    Stream cs{gptr(reinterpret_cast<const uint32_t *>(tables + k * 256)) + 32, 0, 0, 0};
+    Stream cs{gptr(reinterpret_cast<const uint32_t *>(tables + k * 256)) + 32, 0, 0, 0, 0, 0};
     uint32_t x = kL;
     {
         const uint64_t a = seek[k], b = seek[k + 1];
@@ -385,15 +412,13 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         ok = false;
     }
     if (ok) {
-        // the wide table needs (b, f) only while it is built: borrow the ring
         uint32_t *fbtmp;
-        if constexpr (kL1) fbtmp = &sh.ring[h][0];
+        if constexpr (kL1) fbtmp = &sh.fbtmp[h][0];
         else fbtmp = &sh.fb[h][0];
         build_table<kL1>(sh, h, lane, f, incl - local, fbtmp);
     }
     __syncthreads();
-    // prefill the ring with three blocks
-    for (int r = 0; r < 3; r++) refill_commit(refill_issue(cs, lane, ok), sh.ring[h]);
+    refill_sync(cs, lane, ok, sh.ring[h]);
     __syncthreads();
 
     RawView<DT> rv;
@@ -408,8 +433,9 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     const uint32_t other_len = kH == 2 ? __shfl_xor(my_len, 32, 64) : my_len;
     const uint32_t hi_len = my_len > other_len ? my_len : other_len;
     const uint32_t lo_len = my_len < other_len ? my_len : other_len;
-    const uint32_t ng = (hi_len + kBlk - 1) / kBlk;
-    const uint32_t nfull = lo_len / kBlk;
+    // equal in every lane; read as scalars so the group loops are uniform
+    const uint32_t ng = __builtin_amdgcn_readfirstlane((hi_len + kGroupWords - 1) / kGroupWords);
+    const uint32_t nfull = __builtin_amdgcn_readfirstlane(lo_len / kGroupWords);
     using Pre = typename RawView<DT>::Pre;
     uint32_t b0 = h, b1 = 0, hs = 32 * h;
     if constexpr (!kL1) {
@@ -417,60 +443,86 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         b1 = h << 10;
     }
     asm volatile("" : "+v"(b0), "+v"(b1), "+v"(hs));
-    // due: the refill to write into the ring now; next: where this group's
-    // refill goes (may be the same object)
-    auto group = [&](auto check_tag, uint32_t gg, uint32_t g_last, const Pre &cur, Pre &ahead, const Refill &due,
-                     Refill &next) {
+    uint32_t rpos = 0;  // cs.ptr modulo the ring size, advanced every step
+    // Speculation: set when a group consumed a word that had not landed.
+    bool overrun = false;
+    // One group: due is the refill to write into the ring now, next where
+    // this group's refill goes (the same object in the one-deep remainder).
+    // (refills off: the group only reads what a synchronous fill landed)
+    auto group = [&](auto check_tag, uint32_t gg, uint32_t g_last, const Pre &cur, Pre &ahead, Refill &due,
+                     Refill &next, bool refills = true) {
         constexpr bool CHECK = decltype(check_tag)::value;
-        refill_commit(due, sh.ring[h]);
-        next = refill_issue(cs, lane, ok);
+        refill_commit(cs, due, sh.ring[h]);
+        next = refill_issue(cs, lane, ok && refills);
         // the value loaded for a group past the last is never used
         const uint32_t gn = gg + 2 <= g_last ? gg + 2 : g_last;
-        if constexpr (CHECK) ahead = put ? rv.fetch_checked(kBlk * gn + 8 * lane, len) : Pre{};
-        else ahead = rv.fetch(kBlk * gn + 8 * lane);
+        if constexpr (CHECK) ahead = put ? rv.fetch_checked(kGroupWords * gn + 8 * lane, len) : Pre{};
+        else ahead = rv.fetch(kGroupWords * gn + 8 * lane);
+        const uint32_t landed = cs.land, r0 = rpos;
         wave_lds_order();
 #pragma unroll
         for (uint32_t i = 0; i < kGroup; i++) {
             const bool active = !CHECK || (ok && kLanes * (kGroup * gg + i) + lane < len);
-            dec_step<kL1, CHECK, kH>(x, cs.ptr, sh, b0, b1, hs, h, lane, active, i);
+            dec_step<kL1, CHECK, kH>(x, rpos, sh, b0, b1, hs, h, lane, active, i);
         }
         wave_lds_order();
+        // unconditional in full groups, so the compiler counts memory
+        // operations exactly: a shadow half writes what its sibling does
         if constexpr (CHECK) {
-            if (put) rv.flush_checked(kBlk * gg + 8 * lane, stage[lane], cur, len);
+            if (put) rv.flush_checked(kGroupWords * gg + 8 * lane, stage[lane], cur, len);
         } else {
-            if (real) rv.flush(kBlk * gg + 8 * lane, stage[lane], cur);
+            rv.flush(kGroupWords * gg + 8 * lane, stage[lane], cur);
         }
         wave_lds_order();
+        // words this group consumed (at most 256, less than the ring)
+        const uint32_t used = rpos >= r0 ? rpos - r0 : rpos + kRingWords - r0;
+        overrun |= cs.ptr + used > landed;
+        cs.ptr += used;
     };
     // Raw bytes of group g are loaded two groups ahead into one of three
     // register sets, and the refill issued in group g is committed in group
     // g + 2, also from one of three sets: the hot loop runs whole triples of
     // full groups so every set stays in fixed registers.
-    Refill r0 = refill_none(), r1 = refill_none(), r2 = refill_none();
+    Refill q0 = refill_none(), q1 = q0, q2 = q0;
     const uint32_t n3 = nfull / 3 * 3;
     if (n3) {
         const std::false_type u{};
         Pre pa = rv.fetch(8 * lane);
-        Pre pb = rv.fetch(kBlk + 8 * lane);
+        Pre pb = rv.fetch(kGroupWords + 8 * lane);
         Pre pc;
         const uint32_t last = n3 - 1;
 #pragma unroll 1
         for (uint32_t g = 0; g < n3; g += 3) {
-            group(u, g, last, pa, pc, r1, r0);
-            group(u, g + 1, last, pb, pa, r2, r1);
-            group(u, g + 2, last, pc, pb, r0, r2);
+            group(u, g, last, pa, pc, q1, q0);
+            group(u, g + 1, last, pb, pa, q2, q1);
+            group(u, g + 2, last, pc, pb, q0, q2);
         }
     }
     // What is left (at most two full groups and a partial one) runs checked,
-    // with refills committed one group after they are issued: first the two
+    // with refills committed one group after they are issued: first the ones
     // still in flight land, oldest first.
-    refill_commit(r1, sh.ring[h]);
-    refill_commit(r2, sh.ring[h]);
-    Refill pend = refill_none();
+    refill_commit(cs, q1, sh.ring[h]);
+    refill_commit(cs, q2, sh.ring[h]);
     for (uint32_t g = n3; g < ng; g++) {
-        Pre cur = put ? rv.fetch_checked(kBlk * g + 8 * lane, len) : Pre{};
+        Pre cur = put ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
         Pre dummy;
-        group(std::true_type{}, g, g, cur, dummy, pend, pend);
+        group(std::true_type{}, g, g, cur, dummy, q0, q0);
+    }
+    // A chunk whose speculation failed is decoded again from its start,
+    // every group checked and preceded by a synchronous fill, and its
+    // output written again.
+    if (__ballot(overrun)) {
+        refill_commit(cs, q0, sh.ring[h]);
+        cs.ptr = cs.fill = cs.land = cs.fpos = 0;
+        rpos = 0;
+        if (ok) x = cs.words[(int32_t)lane - 32];
+        for (uint32_t g = 0; g < ng; g++) {
+            refill_sync(cs, lane, ok, sh.ring[h]);
+            Pre cur = put ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
+            Pre dummy;
+            Refill none = refill_none();
+            group(std::true_type{}, g, g, cur, dummy, none, none, false);
+        }
     }
 
     if (ok) {

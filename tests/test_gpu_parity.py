@@ -129,6 +129,40 @@ def test_table_edge_cases(dev, oracle_lib):
     _round_trip(x, "bf16", dev, oracle_lib, "table edge cases")
 
 
+def test_high_entropy_chunks_next_to_weights(dev, oracle_lib):
+    """Chunks whose coded byte is uniform over 256 values need about 128
+    stream words per 8-step group, more than the decoder refills per group:
+    their first speculative pass overruns the landed words and the chunk is
+    decoded again from its start.  Alternating them with weight chunks puts
+    one of each in every two-chunk wavefront (and an odd count leaves a
+    shadow half), so a redo next to a half that did not need one is covered."""
+    g = np.random.default_rng(11)
+    parts = []
+    for k in range(7):
+        if k % 2:
+            parts.append(g.integers(0, 65536, 65536, dtype=np.uint64).astype(np.uint16))
+        else:
+            parts.append(_weights(65536, 100 + k))
+    parts.append(g.integers(0, 65536, 4321, dtype=np.uint64).astype(np.uint16))
+    _round_trip(np.concatenate(parts), "bf16", dev, oracle_lib, "high-entropy chunks")
+
+
+def test_two_chunk_wavefronts_with_redo(dev, oracle_lib):
+    """Above eight chunks per compute unit (2048 on a 256-CU device) the
+    decoder runs two chunks per wavefront with the small word ring.  2401
+    chunks (an odd count, so the last wavefront has a shadow half), weights
+    throughout except every 37th chunk and the last three, which are
+    uniform over all 65536 patterns and overrun the refill rate."""
+    nchunks = 2401
+    g = np.random.default_rng(12)
+    x = _weights(65536 * (nchunks - 1) + 4321, 13)
+    hot = [k for k in range(nchunks) if k % 37 == 5] + [nchunks - 3, nchunks - 2, nchunks - 1]
+    for k in hot:
+        a, b = 65536 * k, min(65536 * (k + 1), x.size)
+        x[a:b] = g.integers(0, 65536, b - a, dtype=np.uint64).astype(np.uint16)
+    _round_trip(x, "bf16", dev, oracle_lib, "two-chunk wavefronts")
+
+
 def test_golden_streams_on_gpu(dev):
     path = os.path.join(os.path.dirname(__file__), "golden", "chunk_streams.json")
     cases = json.load(open(path))["cases"]
@@ -247,3 +281,39 @@ def test_corrupt_streams_are_flagged(dev, oracle_lib):
         _, obits = oracle_lib.decode(d, strict=False)
         assert (bits != 0) == (obits != 0), (trial, bits, obits)
     assert detected >= trials - 4
+
+
+def test_corrupt_streams_two_chunk_wavefronts(dev, oracle_lib):
+    """The corruption kinds above on a tensor of 2101 chunks, decoded two
+    chunks per wavefront: error bits agree with the oracle and every access
+    stays in bounds."""
+    import copy
+    from lossless_weight_compression_bf16_amd import _binding as B
+    x = _weights(65536 * 2100 + 777, 14)
+    o = oracle_lib.encode(x, "bf16", threads=8)
+    g = np.random.default_rng(15)
+    for trial in range(8):
+        d = copy.deepcopy(o)
+        kind = trial % 4
+        k = int(g.integers(0, d.tables.shape[0]))
+        if kind == 0:
+            i = int(g.integers(int(d.seek[k]), int(d.seek[k + 1])))
+            d.payload[i] ^= np.uint8(1 << int(g.integers(0, 8)))
+        elif kind == 1:
+            d.payload = d.payload[: int(d.seek[k]) + int(g.integers(0, 200))]
+        elif kind == 2:
+            d.tables[k, int(g.integers(0, 256))] += np.uint16(int(g.integers(1, 5)))
+        else:
+            d.seek[k + 1] = np.uint64(int(d.seek[k + 1]) + 4 * int(g.integers(1, 1000)))
+        _say(f"[parity] corrupt two-chunk trial {trial} kind {kind} chunk {k}")
+        e = _upload(d, dev)
+        y = torch.empty(x.size, dtype=torch.int16, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        B.wc_decode("bf16", e.buffers(), e.n, y, err)
+        bits = int(err.item())
+        oy, obits = oracle_lib.decode(d, threads=8, strict=False)
+        assert (bits != 0) == (obits != 0), (trial, bits, obits)
+        if bits == 0:
+            # an undetected change decodes to the same bytes on both sides
+            assert np.array_equal(y.cpu().numpy().view(np.uint16), oy), trial
+
