@@ -70,41 +70,42 @@ struct DecSharedL2 {
 
 // Per-half stream cursor (values uniform within a half).
 struct Stream {
-    const WC_GLOBAL uint32_t *words;  // payload + seek[k] + 128, as dwords
+    const WC_GLOBAL uint8_t *base;    // the chunk's payload: 128 bytes of states, then words
     uint32_t nw;                      // words in the chunk (pad included, even)
     uint32_t ptr;                     // next word to consume (advanced once per group)
     uint32_t fill;                    // words issued to the ring (landed or in flight)
     uint32_t land;                    // words landed in the ring
     uint32_t fpos;                    // fill modulo the ring size
+    __device__ uint32_t word_pair(uint32_t d) const  // stream dword d
+    {
+        return *reinterpret_cast<const WC_GLOBAL uint32_t *>(base + 128 + 4 * d);
+    }
 };
 
 // A refill moves the next 64-word block into the ring, one dword per lane.
 // Its load is issued unconditionally, so the compiler can count outstanding
 // memory operations exactly: when no refill is due it reads the chunk's
-// first dword, and a lane whose dword lies past the stream end reads the
-// last one in bounds and writes zero.
+// first state, and a lane whose dword lies past the stream end reads the
+// last one in bounds (a valid stream never consumes a word past its end).
 struct Refill {
     uint32_t v;
     uint32_t pos;  // ring dword the lane writes
     bool go;
-    bool in;       // the lane's dword lies inside the stream
 };
 
 __device__ __forceinline__ Refill refill_none()
 {
-    return Refill{0u, 0u, false, false};
+    return Refill{0u, 0u, false};
 }
 
 __device__ __forceinline__ Refill refill_issue(Stream &st, uint32_t lane, bool on)
 {
     Refill r;
     r.go = on && st.fill - st.ptr < kAhead && st.fill < st.nw;
-    const int32_t d0 = (int32_t)(st.fill / 2 + lane), ndw = (int32_t)(st.nw / 2);
-    r.in = d0 < ndw;
-    // dl lies in [-32, ndw): the words area or the 128-byte state area in
-    // front of it
-    const int32_t dl = r.go ? (r.in ? d0 : ndw - 1) : -32;
-    r.v = st.words[dl];
+    // with go, nw >= 2: the clamp stays inside the stream
+    const uint32_t d = min(st.fill / 2 + lane, st.nw / 2 - 1);
+    const uint32_t off = r.go ? 128 + 4 * d : 0u;
+    r.v = *reinterpret_cast<const WC_GLOBAL uint32_t *>(st.base + off);
     r.pos = st.fpos / 2 + lane;
     if (r.go) {
         st.fill += kBlk;
@@ -116,10 +117,9 @@ __device__ __forceinline__ Refill refill_issue(Stream &st, uint32_t lane, bool o
 __device__ __forceinline__ void refill_commit(Stream &st, Refill &r, uint32_t *ring)
 {
     if (r.go) {
-        const uint32_t v = r.in ? r.v : 0u;
-        ring[r.pos] = v;
+        ring[r.pos] = r.v;
         // a read of 32 words starting anywhere in the ring never wraps
-        if (r.pos < kApron / 2) ring[kRingWords / 2 + r.pos] = v;
+        if (r.pos < kApron / 2) ring[kRingWords / 2 + r.pos] = r.v;
         st.land += kBlk;
         r.go = false;
     }
@@ -378,8 +378,8 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     const uint64_t start = (k - sg.chunk_base) * kChunk;
     const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
     // A half with a bad seek entry still issues its refill loads (never
-    // used): they read 16 bytes at words - 128, here the chunk's own table.
-    Stream cs{gptr(reinterpret_cast<const uint32_t *>(tables + k * 256)) + 32, 0, 0, 0, 0, 0};
+    // used): they read the first dword at base, here the chunk's own table.
+    Stream cs{gptr(reinterpret_cast<const uint8_t *>(tables + k * 256)), 0, 0, 0, 0, 0};
     uint32_t x = kL;
     {
         const uint64_t a = seek[k], b = seek[k + 1];
@@ -387,9 +387,9 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
             bits |= WC_EF_BAD_SEEK;
             ok = false;
         } else {
-            cs.words = gptr(reinterpret_cast<const uint32_t *>(payload + a + 128));
+            cs.base = gptr(payload + a);
             cs.nw = (uint32_t)min<uint64_t>((b - a - 128) / 2, 2ull * kMaxWords + 2);
-            x = gptr(reinterpret_cast<const uint32_t *>(payload + a))[lane];
+            x = reinterpret_cast<const WC_GLOBAL uint32_t *>(cs.base)[lane];
         }
     }
     // table: 8 symbols per lane, validated (sum 4096) before it is used
@@ -491,8 +491,13 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         Pre pb = rv.fetch(kGroupWords + 8 * lane);
         Pre pc;
         const uint32_t last = n3 - 1;
+        // the first triple is peeled, so the loop is entered with the
+        // memory operations in flight that every iteration leaves behind
+        group(u, 0, last, pa, pc, q1, q0);
+        group(u, 1, last, pb, pa, q2, q1);
+        group(u, 2, last, pc, pb, q0, q2);
 #pragma unroll 1
-        for (uint32_t g = 0; g < n3; g += 3) {
+        for (uint32_t g = 3; g < n3; g += 3) {
             group(u, g, last, pa, pc, q1, q0);
             group(u, g + 1, last, pb, pa, q2, q1);
             group(u, g + 2, last, pc, pb, q0, q2);
@@ -515,7 +520,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         refill_commit(cs, q0, sh.ring[h]);
         cs.ptr = cs.fill = cs.land = cs.fpos = 0;
         rpos = 0;
-        if (ok) x = cs.words[(int32_t)lane - 32];
+        if (ok) x = reinterpret_cast<const WC_GLOBAL uint32_t *>(cs.base)[lane];
         for (uint32_t g = 0; g < ng; g++) {
             refill_sync(cs, lane, ok, sh.ring[h]);
             Pre cur = put ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
@@ -531,7 +536,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         } else if (cs.nw - cs.ptr > 1) {
             bits |= WC_EF_BAD_TAIL;
         } else if (cs.nw - cs.ptr == 1) {
-            const uint32_t last = cs.words[cs.ptr >> 1];
+            const uint32_t last = cs.word_pair(cs.ptr >> 1);
             if ((cs.ptr & 1 ? last >> 16 : last & 0xFFFF) != 0) bits |= WC_EF_BAD_TAIL;
         }
         if (x != kL) bits |= WC_EF_BAD_FINAL_STATE;
