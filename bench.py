@@ -41,7 +41,39 @@ def parse():
                    help="target CPU work for the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the round-trip check before timing")
+    p.add_argument("--copy-ref", action="store_true",
+                   help="after timing, launch one plain device copy of 256 MiB (read 256 MiB, write 256 MiB): "
+                        "the reference for scaling hardware byte counters taken over this run")
     return p.parse_args()
+
+
+COPY_REF_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest():
+    """sha256 over the HIP sources: measured traffic holds only for the
+    kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lossless_weight_compression_bf16_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the counter passes recorded in
+    profiles/traffic.json, or None when none match these sources."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE)).get(f"{kernel}@{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_digest():
+        return None
+    return rec.get("traffic_bytes")
 
 
 def cpu_baseline(w, xs, target_s):
@@ -232,8 +264,15 @@ def main():
         "kernels": kernels,
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(dominant, w.name), "alg_bytes": int(dom_bytes)},
     }
+    if args.copy_ref:
+        src = torch.empty(COPY_REF_BYTES // 4, dtype=torch.int32, device=dev).fill_(7)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.add(src, 0, out=dst)  # the plain copy kernel of known size
+        torch.cuda.synchronize()
+        log(f"[bench] copy reference: {COPY_REF_BYTES} B read, {COPY_REF_BYTES} B written")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")
         result["cpu_baseline"] = cpu_baseline(w, xs, args.cpu_seconds)
