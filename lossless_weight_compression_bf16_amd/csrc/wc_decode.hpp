@@ -479,29 +479,76 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         overrun |= cs.ptr + used > landed;
         cs.ptr += used;
     };
-    // Raw bytes of group g are loaded two groups ahead into one of three
-    // register sets, and the refill issued in group g is committed in group
-    // g + 2, also from one of three sets: the hot loop runs whole triples of
-    // full groups so every set stays in fixed registers.
+    // Full groups run pipelined: group gg carries group gg-1's epilogue.
+    // Its stage bytes are read before step 0 overwrites them; after step 0
+    // they are joined with its raw bytes and stored, its consumption is
+    // settled (so refills see a cursor one group behind, which only delays
+    // them), and this group's refill and the raw bytes of group gg+2 are
+    // loaded.  The epilogue's instructions thus fill the step's LDS waits.
+    struct Pend {
+        uint32_t landed, r0;  // words landed at the group's start, its starting cursor
+    };
+    auto settle = [&](const Pend &pd, uint32_t r_end) {
+        const uint32_t used = r_end >= pd.r0 ? r_end - pd.r0 : r_end + kRingWords - pd.r0;
+        overrun |= cs.ptr + used > pd.landed;
+        cs.ptr += used;
+    };
+    auto fast = [&](auto prev_tag, uint32_t gg, uint32_t g_last, Pre &pv, Refill &due, Refill &next, Pend &pd) {
+        constexpr bool PREV = decltype(prev_tag)::value;
+        refill_commit(cs, due, sh.ring[h]);
+        const Pend mine{cs.land, rpos};
+        uint2 sprev = make_uint2(0u, 0u);
+        wave_lds_order();
+        if constexpr (PREV) sprev = stage[lane];
+#pragma unroll
+        for (uint32_t i = 0; i < kGroup; i++) {
+            dec_step<kL1, false, kH>(x, rpos, sh, b0, b1, hs, h, lane, true, i);
+            if (i == 0) {
+                // unconditional, so the compiler counts memory operations
+                // exactly: a shadow half writes what its sibling does
+                if constexpr (PREV) {
+                    rv.flush(kGroupWords * (gg - 1) + 8 * lane, sprev, pv);
+                    settle(pd, mine.r0);
+                }
+                next = refill_issue(cs, lane, ok);
+                // the value loaded for a group past the last is never used
+                pv = rv.fetch(kGroupWords * (gg + 2 <= g_last ? gg + 2 : g_last) + 8 * lane);
+            }
+        }
+        wave_lds_order();
+        pd = mine;
+    };
+    // Raw bytes of group g are loaded three groups before its store into
+    // one of three register sets, and the refill issued in group g is
+    // committed in group g + 2, also from one of three sets: the hot loop
+    // runs whole triples of full groups so every set stays in fixed
+    // registers.
     Refill q0 = refill_none(), q1 = q0, q2 = q0;
     const uint32_t n3 = nfull / 3 * 3;
     if (n3) {
-        const std::false_type u{};
+        const std::false_type no{};
+        const std::true_type yes{};
         Pre pa = rv.fetch(8 * lane);
         Pre pb = rv.fetch(kGroupWords + 8 * lane);
         Pre pc;
+        Pend pd{0u, 0u};
         const uint32_t last = n3 - 1;
         // the first triple is peeled, so the loop is entered with the
         // memory operations in flight that every iteration leaves behind
-        group(u, 0, last, pa, pc, q1, q0);
-        group(u, 1, last, pb, pa, q2, q1);
-        group(u, 2, last, pc, pb, q0, q2);
+        fast(no, 0, last, pc, q1, q0, pd);
+        fast(yes, 1, last, pa, q2, q1, pd);
+        fast(yes, 2, last, pb, q0, q2, pd);
 #pragma unroll 1
         for (uint32_t g = 3; g < n3; g += 3) {
-            group(u, g, last, pa, pc, q1, q0);
-            group(u, g + 1, last, pb, pa, q2, q1);
-            group(u, g + 2, last, pc, pb, q0, q2);
+            fast(yes, g, last, pc, q1, q0, pd);
+            fast(yes, g + 1, last, pa, q2, q1, pd);
+            fast(yes, g + 2, last, pb, q0, q2, pd);
         }
+        // the last full group's epilogue
+        wave_lds_order();
+        rv.flush(kGroupWords * last + 8 * lane, stage[lane], pc);
+        wave_lds_order();
+        settle(pd, rpos);
     }
     // What is left (at most two full groups and a partial one) runs checked,
     // with refills committed one group after they are issued: first the ones
