@@ -262,24 +262,69 @@ struct SymView {
     }
 };
 
+// Full groups: each lane loads its 8 consecutive elements of a group with
+// wide loads; their coded bytes pass through an LDS stage to the lanes that
+// encode them (step i of lane l encodes element 32 i + l of the group).
+template <int DT>
+struct WideView;
+
+template <>
+struct WideView<WC_BF16> {
+    const WC_GLOBAL u32x4 *in;  // the chunk; 16 bytes = 8 elements per lane per group
+    struct Pre {
+        u32x4 v;
+    };
+    __device__ Pre fetch(uint32_t g, uint32_t lane) const { return Pre{in[kLanes * g + lane]}; }
+    // the high bytes of the 8 elements, in element order
+    __device__ static uint2 bytes(const Pre &p)
+    {
+        return make_uint2(__builtin_amdgcn_perm(p.v.y, p.v.x, 0x07050301u),
+                          __builtin_amdgcn_perm(p.v.w, p.v.z, 0x07050301u));
+    }
+};
+
+template <>
+struct WideView<WC_FP32> {
+    const WC_GLOBAL u32x4 *in;  // 32 bytes = 8 elements per lane per group
+    struct Pre {
+        u32x4 a, b;
+    };
+    __device__ Pre fetch(uint32_t g, uint32_t lane) const
+    {
+        return Pre{in[2 * (kLanes * g + lane)], in[2 * (kLanes * g + lane) + 1]};
+    }
+    // the exponent bytes of the 8 elements, in element order
+    __device__ static uint2 bytes(const Pre &p)
+    {
+        auto e = [](uint32_t u) { return (u >> 23) & 0xFFu; };
+        return make_uint2(e(p.a.x) | e(p.a.y) << 8 | e(p.a.z) << 16 | e(p.a.w) << 24,
+                          e(p.b.x) | e(p.b.y) << 8 | e(p.b.z) << 16 | e(p.b.w) << 24);
+    }
+};
+
 // One encode step for one lane: renormalise (the low 16 bits go to the word
 // list, which grows downwards from index p; the lane's rank among the half's
-// emitting lanes orders words within a step) and push the symbol.  `store`
-// is false for a half that only shadows its neighbour's chunk.
-// The store is issued by every lane on every step (the compiler can then count
-// outstanding memory operations exactly); a lane with nothing to emit writes
-// into its own state word, which the final states overwrite.
+// emitting lanes orders words within a step) and push the symbol.  Only
+// emitting lanes store (an exec-masked store: the instruction is issued every
+// step, so the compiler still counts memory operations exactly); stores go to
+// a wave-uniform base plus a 32-bit lane offset, woff being the half's word
+// area relative to that base.
 template <bool CHECK>
-__device__ inline void enc_step(uint32_t &x, uint32_t &p, bool active, bool store, const EncSym &e,
-                                WC_GLOBAL uint16_t *words, uint32_t h, uint32_t lane)
+__device__ __forceinline__ void enc_step(uint32_t &x, uint32_t &p, bool active, const EncSym &e,
+                                         WC_GLOBAL uint8_t *base, uint32_t woff, uint32_t h, uint32_t hs)
 {
     const bool emit = (!CHECK || active) && x > e.th;
     const uint64_t m = __ballot(emit);
     const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
-    p -= __popc(h ? mh : ml);
-    const uint32_t slot = __builtin_amdgcn_mbcnt_hi(mh, __builtin_amdgcn_mbcnt_lo(h ? 0u : ml, p));
-    // words[-64 + 2 lane] is the low half of this lane's state word
-    words[emit && store ? (int32_t)slot : (int32_t)(2 * lane) - 64] = (uint16_t)(x & 0xFFFF);
+    p -= __popc((uint32_t)(m >> hs));
+    // rank within the own half: lanes 0-31 count the low mask, lanes 32-63
+    // the high one (mbcnt_hi adds nothing below lane 32)
+    const uint32_t lo = __builtin_amdgcn_mbcnt_lo(ml, p);
+    const uint32_t hi = __builtin_amdgcn_mbcnt_hi(mh, p);
+    const uint32_t slot = h ? hi : lo;
+    uint32_t off = woff + 2 * slot;
+    asm("" : "+v"(off));  // a 32-bit offset from the uniform base, not a per-lane pointer
+    if (emit) *reinterpret_cast<WC_GLOBAL uint16_t *>(base + off) = (uint16_t)(x & 0xFFFF);
     const uint32_t xr = emit ? x >> 16 : x;
     const uint32_t q = div_exact(xr, e.mp, (e.fm_sh >> 16) & 0xFF, e.fm_sh >> 24);
     const uint32_t xn = xr + __umul24(q, e.fm_sh & 0xFFFF) + e.b;
@@ -292,6 +337,7 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
                                                uint64_t total_chunks)
 {
     __shared__ EncSym enc[2][256];
+    __shared__ uint32_t estage[2][kEncBlk / 4];  // one full group's coded bytes per half
     const uint32_t lane = threadIdx.x & 31, h = threadIdx.x >> 5;
     // with an odd chunk count the last wavefront's second half shadows the
     // first half's chunk: it runs the same unchecked code but stores nothing
@@ -331,9 +377,14 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     }
     __syncthreads();
 
-    // a shadow half writes into the spare slot after the last chunk's
-    WC_GLOBAL uint8_t *slot = gptr(slots) + (real ? k : total_chunks) * kSlotBytes;
-    WC_GLOBAL uint16_t *words = reinterpret_cast<WC_GLOBAL uint16_t *>(slot + 128);
+    // Half h writes slot 2 blockIdx + h, so a shadow half (only ever the
+    // second half of the last wavefront) writes the spare slot after the
+    // last chunk's.  Word stores address a wave-uniform base plus a lane
+    // offset: the half's words start 128 bytes into its slot.
+    WC_GLOBAL uint8_t *const wbase = gptr(slots) + 2ull * blockIdx.x * kSlotBytes;
+    WC_GLOBAL uint8_t *slot = wbase + h * kSlotBytes;
+    uint32_t woff = h * kSlotBytes + 128, hs = 32 * h;
+    asm volatile("" : "+v"(woff), "+v"(hs));
     SymView<DT> sv;
     sv.in = gptr<const typename SymView<DT>::Elem>(sg.ptr) + start;
     uint32_t x = kL;
@@ -343,8 +394,9 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     // lane of both halves is active run unchecked; the partial last group of
     // a shorter chunk runs checked, first.
     const uint32_t other_len = __shfl_xor(len, 32, 64);
-    const uint32_t ng = ((len > other_len ? len : other_len) + kEncBlk - 1) / kEncBlk;
-    const uint32_t nfull = (len < other_len ? len : other_len) / kEncBlk;
+    // equal in every lane; read as scalars so the group loops are uniform
+    const uint32_t ng = __builtin_amdgcn_readfirstlane(((len > other_len ? len : other_len) + kEncBlk - 1) / kEncBlk);
+    const uint32_t nfull = __builtin_amdgcn_readfirstlane((len < other_len ? len : other_len) / kEncBlk);
     using Pre = typename SymView<DT>::Pre;
     auto group = [&](auto check_tag, uint32_t g, uint32_t g_next, const Pre &cur, Pre &ahead) {
         constexpr bool CHECK = decltype(check_tag)::value;
@@ -355,7 +407,7 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
 #pragma unroll
         for (int i = kEncGroup - 1; i >= 0; i--) {
             const bool active = !CHECK || kEncBlk * g + kLanes * i + lane < len;
-            enc_step<CHECK>(x, p_w, active, real, es[i], words, h, lane);
+            enc_step<CHECK>(x, p_w, active, es[i], wbase, woff, h, hs);
         }
     };
     // Groups run from the last to the first.  The groups above the largest
@@ -369,17 +421,48 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
         group(std::true_type{}, g, g, cur, dummy);
     }
     if (n3) {
-        const std::false_type u{};
-        Pre pa = sv.template fetch<false>(n3 - 1, lane, len);
-        Pre pb = sv.template fetch<false>(n3 - 2, lane, len);
-        Pre pc;
+        // Full groups, descending: group g's wide load is issued three groups
+        // before g is encoded, its bytes go through the stage one group
+        // before, and each group reads its per-symbol constants from the
+        // symbols so staged.  Loads and stage traffic overlap the steps.
+        using WPre = typename WideView<DT>::Pre;
+        WideView<DT> wv;
+        wv.in = reinterpret_cast<const WC_GLOBAL u32x4 *>(sv.in);
+        const uint8_t *stg = reinterpret_cast<const uint8_t *>(&estage[h][0]);
+        auto transpose = [&](const WPre &d, uint32_t (&sy)[kEncGroup]) {
+            const uint2 b = WideView<DT>::bytes(d);
+            wave_lds_order();
+            reinterpret_cast<uint2 *>(&estage[h][0])[lane] = b;
+            wave_lds_order();
+#pragma unroll
+            for (uint32_t i = 0; i < kEncGroup; i++) sy[i] = stg[kLanes * i + lane];
+        };
+        uint32_t sy[kEncGroup];
+        // g: the group encoded; gl: the group whose load is issued; nx: the
+        // next group's data, staged now
+        auto fgroup = [&](uint32_t gl, WPre &load_into, const WPre &nx) {
+            load_into = wv.fetch(gl, lane);
+            EncSym es[kEncGroup];
+#pragma unroll
+            for (uint32_t i = 0; i < kEncGroup; i++) es[i] = enc[h][sy[i]];
+            uint32_t sn[kEncGroup];
+            transpose(nx, sn);
+#pragma unroll
+            for (int i = kEncGroup - 1; i >= 0; i--) enc_step<false>(x, p_w, true, es[i], wbase, woff, h, hs);
+#pragma unroll
+            for (uint32_t i = 0; i < kEncGroup; i++) sy[i] = sn[i];
+        };
+        // n3 - 1 = 2 (mod 3): the sets hold groups 2, 1, 0 (mod 3)
+        WPre s2 = wv.fetch(n3 - 1, lane);
+        transpose(s2, sy);
+        WPre s1 = wv.fetch(n3 - 2, lane);
+        WPre s0 = wv.fetch(n3 - 3, lane);
 #pragma unroll 1
         for (uint32_t g = n3; g > 0; g -= 3) {
-            // groups g-1, g-2, g-3, each loading the group two below it (the
-            // last two re-load themselves)
-            group(u, g - 1, g - 3, pa, pc);
-            group(u, g - 2, g >= 4 ? g - 4 : g - 2, pb, pa);
-            group(u, g - 3, g >= 5 ? g - 5 : g - 3, pc, pb);
+            // groups g-1, g-2, g-3; loads below group 0 re-load group 0
+            fgroup(g >= 4 ? g - 4 : 0, s2, s1);
+            fgroup(g >= 5 ? g - 5 : 0, s1, s0);
+            fgroup(g >= 6 ? g - 6 : 0, s0, s2);
         }
     }
 
