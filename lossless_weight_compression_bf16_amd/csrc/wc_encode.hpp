@@ -1,14 +1,15 @@
 // wc_encode.hpp -- encoder kernels for gfx950.
 //
 //   k_split_hist  one 256-thread block per chunk: coalesced 16-byte loads of
-//                 the tensor (four in flight per thread), raw planes written
+//                 the tensor (eight in flight per thread), raw planes written
 //                 back with vector stores, the coded plane counted into
 //                 per-lane LDS sub-histograms, then the chunk's 12-bit table
 //                 built with integer arithmetic only.
 //   k_encode      one wavefront per two chunks (one chunk per 32-lane half):
 //                 32 interleaved rANS states, reverse order, words written
 //                 downwards into the chunk's scratch slot.
-//   k_scan        exclusive scan of the chunk sizes into the seek table.
+//   k_scan_*      exclusive scan of the chunk sizes into the seek table
+//                 (tile sums, then per-tile scans).
 //   k_compact     moves every chunk's payload from its slot to its offset.
 #pragma once
 
@@ -147,8 +148,9 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
         const WC_GLOBAL uint16_t *in = gptr<uint16_t>(sg.ptr) + start;
         WC_GLOBAL uint8_t *lo = gptr(raw) + sg.raw_base + start;
         const uint32_t ng = len / 8;  // groups of 8 elements = 16 bytes
-        // four 16-byte loads in flight per thread
-        constexpr uint32_t U = 4;
+        // eight 16-byte loads in flight per thread (with four blocks per CU
+        // that is 128 KiB in flight per CU, what HBM latency needs)
+        constexpr uint32_t U = 8;
         uint32_t g = tid;
         for (; g + 256 * (U - 1) < ng; g += 256 * U) {
             u32x4 v[U];
@@ -476,38 +478,73 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
 }
 
 // --------------------------------------------------------------------- scan
+// Two launches over tiles of 4096 chunks: tile sums, then each tile adds the
+// sums of the tiles before it and scans its own chunk sizes.  The tile sums
+// live in the spare slot after the last chunk's (free once the encoder is
+// done: only a shadow half writes there).
 
-__global__ __launch_bounds__(1024) void k_scan(const uint2 *__restrict__ meta, uint64_t total_chunks,
-                                               uint64_t *__restrict__ seek, uint64_t capacity,
-                                               uint32_t *err)
+constexpr uint32_t kScanTile = 4096;  // chunks per tile: 4 per thread of 1024
+
+__device__ inline uint64_t block_sum1024(uint64_t v, uint64_t *wsum)
+{
+    const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 5 >> 1;
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) wsum[w] = v;
+    __syncthreads();
+    uint64_t t = 0;
+    for (uint32_t i = 0; i < 16; i++) t += wsum[i];
+    __syncthreads();
+    return t;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_tiles(const uint2 *__restrict__ meta, uint64_t total_chunks,
+                                                     uint64_t *__restrict__ tile_sum)
+{
+    __shared__ uint64_t wsum[16];
+    const uint64_t base = (uint64_t)blockIdx.x * kScanTile;
+    uint64_t v = 0;
+#pragma unroll
+    for (uint32_t u = 0; u < 4; u++) {
+        const uint64_t i = base + threadIdx.x + 1024 * u;
+        if (i < total_chunks) v += meta[i].x;
+    }
+    v = block_sum1024(v, wsum);
+    if (threadIdx.x == 0) tile_sum[blockIdx.x] = v;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_apply(const uint2 *__restrict__ meta, uint64_t total_chunks,
+                                                     const uint64_t *__restrict__ tile_sum,
+                                                     uint64_t *__restrict__ seek, uint64_t capacity,
+                                                     uint32_t *err)
 {
     __shared__ uint64_t wsum[16];
     const uint32_t tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const uint64_t per = (total_chunks + 1023) / 1024;
-    const uint64_t b = min(total_chunks, per * tid), e = min(total_chunks, b + per);
-    uint64_t local = 0;
-    for (uint64_t i = b; i < e; i++) local += meta[i].x;
-    // inclusive scan in the wavefront, then across the 16 wavefronts
+    // the sizes of every chunk before this tile
+    uint64_t before = 0;
+    for (uint32_t t = tid; t < blockIdx.x; t += 1024) before += tile_sum[t];
+    before = block_sum1024(before, wsum);
+    // this thread's four consecutive chunks
+    const uint64_t c0 = (uint64_t)blockIdx.x * kScanTile + 4 * tid;
+    uint64_t sz[4];
+#pragma unroll
+    for (uint32_t j = 0; j < 4; j++) sz[j] = c0 + j < total_chunks ? meta[c0 + j].x : 0u;
+    const uint64_t local = sz[0] + sz[1] + sz[2] + sz[3];
     uint64_t incl = local;
     for (int o = 1; o < 64; o <<= 1) {
-        uint64_t v = __shfl_up(incl, o, 64);
+        const uint64_t v = __shfl_up(incl, o, 64);
         if (lane >= (uint32_t)o) incl += v;
     }
     if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    uint64_t off = 0;
-    for (uint32_t i = 0; i < w; i++) off += wsum[i];
-    uint64_t run = off + incl - local;
-    if (tid == 0) seek[0] = 0;
-    for (uint64_t i = b; i < e; i++) {
-        run += meta[i].x;
-        seek[i + 1] = run;
+    uint64_t run = before + incl - local;
+    for (uint32_t i = 0; i < w; i++) run += wsum[i];
+#pragma unroll
+    for (uint32_t j = 0; j < 4; j++) {
+        run += sz[j];
+        if (c0 + j < total_chunks) seek[c0 + j + 1] = run;
     }
-    if (tid == 1023) {
-        uint64_t total = 0;
-        for (int i = 0; i < 16; i++) total += wsum[i];
-        if (total > capacity && err) atomicOr(err, WC_EF_CAPACITY);
-    }
+    if (blockIdx.x == 0 && tid == 0) seek[0] = 0;
+    if (c0 < total_chunks && total_chunks <= c0 + 4 && run > capacity && err) atomicOr(err, WC_EF_CAPACITY);
 }
 
 // ------------------------------------------------------------------ compact
@@ -522,22 +559,36 @@ __global__ __launch_bounds__(256) void k_compact(const uint8_t *__restrict__ slo
     const uint64_t dst_off = seek[k];
     if (dst_off + mk.x > capacity) return;  // reported by the scan
     const uint32_t p = mk.y, nw = kMaxWords - p, ndw = (nw + 1) / 2;
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(slots + k * kSlotBytes);
-    uint32_t *dst = reinterpret_cast<uint32_t *>(payload + dst_off);
+    const WC_GLOBAL uint32_t *src = reinterpret_cast<const WC_GLOBAL uint32_t *>(gptr(slots) + k * kSlotBytes);
+    WC_GLOBAL uint32_t *dst = reinterpret_cast<WC_GLOBAL uint32_t *>(gptr(payload) + dst_off);
     const uint32_t tid = threadIdx.x;
     if (tid < 32) dst[tid] = src[tid];
-    const uint32_t *ws = src + 32;  // word area as dwords: word j is half (j & 1) of dword j / 2
-    for (uint32_t i = tid; i < ndw; i += 256) {
-        const uint32_t j = p + 2 * i;  // word that lands in the low half
-        uint32_t v;
-        if ((p & 1) == 0) {
-            v = ws[j >> 1];
-        } else {
-            v = ws[j >> 1] >> 16;
-            if (j + 1 < kMaxWords) v |= ws[(j + 1) >> 1] << 16;
+    // word area as dwords: word j is half (j & 1) of dword j / 2; output
+    // dword i holds words p + 2 i and p + 2 i + 1.  Four dwords per thread
+    // per round, interleaved so every load is coalesced and four are in
+    // flight.
+    const WC_GLOBAL uint32_t *ws = src + 32 + (p >> 1);
+    WC_GLOBAL uint32_t *wd = dst + 32;
+    const bool odd = p & 1;
+    for (uint32_t i0 = 0; i0 < ndw; i0 += 1024) {
+        uint32_t v[4], w[4];
+#pragma unroll
+        for (uint32_t u = 0; u < 4; u++) {
+            const uint32_t i = i0 + tid + 256 * u;
+            // with an odd start the last dword's upper word lies one dword
+            // past the slot (the next slot's, or the spare slot after the
+            // last chunk's); the pad mask below drops it
+            v[u] = i < ndw ? ws[i] : 0u;
+            w[u] = odd && i < ndw ? ws[i + 1] : 0u;
         }
-        if (2 * i + 1 >= nw) v &= 0xFFFFu;  // odd count: zero pad word
-        dst[32 + i] = v;
+#pragma unroll
+        for (uint32_t u = 0; u < 4; u++) {
+            const uint32_t i = i0 + tid + 256 * u;
+            if (i >= ndw) continue;
+            uint32_t d = odd ? (v[u] >> 16) | (w[u] << 16) : v[u];
+            if (2 * i + 1 >= nw) d &= 0xFFFFu;  // odd count: zero pad word
+            wd[i] = d;
+        }
     }
 }
 

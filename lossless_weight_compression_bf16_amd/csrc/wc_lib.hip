@@ -1,7 +1,7 @@
 // wc_lib.hip -- C ABI of the gfx950 lossless weight codec (see include/wc.h).
 //
 // Host side: argument validation, buffer layout, and the launch sequence
-//   encode: k_split_hist -> k_encode -> k_scan -> k_compact
+//   encode: k_split_hist -> k_encode -> k_scan_tiles, k_scan_apply -> k_compact
 //   decode: k_decode
 // on the caller's stream.  No allocation, no synchronisation, no global state.
 #include <hip/hip_runtime.h>
@@ -100,8 +100,15 @@ wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, c
                            out->tables, slots, meta, chunks);
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return WC_ERR_HIP;
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, meta, chunks, out->seek, out->payload_bytes,
-                       d_err);
+    {
+        // tile sums go to the spare slot after the last chunk's
+        const uint32_t tiles = (uint32_t)((chunks + kScanTile - 1) / kScanTile);
+        uint64_t *tile_sum = reinterpret_cast<uint64_t *>(slots + chunks * kSlotBytes);
+        if (chunks)
+            hipLaunchKernelGGL(k_scan_tiles, dim3(tiles), dim3(1024), 0, stream, meta, chunks, tile_sum);
+        hipLaunchKernelGGL(k_scan_apply, dim3(tiles ? tiles : 1), dim3(1024), 0, stream, meta, chunks, tile_sum,
+                           out->seek, out->payload_bytes, d_err);
+    }
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return WC_ERR_HIP;
     if (chunks) {
         hipLaunchKernelGGL(k_compact, dim3((uint32_t)chunks), dim3(256), 0, stream, slots, meta, out->seek,
