@@ -1,7 +1,7 @@
 // wc_encode.hpp -- encoder kernels for gfx950.
 //
 //   k_split_hist  one 256-thread block per chunk: coalesced 16-byte loads of
-//                 the tensor (eight in flight per thread), raw planes written
+//                 the tensor (four in flight per thread), raw planes written
 //                 back with vector stores, the coded plane counted into
 //                 per-lane LDS sub-histograms, then the chunk's 12-bit table
 //                 built with integer arithmetic only.
@@ -107,12 +107,12 @@ __device__ inline uint32_t normalize256(uint32_t c, uint32_t T, uint32_t *red, u
 
 // ------------------------------------------------------------ split + table
 
-// Per-lane sub-histograms: lane c of every wavefront counts into copy c,
-// two 16-bit counters per word (a copy sees at most 4 x 256 = 1024 symbols
-// of a chunk, so counters never carry into their neighbour).  No two lanes
-// of one LDS atomic ever hit the same word; the odd stride spreads the copies
-// over the banks.
-constexpr uint32_t kHistCopies = 64;
+// Sub-histograms: lanes c and c + 32 of every wavefront count into copy c,
+// two 16-bit counters per word (a copy sees at most 2048 symbols of a
+// chunk, so counters never carry into their neighbour).  At most two lanes
+// of one LDS atomic hit the same word; the odd stride spreads the copies
+// over the banks.  32 copies (16.5 KiB) leave room for six blocks per CU.
+constexpr uint32_t kHistCopies = 32;
 constexpr uint32_t kHistStride = 129;
 
 __device__ inline void hist_add(uint32_t *my, uint32_t b)
@@ -142,15 +142,14 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
         if (end + tid < pad_end) raw[end + tid] = 0;
     }
     __syncthreads();
-    uint32_t *my = hist + (tid & 63) * kHistStride;
+    uint32_t *my = hist + (tid & (kHistCopies - 1)) * kHistStride;
 
     if constexpr (DT == WC_BF16) {
         const WC_GLOBAL uint16_t *in = gptr<uint16_t>(sg.ptr) + start;
         WC_GLOBAL uint8_t *lo = gptr(raw) + sg.raw_base + start;
         const uint32_t ng = len / 8;  // groups of 8 elements = 16 bytes
-        // eight 16-byte loads in flight per thread (with four blocks per CU
-        // that is 128 KiB in flight per CU, what HBM latency needs)
-        constexpr uint32_t U = 8;
+        // four 16-byte loads in flight per thread
+        constexpr uint32_t U = 4;
         uint32_t g = tid;
         for (; g + 256 * (U - 1) < ng; g += 256 * U) {
             u32x4 v[U];
@@ -564,16 +563,17 @@ __global__ __launch_bounds__(256) void k_compact(const uint8_t *__restrict__ slo
     const uint32_t tid = threadIdx.x;
     if (tid < 32) dst[tid] = src[tid];
     // word area as dwords: word j is half (j & 1) of dword j / 2; output
-    // dword i holds words p + 2 i and p + 2 i + 1.  Four dwords per thread
-    // per round, interleaved so every load is coalesced and four are in
-    // flight.
+    // dword i holds words p + 2 i and p + 2 i + 1.  Up to 16 dwords per
+    // thread per round, interleaved so every load is coalesced and up to 16
+    // are in flight.
     const WC_GLOBAL uint32_t *ws = src + 32 + (p >> 1);
     WC_GLOBAL uint32_t *wd = dst + 32;
     const bool odd = p & 1;
-    for (uint32_t i0 = 0; i0 < ndw; i0 += 1024) {
-        uint32_t v[4], w[4];
+    constexpr uint32_t U = 16;
+    for (uint32_t i0 = 0; i0 < ndw; i0 += 256 * U) {
+        uint32_t v[U], w[U];
 #pragma unroll
-        for (uint32_t u = 0; u < 4; u++) {
+        for (uint32_t u = 0; u < U; u++) {
             const uint32_t i = i0 + tid + 256 * u;
             // with an odd start the last dword's upper word lies one dword
             // past the slot (the next slot's, or the spare slot after the
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(256) void k_compact(const uint8_t *__restrict__ slo
             w[u] = odd && i < ndw ? ws[i + 1] : 0u;
         }
 #pragma unroll
-        for (uint32_t u = 0; u < 4; u++) {
+        for (uint32_t u = 0; u < U; u++) {
             const uint32_t i = i0 + tid + 256 * u;
             if (i >= ndw) continue;
             uint32_t d = odd ? (v[u] >> 16) | (w[u] << 16) : v[u];
