@@ -266,6 +266,22 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(dominant, w.name), "alg_bytes": int(dom_bytes)},
     }
+    # achievable bandwidth on this GPU: a plain device copy, 1 GiB each way
+    # (larger than the 256 MB Infinity Cache), in the same run
+    csrc = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(3)
+    cdst = torch.empty_like(csrc)
+    torch.add(csrc, 0, out=cdst)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    c0.record(stream)
+    for _ in range(reps):
+        torch.add(csrc, 0, out=cdst)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / reps
+    result["copy_GBps"] = round(2 * csrc.numel() * 4 / (copy_ms / 1e3) / 1e9, 1)
+    result["decode_vs_copy"] = round(alg["rans_decode"] / (dec_ms / 1e3) / 1e9 / result["copy_GBps"], 4)
+    del csrc, cdst
     if args.copy_ref:
         src = torch.empty(COPY_REF_BYTES // 4, dtype=torch.int32, device=dev).fill_(7)
         dst = torch.empty_like(src)
