@@ -13,7 +13,7 @@
 //                            b | (f-4096) << 16 (1 KiB); two LDS reads per
 //                            step but 3x the wavefronts per CU, used when
 //                            there are enough chunks to fill the machine;
-//   - a 320-word ring of the compressed stream (plus its first 32 words
+//   - a 320-word ring of the compressed stream (plus its first 64 words
 //     repeated after the end, so a step's 32 reads never wrap), refilled
 //     64 words at a time: a refill is loaded at the start of a group of 8
 //     steps and written to the ring at the start of the group after next,
@@ -43,7 +43,7 @@ constexpr uint32_t kGroup = 8;                       // steps per group
 constexpr uint32_t kGroupWords = kLanes * kGroup;    // most words one group consumes
 constexpr uint32_t kBlk = 2 * kLanes;                // words per refill block, one dword per lane
 constexpr uint32_t kRingWords = kGroupWords + kBlk;  // 320
-constexpr uint32_t kApron = kLanes;                  // ring words 0..31 repeated after the end
+constexpr uint32_t kApron = 2 * kLanes;              // ring words 0..63 repeated after the end
 constexpr uint32_t kRingAlloc = kRingWords + kApron;
 // A block is issued only while fewer than kAhead words are issued and
 // unconsumed; it lands at least one group later, when the read position
@@ -118,7 +118,8 @@ __device__ __forceinline__ void refill_commit(Stream &st, Refill &r, uint32_t *r
 {
     if (r.go) {
         ring[r.pos] = r.v;
-        // a read of 32 words starting anywhere in the ring never wraps
+        // the cursor wraps every second step, so the 32 reads of a step
+        // start below kRingWords + 32 and never wrap
         if (r.pos < kApron / 2) ring[kRingWords / 2 + r.pos] = r.v;
         st.land += kBlk;
         r.go = false;
@@ -293,12 +294,14 @@ __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, ui
         half = (uint32_t)(m >> hs);
     }
     const uint16_t *ring = reinterpret_cast<const uint16_t *>(&sh.ring[h][0]);
-    const uint32_t w = ring[widx];  // widx < kRingWords + 32
+    const uint32_t w = ring[widx];  // widx < kRingWords + 64
     // x = need ? xd << 16 | w : xd, as one byte permute of (xd, w)
     const uint32_t sel = need ? 0x05040100u : 0x07060504u;
     const uint32_t xn = __builtin_amdgcn_perm(xd, w, sel);
-    const uint32_t np = rpos + __popc(half);
-    rpos = np < kRingWords ? np : np - kRingWords;
+    // the cursor is reduced modulo the ring size every second step (after
+    // one unreduced step it is below kRingWords + 32)
+    rpos += __popc(half);
+    if (i & 1) rpos = rpos < kRingWords ? rpos : rpos - kRingWords;
     asm volatile("" : "+v"(rpos));
     if (!CHECK || active) x = xn;
     // the byte store must not see the table byte itself: then the symbol
