@@ -278,6 +278,12 @@ __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, ui
 {
     uint32_t s;
     const uint32_t xd = Lookup<kL1>::step(sh, b0, b1, x, s);
+    // the decoded byte goes to the stage now: its store can fill the wait
+    // the ballot's consumers need after the compare.  The store must not
+    // see the table byte itself: then the symbol load would be an
+    // any-extending one and need a mask.
+    asm("" : "+v"(s));
+    reinterpret_cast<uint8_t *>(&sh.stage[h][0])[kLanes * i + lane] = (uint8_t)s;
     const bool need = (!CHECK || active) && xd < kL;
     const uint64_t m = __ballot(need);
     const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
@@ -304,10 +310,6 @@ __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, ui
     if (i & 1) rpos = rpos < kRingWords ? rpos : rpos - kRingWords;
     asm volatile("" : "+v"(rpos));
     if (!CHECK || active) x = xn;
-    // the byte store must not see the table byte itself: then the symbol
-    // load would be an any-extending one and need a mask
-    asm("" : "+v"(s));
-    reinterpret_cast<uint8_t *>(&sh.stage[h][0])[kLanes * i + lane] = (uint8_t)s;
 }
 
 // Builds the slot table of half h from the lane's 8 frequencies f[] (symbols
