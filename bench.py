@@ -41,6 +41,9 @@ def parse():
                    help="target CPU work for the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the round-trip check before timing")
+    p.add_argument("--cold-reps", type=int, default=5,
+                   help="decode-only repetitions after a 1 GiB write that evicts the Infinity Cache and L2 "
+                        "(and as many back-to-back warm ones); 0 skips both")
     p.add_argument("--copy-ref", action="store_true",
                    help="after timing, launch one plain device copy of 256 MiB (read 256 MiB, write 256 MiB): "
                         "the reference for scaling hardware byte counters taken over this run")
@@ -76,10 +79,23 @@ def measured_traffic(kernel, workload):
     return rec.get("traffic_bytes")
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, xs, target_s):
-    """The oracle, as it stands, on a bounded sample of the same set."""
+    """The oracle, as it stands, on a bounded sample of the same set: with
+    one thread per host core available (at most 16), and with one thread on a
+    smaller piece of the same sample."""
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    threads = max(1, min(16, avail))
     # calibrate on one tensor-sized piece
     probe = xs[0][: min(xs[0].size, 4 * 65536)]
     t = time.perf_counter()
@@ -106,6 +122,16 @@ def cpu_baseline(w, xs, target_s):
         assert np.array_equal(y, x)
         nbytes += x.size * w.elem_bytes
     total = t_enc + t_dec
+    # one thread, on the first ~1/threads of the same sample (whole chunks)
+    one = sample[0][: max(65536, (count // threads) // 65536 * 65536)]
+    t = time.perf_counter()
+    e = oracle.encode(one, w.dtype, threads=1)
+    t1_enc = time.perf_counter() - t
+    t = time.perf_counter()
+    y, _ = oracle.decode(e, threads=1)
+    t1_dec = time.perf_counter() - t
+    assert np.array_equal(y, one)
+    b1 = one.size * w.elem_bytes
     return {
         "value": nbytes / total / 1e9,
         "unit": "GB/s",
@@ -116,7 +142,42 @@ def cpu_baseline(w, xs, target_s):
         "encode_GBps": nbytes / t_enc / 1e9,
         "decode_GBps": nbytes / t_dec / 1e9,
         "seconds": total,
+        "one_thread": {"value": b1 / (t1_enc + t1_dec) / 1e9, "encode_GBps": b1 / t1_enc / 1e9,
+                       "decode_GBps": b1 / t1_dec / 1e9, "elements": int(one.size)},
+        "host_cpus": avail,
+        "cpu_model": cpu_model(),
     }
+
+
+def coded_plane_entropy(w, xs, tables, seek, max_chunks=4096):
+    """Bits per coded symbol over a strided sample of chunks: the empirical
+    entropy of each chunk's coded bytes, their cross-entropy under the chunk's
+    12-bit table (the ideal rANS length for that table), and the payload the
+    encoder actually produced (states, words and padding)."""
+    C = tables.shape[0]
+    stride = max(1, -(-C // max_chunks))
+    h_emp = h_q = 0.0
+    syms = pay = 0
+    k = 0
+    for x in xs:
+        for c0 in range(0, x.size, 65536):
+            if k % stride == 0:
+                seg = x[c0:c0 + 65536]
+                if w.dtype == "bf16":
+                    sym = (seg.view(np.uint16) >> 8).astype(np.uint8)
+                else:
+                    sym = ((seg.view(np.uint32) >> 23) & 0xFF).astype(np.uint8)
+                cnt = np.bincount(sym, minlength=256).astype(np.float64)
+                nz = cnt > 0
+                f = tables[k].astype(np.float64)
+                h_emp += float(-(cnt[nz] * np.log2(cnt[nz] / seg.size)).sum())
+                h_q += float(-(cnt[nz] * np.log2(f[nz] / 4096.0)).sum())
+                syms += seg.size
+                pay += int(seek[k + 1] - seek[k])
+            k += 1
+    return {"H_emp": round(h_emp / syms, 4), "H_q": round(h_q / syms, 4),
+            "payload_bits": round(8.0 * pay / syms, 4),
+            "chunks_sampled": -(-C // stride), "chunk_stride": stride}
 
 
 def main():
@@ -187,10 +248,12 @@ def main():
     torch.cuda.synchronize()
     if int(err.item()):
         raise RuntimeError(f"device error bits {int(err.item()):#x}")
+    checked = None
     if not args.no_check:
         for a, b in zip(ins, outs):
             if not torch.equal(a, b):
                 raise RuntimeError("round trip is not bit-exact")
+        checked = True
         log("[bench] round trip bit-exact")
     compressed = int(raw.numel() + tables.numel() * 2 + seek.numel() * 8 + payload_bytes)
     ratio = compressed / raw_in_bytes
@@ -208,12 +271,10 @@ def main():
     if int(err.item()):
         raise RuntimeError(f"device error bits {int(err.item()):#x}")
 
-    stage_ms = {s: 0.0 for s in STAGES}
-    dec_ms = 0.0
-    for i in range(K):
-        for j, s in enumerate(STAGES):
-            stage_ms[s] += evs[i].elapsed_ms(j, j + 1) / K
-        dec_ms += evs[i].elapsed_ms(5, 6) / K
+    per_step = {s: [evs[i].elapsed_ms(j, j + 1) for i in range(K)] for j, s in enumerate(STAGES)}
+    per_step["rans_decode"] = [evs[i].elapsed_ms(5, 6) for i in range(K)]
+    stage_ms = {s: sum(per_step[s]) / K for s in STAGES}
+    dec_ms = sum(per_step["rans_decode"]) / K
     enc_ms = sum(stage_ms.values())
 
     # algorithmic bytes (the minimum the method moves), per launch
@@ -235,7 +296,8 @@ def main():
 
     kernels = {}
     for k, t in times.items():
-        entry = {"ms": round(t, 5)}
+        entry = {"ms": round(t, 5), "ms_median": round(float(np.median(per_step[k])), 5),
+                 "ms_min": round(min(per_step[k]), 5)}
         if k in alg and t > 0:
             entry["alg_GBps"] = round(alg[k] / (t / 1e3) / 1e9, 2)
             entry["hbm_frac"] = round(alg[k] / (t / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)
@@ -257,6 +319,7 @@ def main():
         "config": {"workload": w.name, "tensors": len(w.shapes), "elements": n,
                    "raw_bytes": raw_in_bytes, "chunks": C, "weights": w.dtype},
         "ratio": round(ratio, 5),
+        "round_trip_bit_exact": checked,
         "encode_GBps": round(raw_in_bytes / (enc_ms / 1e3) / 1e9, 3),
         "decode_GBps": round(raw_in_bytes / (dec_ms / 1e3) / 1e9, 3),
         "decode_hbm_frac": round(alg["rans_decode"] / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -266,6 +329,33 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(dominant, w.name), "alg_bytes": int(dom_bytes)},
     }
+    # decode alone, warm (back to back) and cold (after a 1 GiB write that
+    # evicts the 256 MB Infinity Cache and the L2s)
+    if args.cold_reps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+        dec_bufs = B.make_buffers(raw, tables, seek, payload, payload_bytes)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        warm, cold = [], []
+        for mode in ("warm", "cold"):
+            for _ in range(args.cold_reps):
+                if mode == "cold":
+                    flush.fill_(1)
+                ev[0].record(stream)
+                B.wc_decode_batch(w.dtype, h_out, d_out, len(outs), dec_bufs, err, stream)
+                ev[1].record(stream)
+                torch.cuda.synchronize()
+                (warm if mode == "warm" else cold).append(ev[0].elapsed_time(ev[1]))
+        del flush
+        if int(err.item()):
+            raise RuntimeError(f"device error bits {int(err.item()):#x}")
+        for mode, ts in (("warm", warm), ("cold", cold)):
+            med = float(np.median(ts))
+            result[f"decode_{mode}"] = {
+                "ms_median": round(med, 5), "ms_min": round(min(ts), 5), "reps": len(ts),
+                "hbm_frac_median": round(alg["rans_decode"] / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    result["entropy"] = coded_plane_entropy(
+        w, xs, tables.cpu().numpy().view(np.uint16).reshape(C, 256), seek.cpu().numpy().view(np.uint64))
+
     # achievable bandwidth on this GPU: a plain device copy, 1 GiB each way
     # (larger than the 256 MB Infinity Cache), in the same run
     csrc = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(3)
