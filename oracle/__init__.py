@@ -22,9 +22,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "wc_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libwc_oracle.so")
 
-BF16 = 0
-FP32 = 1
-DTYPES = {"bf16": BF16, "fp32": FP32}
+BF16, FP32, BF16_REORDER, FP16, FP16_REORDER = 0, 1, 2, 3, 4
+DTYPES = {"bf16": BF16, "fp32": FP32, "bf16r": BF16_REORDER, "fp16": FP16, "fp16r": FP16_REORDER}
+# option bits of a format word
+OPT_TENSOR_TABLE = 0x100  # one table per tensor
+OPT_RAW_FALLBACK = 0x200  # chunks that do not shrink are stored raw
 
 OK, ERR_ARG, ERR_CAPACITY, ERR_CORRUPT = 0, 1, 2, 3
 EF_BAD_TABLE, EF_WORD_OVERRUN, EF_BAD_FINAL_STATE, EF_BAD_TAIL, EF_BAD_SEEK = 1, 2, 4, 8, 16
@@ -66,6 +68,9 @@ def lib() -> ctypes.CDLL:
         L.wco_merge_fp32.argtypes = [P, P, U64, P]
         L.wco_histogram.argtypes = [P, U32, P]
         L.wco_normalize.argtypes = [P, U32, P]
+        L.wco_normalize64.argtypes = [P, U64, P]
+        L.wco_split_u16.argtypes = [I, P, U64, P, P]
+        L.wco_merge_u16.argtypes = [I, P, P, U64, P]
         L.wco_encode_chunk.argtypes = [P, U32, P, P]
         L.wco_encode_chunk.restype = U32
         L.wco_decode_chunk.argtypes = [P, U64, P, U32, P]
@@ -83,8 +88,17 @@ def _p(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _dt(dtype) -> int:
-    return DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+def _dt(dtype, options: int = 0) -> int:
+    """Format word: the layout named by `dtype` OR-ed with option bits."""
+    return (DTYPES[dtype] if isinstance(dtype, str) else int(dtype)) | int(options)
+
+
+def options(tensor_table: bool = False, raw_fallback: bool = False) -> int:
+    return (OPT_TENSOR_TABLE if tensor_table else 0) | (OPT_RAW_FALLBACK if raw_fallback else 0)
+
+
+def elem_type(dtype):
+    return np.uint32 if dtype in ("fp32", FP32) else np.uint16
 
 
 @dataclass
@@ -97,9 +111,9 @@ class Layout:
     payload_capacity: int
 
 
-def query_layout(dtype, n: int) -> Layout:
+def query_layout(dtype, n: int, opts: int = 0) -> Layout:
     out = _Layout()
-    rc = lib().wco_query_layout(_dt(dtype), n, ctypes.byref(out))
+    rc = lib().wco_query_layout(_dt(dtype, opts), n, ctypes.byref(out))
     if rc != OK:
         raise ValueError(f"wco_query_layout failed: {rc}")
     return Layout(out.n, out.num_chunks, out.raw_bytes, out.table_bytes, out.seek_bytes,
@@ -121,6 +135,23 @@ def merge_bf16(hi: np.ndarray, lo: np.ndarray) -> np.ndarray:
     lo = np.ascontiguousarray(lo, np.uint8)
     v = np.empty(hi.size, np.uint16)
     lib().wco_merge_bf16(_p(hi), _p(lo), hi.size, _p(v))
+    return v
+
+
+def split_u16(layout, v: np.ndarray):
+    """Any 16-bit layout ("bf16", "bf16r", "fp16", "fp16r"): (coded, raw)."""
+    v = np.ascontiguousarray(v, dtype=np.uint16).ravel()
+    hi = np.empty(v.size, np.uint8)
+    lo = np.empty(v.size, np.uint8)
+    lib().wco_split_u16(_dt(layout), _p(v), v.size, _p(hi), _p(lo))
+    return hi, lo
+
+
+def merge_u16(layout, hi: np.ndarray, lo: np.ndarray) -> np.ndarray:
+    hi = np.ascontiguousarray(hi, np.uint8)
+    lo = np.ascontiguousarray(lo, np.uint8)
+    v = np.empty(hi.size, np.uint16)
+    lib().wco_merge_u16(_dt(layout), _p(hi), _p(lo), hi.size, _p(v))
     return v
 
 
@@ -159,6 +190,17 @@ def normalize(counts, total: int | None = None) -> np.ndarray:
     return f
 
 
+def normalize64(counts, total: int | None = None) -> np.ndarray:
+    """The same normalisation for 64-bit counts (a whole tensor's histogram)."""
+    c = np.ascontiguousarray(counts, np.uint64)
+    assert c.size == 256
+    if total is None:
+        total = int(c.sum())
+    f = np.empty(256, np.uint16)
+    lib().wco_normalize64(_p(c), total, _p(f))
+    return f
+
+
 def encode_chunk(sym: np.ndarray, freq: np.ndarray) -> np.ndarray:
     sym = np.ascontiguousarray(sym, np.uint8)
     freq = np.ascontiguousarray(freq, np.uint16)
@@ -183,41 +225,42 @@ class Encoded:
     dtype: str
     n: int
     raw: np.ndarray      # uint8
-    tables: np.ndarray   # uint16, chunks x 256
+    tables: np.ndarray   # uint16, chunks x 256 (1 x 256 with a tensor table)
     seek: np.ndarray     # uint64, chunks + 1
     payload: np.ndarray  # uint8, seek[-1] bytes
+    opts: int = 0        # option bits
 
     @property
     def total_bytes(self) -> int:
         return int(self.raw.size + self.tables.nbytes + self.seek.nbytes + self.payload.size)
 
 
-def encode(x: np.ndarray, dtype: str = "bf16", threads: int = 1) -> Encoded:
-    """Encode the flat bit patterns of x (uint16 for bf16, uint32 for fp32)."""
-    want = np.uint16 if dtype == "bf16" else np.uint32
-    x = np.ascontiguousarray(x).view(want).ravel()
-    lay = query_layout(dtype, x.size)
+def encode(x: np.ndarray, dtype: str = "bf16", threads: int = 1, opts: int = 0) -> Encoded:
+    """Encode the flat bit patterns of x (uint32 for fp32, uint16 otherwise)."""
+    x = np.ascontiguousarray(x).view(elem_type(dtype)).ravel()
+    lay = query_layout(dtype, x.size, opts)
     raw = np.zeros(lay.raw_bytes, np.uint8)
-    tables = np.zeros(lay.num_chunks * 256, np.uint16)
+    tables = np.zeros(lay.table_bytes // 2, np.uint16)
     seek = np.zeros(lay.num_chunks + 1, np.uint64)
     payload = np.zeros(max(lay.payload_capacity, 1), np.uint8)
-    rc = lib().wco_encode(_dt(dtype), _p(x), x.size, _p(raw), _p(tables), _p(seek), _p(payload),
-                          lay.payload_capacity, threads)
+    rc = lib().wco_encode(_dt(dtype, opts), _p(x), x.size, _p(raw), _p(tables), _p(seek),
+                          _p(payload), lay.payload_capacity, threads)
     if rc != OK:
         raise RuntimeError(f"wco_encode failed: {rc}")
     return Encoded(dtype, x.size, raw, tables.reshape(-1, 256), seek,
-                   payload[: int(seek[-1])].copy())
+                   payload[: int(seek[-1])].copy(), opts)
 
 
 def decode(e: Encoded, threads: int = 1, strict: bool = True):
     """Decode to the flat bit patterns; returns (array, error_bits)."""
-    want = np.uint16 if e.dtype == "bf16" else np.uint32
-    out = np.zeros(e.n, want)
+    out = np.zeros(e.n, elem_type(e.dtype))
     err = ctypes.c_uint32(0)
     payload = np.ascontiguousarray(e.payload, np.uint8)
     pay = payload if payload.size else np.zeros(1, np.uint8)
-    rc = lib().wco_decode(_dt(e.dtype), _p(np.ascontiguousarray(e.raw, np.uint8)),
-                          _p(np.ascontiguousarray(e.tables, np.uint16)),
+    tables = np.ascontiguousarray(e.tables, np.uint16)
+    tables = tables if tables.size else np.zeros(256, np.uint16)
+    rc = lib().wco_decode(_dt(e.dtype, e.opts), _p(np.ascontiguousarray(e.raw, np.uint8)),
+                          _p(tables),
                           _p(np.ascontiguousarray(e.seek, np.uint64)), _p(pay), payload.size, e.n,
                           _p(out), threads, ctypes.byref(err))
     if rc not in (OK, ERR_CORRUPT):
@@ -229,12 +272,12 @@ def decode(e: Encoded, threads: int = 1, strict: bool = True):
 
 # ------------------------------------------------------------------ batch
 
-def plan_batch(dtype, ns):
+def plan_batch(dtype, ns, opts: int = 0):
     ns = np.ascontiguousarray(ns, np.uint64)
     cb = np.zeros(max(ns.size, 1), np.uint64)
     rb = np.zeros(max(ns.size, 1), np.uint64)
     tot = _Layout()
-    lib().wco_plan_batch(_dt(dtype), _p(ns), ns.size, _p(cb), _p(rb), ctypes.byref(tot))
+    lib().wco_plan_batch(_dt(dtype, opts), _p(ns), ns.size, _p(cb), _p(rb), ctypes.byref(tot))
     return cb[: ns.size], rb[: ns.size], Layout(tot.n, tot.num_chunks, tot.raw_bytes,
                                                   tot.table_bytes, tot.seek_bytes,
                                                   tot.payload_capacity)
@@ -248,30 +291,29 @@ class EncodedBatch:
     tables: np.ndarray
     seek: np.ndarray
     payload: np.ndarray
+    opts: int = 0
 
 
-def encode_batch(xs, dtype: str = "bf16", threads: int = 1) -> EncodedBatch:
-    want = np.uint16 if dtype == "bf16" else np.uint32
-    arrs = [np.ascontiguousarray(x).view(want).ravel() for x in xs]
+def encode_batch(xs, dtype: str = "bf16", threads: int = 1, opts: int = 0) -> EncodedBatch:
+    arrs = [np.ascontiguousarray(x).view(elem_type(dtype)).ravel() for x in xs]
     ns = np.array([a.size for a in arrs], np.uint64)
-    _, _, tot = plan_batch(dtype, ns)
+    _, _, tot = plan_batch(dtype, ns, opts)
     raw = np.zeros(max(tot.raw_bytes, 1), np.uint8)
-    tables = np.zeros(max(tot.num_chunks * 256, 1), np.uint16)
+    tables = np.zeros(max(tot.table_bytes // 2, 1), np.uint16)
     seek = np.zeros(tot.num_chunks + 1, np.uint64)
     payload = np.zeros(max(tot.payload_capacity, 1), np.uint8)
     ptrs = (ctypes.c_void_p * max(len(arrs), 1))(*[a.ctypes.data for a in arrs])
-    rc = lib().wco_encode_batch(_dt(dtype), ptrs, _p(ns), len(arrs), _p(raw), _p(tables),
+    rc = lib().wco_encode_batch(_dt(dtype, opts), ptrs, _p(ns), len(arrs), _p(raw), _p(tables),
                                 _p(seek), _p(payload), tot.payload_capacity, threads)
     if rc != OK:
         raise RuntimeError(f"wco_encode_batch failed: {rc}")
     return EncodedBatch(dtype, [int(v) for v in ns], raw[: tot.raw_bytes],
-                        tables[: tot.num_chunks * 256].reshape(-1, 256), seek,
-                        payload[: int(seek[-1])].copy())
+                        tables[: tot.table_bytes // 2].reshape(-1, 256), seek,
+                        payload[: int(seek[-1])].copy(), opts)
 
 
 def decode_batch(e: EncodedBatch, threads: int = 1):
-    want = np.uint16 if e.dtype == "bf16" else np.uint32
-    outs = [np.zeros(n, want) for n in e.ns]
+    outs = [np.zeros(n, elem_type(e.dtype)) for n in e.ns]
     ns = np.array(e.ns, np.uint64)
     ptrs = (ctypes.c_void_p * max(len(outs), 1))(*[o.ctypes.data for o in outs])
     err = ctypes.c_uint32(0)
@@ -279,7 +321,7 @@ def decode_batch(e: EncodedBatch, threads: int = 1):
     tables = np.ascontiguousarray(e.tables, np.uint16)
     tables = tables if tables.size else np.zeros(1, np.uint16)
     pay = e.payload if e.payload.size else np.zeros(1, np.uint8)
-    rc = lib().wco_decode_batch(_dt(e.dtype), ptrs, _p(ns), len(outs), _p(raw), _p(tables),
+    rc = lib().wco_decode_batch(_dt(e.dtype, e.opts), ptrs, _p(ns), len(outs), _p(raw), _p(tables),
                                 _p(np.ascontiguousarray(e.seek, np.uint64)), _p(pay),
                                 e.payload.size, threads, ctypes.byref(err))
     if rc not in (OK, ERR_CORRUPT):

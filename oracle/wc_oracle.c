@@ -36,6 +36,27 @@
  *     odd, so every payload is a multiple of 4 bytes.
  * Tables are stored as 256 u16 per chunk, the seek table as u64 offsets
  * (seek[0] = 0, seek[k+1] = seek[k] + size of chunk k).
+ *
+ * Format variants (the pages' other layouts and options; a format word is a
+ * layout code OR-ed with option bits):
+ *   - BF16_REORDER ("PTWM" README, "How it works" step 1, bit reorder): the
+ *     exponent moves to the most significant position and the sign right
+ *     below it, so for BF16 the coded byte is the 8-bit exponent and the raw
+ *     byte is the sign followed by the 7 mantissa bits.
+ *   - FP16 ("PTWM" README, dtype table: float16 takes a 2-plane byte split):
+ *     the high byte (sign, 5 exponent bits, 2 mantissa bits) is coded, the
+ *     low byte raw.  FP16_REORDER applies the same page's bit reorder first:
+ *     the coded byte holds the 5 exponent bits, then the sign, then the top
+ *     2 mantissa bits; the raw byte the other 8 mantissa bits.
+ *   - TENSOR_TABLE (reading: the per-tensor codec records of the "PTWM"
+ *     README's container, one table for a tensor's chunks): a single table,
+ *     normalised from the histogram of the tensor's whole coded plane, codes
+ *     every chunk of the tensor.
+ *   - RAW_FALLBACK ("PTWM" README, "Configuration": raw bytes are stored when
+ *     compression does not pay; here applied per chunk): a chunk whose coded
+ *     payload would be at least its symbol count rounded up to 4 bytes is
+ *     stored as its symbols, zero-padded to that size.  A payload of exactly
+ *     that size therefore marks a raw chunk.
  */
 #include "wc_oracle.h"
 
@@ -52,10 +73,25 @@
 
 /* ------------------------------------------------------------------ layout */
 
-static uint64_t raw_bytes_of(int dtype, uint64_t n)
+/* The layout code of a format word, or -1 if the word is not a format. */
+static int layout_of(int format)
 {
-    if (dtype == WCO_BF16) return n;
+    int layout = format & WCO_LAYOUT_MASK;
+    if (layout > WCO_FP16_REORDER) return -1;
+    if (format & ~(WCO_LAYOUT_MASK | WCO_OPT_TENSOR_TABLE | WCO_OPT_RAW_FALLBACK)) return -1;
+    return layout;
+}
+
+static uint64_t raw_bytes_of(int layout, uint64_t n)
+{
+    if (layout != WCO_FP32) return n;
     return (n + 7) / 8 + 3 * n;
+}
+
+/* Payload size of a chunk of len symbols stored raw. */
+static uint64_t raw_chunk_size(uint64_t len)
+{
+    return (len + 3) / 4 * 4;
 }
 
 /* Largest payload a chunk of len symbols can take: 32 states, at most one
@@ -68,17 +104,18 @@ static uint64_t chunk_capacity(uint64_t len)
 
 int wco_query_layout(int dtype, uint64_t n, wco_layout *out)
 {
-    if (!out || (dtype != WCO_BF16 && dtype != WCO_FP32)) return WCO_ERR_ARG;
+    int layout = layout_of(dtype);
+    if (!out || layout < 0) return WCO_ERR_ARG;
     uint64_t c = (n + ORC_CHUNK - 1) / ORC_CHUNK;
     out->n = n;
     out->num_chunks = c;
-    out->raw_bytes = raw_bytes_of(dtype, n);
-    out->table_bytes = 512 * c;
+    out->raw_bytes = raw_bytes_of(layout, n);
+    out->table_bytes = (dtype & WCO_OPT_TENSOR_TABLE) ? 512 : 512 * c;
     out->seek_bytes = 8 * (c + 1);
     out->payload_capacity = 0;
     for (uint64_t k = 0; k < c; k++) {
         uint64_t len = (k + 1 < c) ? ORC_CHUNK : n - k * ORC_CHUNK;
-        out->payload_capacity += chunk_capacity(len);
+        out->payload_capacity += (dtype & WCO_OPT_RAW_FALLBACK) ? raw_chunk_size(len) : chunk_capacity(len);
     }
     return WCO_OK;
 }
@@ -96,6 +133,45 @@ void wco_split_bf16(const uint16_t *v, uint64_t n, uint8_t *hi, uint8_t *lo)
 void wco_merge_bf16(const uint8_t *hi, const uint8_t *lo, uint64_t n, uint16_t *v)
 {
     for (uint64_t i = 0; i < n; i++) v[i] = (uint16_t)(((uint16_t)hi[i] << 8) | lo[i]);
+}
+
+/* The 16-bit layouts, one element at a time: take the value apart into
+ * sign, exponent and mantissa fields, put the fields in the layout's order,
+ * and cut the 16 bits into the coded high byte and the raw low byte. */
+void wco_split_u16(int layout, const uint16_t *v, uint64_t n, uint8_t *hi, uint8_t *lo)
+{
+    for (uint64_t i = 0; i < n; i++) {
+        uint32_t x = v[i], r;
+        uint32_t sign = x >> 15;
+        if (layout == WCO_BF16_REORDER) {
+            uint32_t e = (x >> 7) & 0xFF, m = x & 0x7F; /* 8 exponent, 7 mantissa bits */
+            r = (e << 8) | (sign << 7) | m;
+        } else if (layout == WCO_FP16_REORDER) {
+            uint32_t e = (x >> 10) & 0x1F, m = x & 0x3FF; /* 5 exponent, 10 mantissa bits */
+            r = (e << 11) | (sign << 10) | m;
+        } else { /* BF16, FP16: the bits as they are */
+            r = x;
+        }
+        hi[i] = (uint8_t)(r >> 8);
+        lo[i] = (uint8_t)(r & 0xFF);
+    }
+}
+
+void wco_merge_u16(int layout, const uint8_t *hi, const uint8_t *lo, uint64_t n, uint16_t *v)
+{
+    for (uint64_t i = 0; i < n; i++) {
+        uint32_t r = ((uint32_t)hi[i] << 8) | lo[i], x;
+        if (layout == WCO_BF16_REORDER) {
+            uint32_t e = r >> 8, sign = (r >> 7) & 1, m = r & 0x7F;
+            x = (sign << 15) | (e << 7) | m;
+        } else if (layout == WCO_FP16_REORDER) {
+            uint32_t e = r >> 11, sign = (r >> 10) & 1, m = r & 0x3FF;
+            x = (sign << 15) | (e << 10) | m;
+        } else {
+            x = r;
+        }
+        v[i] = (uint16_t)x;
+    }
 }
 
 void wco_split_fp32(const uint32_t *u, uint64_t n, uint8_t *exp, uint8_t *raw)
@@ -146,20 +222,21 @@ void wco_histogram(const uint8_t *sym, uint32_t n, uint32_t counts[256])
  *     first) get f += 1.  (D < number of regular symbols always holds.)
  *  5. D < 0: -D times, the symbol with the largest f (ties: smaller symbol)
  *     gets f -= 1.  (That f is always >= 2.)
- * c*4096 <= 65536*4096 = 2^28, so everything is exact in 32 bits.
+ * The arithmetic is done in 64 bits, so counts of a whole tensor (total below
+ * 2^52) are exact too; for a chunk c*4096 <= 2^28.
  */
-void wco_normalize(const uint32_t counts[256], uint32_t total, uint16_t freq[256])
+void wco_normalize64(const uint64_t counts[256], uint64_t total, uint16_t freq[256])
 {
-    uint32_t f[256], r[256];
+    uint64_t f[256], r[256];
     int regular[256];
-    int32_t sum = 0;
+    int64_t sum = 0;
     for (int s = 0; s < 256; s++) {
         f[s] = 0;
         r[s] = 0;
         regular[s] = 0;
         if (counts[s] == 0) continue;
-        uint32_t scaled = counts[s] * ORC_M;
-        uint32_t q = scaled / total;
+        uint64_t scaled = counts[s] * ORC_M;
+        uint64_t q = scaled / total;
         r[s] = scaled % total;
         if (q >= 1) {
             f[s] = q;
@@ -167,9 +244,9 @@ void wco_normalize(const uint32_t counts[256], uint32_t total, uint16_t freq[256
         } else {
             f[s] = 1;
         }
-        sum += (int32_t)f[s];
+        sum += (int64_t)f[s];
     }
-    int32_t d = (int32_t)ORC_M - sum;
+    int64_t d = (int64_t)ORC_M - sum;
 
     if (d > 0) {
         /* order the regular symbols by remainder descending, symbol ascending
@@ -198,6 +275,13 @@ void wco_normalize(const uint32_t counts[256], uint32_t total, uint16_t freq[256
         }
     }
     for (int s = 0; s < 256; s++) freq[s] = (uint16_t)f[s];
+}
+
+void wco_normalize(const uint32_t counts[256], uint32_t total, uint16_t freq[256])
+{
+    uint64_t c[256];
+    for (int s = 0; s < 256; s++) c[s] = counts[s];
+    wco_normalize64(c, total, freq);
 }
 
 /* ------------------------------------------------------------ chunk codec */
@@ -323,7 +407,7 @@ uint32_t wco_decode_chunk(const uint8_t *p, uint64_t size, const uint16_t freq[2
 /* ------------------------------------------------------------ whole tensor */
 
 typedef struct {
-    int dtype;
+    int format;
     const void *in;
     uint64_t n;
     const uint8_t *coded; /* the coded plane (hi bytes or exponent bytes) */
@@ -340,11 +424,21 @@ static void *encode_range(void *arg)
     for (uint64_t k = j->k0; k < j->k1; k++) {
         uint64_t start = k * ORC_CHUNK;
         uint32_t len = (uint32_t)((j->n - start < ORC_CHUNK) ? j->n - start : ORC_CHUNK);
-        uint32_t counts[256];
-        wco_histogram(j->coded + start, len, counts);
-        wco_normalize(counts, len, j->tables + 256 * k);
-        j->sizes[k] = wco_encode_chunk(j->coded + start, len, j->tables + 256 * k,
-                                       j->scratch + slot * k);
+        uint16_t *table = j->tables;
+        if (!(j->format & WCO_OPT_TENSOR_TABLE)) {
+            uint32_t counts[256];
+            table = j->tables + 256 * k;
+            wco_histogram(j->coded + start, len, counts);
+            wco_normalize(counts, len, table);
+        }
+        uint8_t *out = j->scratch + slot * k;
+        uint32_t size = wco_encode_chunk(j->coded + start, len, table, out);
+        if ((j->format & WCO_OPT_RAW_FALLBACK) && size >= raw_chunk_size(len)) {
+            size = (uint32_t)raw_chunk_size(len);
+            memcpy(out, j->coded + start, len);
+            memset(out + len, 0, size - len);
+        }
+        j->sizes[k] = size;
     }
     return NULL;
 }
@@ -379,18 +473,28 @@ static void enc_set_range(void *job, uint64_t k0, uint64_t k1)
 int wco_encode(int dtype, const void *in, uint64_t n, uint8_t *raw, uint16_t *tables,
                uint64_t *seek, uint8_t *payload, uint64_t payload_capacity, int threads)
 {
-    if (dtype != WCO_BF16 && dtype != WCO_FP32) return WCO_ERR_ARG;
+    int layout = layout_of(dtype);
+    if (layout < 0) return WCO_ERR_ARG;
     if (!seek) return WCO_ERR_ARG;
     seek[0] = 0;
-    if (n == 0) return WCO_OK;
+    if (n == 0) {
+        /* a tensor without elements still owns its (empty) table */
+        if ((dtype & WCO_OPT_TENSOR_TABLE) && tables) memset(tables, 0, 512);
+        return WCO_OK;
+    }
     if (!in || !raw || !tables || !payload) return WCO_ERR_ARG;
 
     uint64_t chunks = (n + ORC_CHUNK - 1) / ORC_CHUNK;
     uint8_t *coded = (uint8_t *)malloc(n);
-    if (dtype == WCO_BF16)
-        wco_split_bf16((const uint16_t *)in, n, coded, raw);
-    else
+    if (layout == WCO_FP32)
         wco_split_fp32((const uint32_t *)in, n, coded, raw);
+    else
+        wco_split_u16(layout, (const uint16_t *)in, n, coded, raw);
+    if (dtype & WCO_OPT_TENSOR_TABLE) {
+        uint64_t counts[256] = {0};
+        for (uint64_t i = 0; i < n; i++) counts[coded[i]]++;
+        wco_normalize64(counts, n, tables);
+    }
 
     /* each chunk is coded into its own worst-case slot, then the payloads are
      * laid end to end */
@@ -401,7 +505,7 @@ int wco_encode(int dtype, const void *in, uint64_t n, uint8_t *raw, uint16_t *ta
     uint32_t *sizes = (uint32_t *)malloc(sizeof(uint32_t) * chunks);
     enc_job *jobs = (enc_job *)calloc(workers, sizeof(enc_job));
     for (uint64_t i = 0; i < workers; i++) {
-        jobs[i].dtype = dtype;
+        jobs[i].format = dtype;
         jobs[i].in = in;
         jobs[i].n = n;
         jobs[i].coded = coded;
@@ -426,6 +530,7 @@ int wco_encode(int dtype, const void *in, uint64_t n, uint8_t *raw, uint16_t *ta
 }
 
 typedef struct {
+    int format;
     const uint16_t *tables;
     const uint64_t *seek;
     const uint8_t *payload;
@@ -448,7 +553,15 @@ static void *decode_range(void *arg)
             memset(j->coded + start, 0, len);
             continue;
         }
-        uint32_t e = wco_decode_chunk(j->payload + a, b - a, j->tables + 256 * k, len, j->coded + start);
+        if ((j->format & WCO_OPT_RAW_FALLBACK) && b - a == raw_chunk_size(len)) {
+            /* stored raw: the symbols, then zero padding */
+            memcpy(j->coded + start, j->payload + a, len);
+            for (uint64_t i = a + len; i < b; i++)
+                if (j->payload[i] != 0) j->err |= WCO_EF_BAD_TAIL;
+            continue;
+        }
+        const uint16_t *table = (j->format & WCO_OPT_TENSOR_TABLE) ? j->tables : j->tables + 256 * k;
+        uint32_t e = wco_decode_chunk(j->payload + a, b - a, table, len, j->coded + start);
         if (e & (WCO_EF_BAD_TABLE | WCO_EF_BAD_SEEK)) memset(j->coded + start, 0, len);
         j->err |= e;
     }
@@ -466,7 +579,8 @@ int wco_decode(int dtype, const uint8_t *raw, const uint16_t *tables, const uint
                uint32_t *err_bits)
 {
     if (err_bits) *err_bits = 0;
-    if (dtype != WCO_BF16 && dtype != WCO_FP32) return WCO_ERR_ARG;
+    int layout = layout_of(dtype);
+    if (layout < 0) return WCO_ERR_ARG;
     if (n == 0) return WCO_OK;
     if (!raw || !tables || !seek || !payload || !out) return WCO_ERR_ARG;
 
@@ -476,6 +590,7 @@ int wco_decode(int dtype, const uint8_t *raw, const uint16_t *tables, const uint
     uint64_t workers = (uint64_t)nthreads < chunks ? (uint64_t)nthreads : chunks;
     dec_job *jobs = (dec_job *)calloc(workers, sizeof(dec_job));
     for (uint64_t i = 0; i < workers; i++) {
+        jobs[i].format = dtype;
         jobs[i].tables = tables;
         jobs[i].seek = seek;
         jobs[i].payload = payload;
@@ -487,10 +602,10 @@ int wco_decode(int dtype, const uint8_t *raw, const uint16_t *tables, const uint
     uint32_t err = 0;
     for (uint64_t i = 0; i < workers; i++) err |= jobs[i].err;
 
-    if (dtype == WCO_BF16)
-        wco_merge_bf16(coded, raw, n, (uint16_t *)out);
-    else
+    if (layout == WCO_FP32)
         wco_merge_fp32(coded, raw, n, (uint32_t *)out);
+    else
+        wco_merge_u16(layout, coded, raw, n, (uint16_t *)out);
     free(jobs);
     free(coded);
     if (err_bits) *err_bits = err;
@@ -502,7 +617,7 @@ int wco_decode(int dtype, const uint8_t *raw, const uint16_t *tables, const uint
 int wco_plan_batch(int dtype, const uint64_t *n, uint32_t count, uint64_t *chunk_base,
                    uint64_t *raw_base, wco_layout *total)
 {
-    if (dtype != WCO_BF16 && dtype != WCO_FP32) return WCO_ERR_ARG;
+    if (layout_of(dtype) < 0) return WCO_ERR_ARG;
     uint64_t chunks = 0, raw = 0, cap = 0, elems = 0;
     for (uint32_t i = 0; i < count; i++) {
         wco_layout one;
@@ -519,7 +634,7 @@ int wco_plan_batch(int dtype, const uint64_t *n, uint32_t count, uint64_t *chunk
         total->n = elems;
         total->num_chunks = chunks;
         total->raw_bytes = raw;
-        total->table_bytes = 512 * chunks;
+        total->table_bytes = (dtype & WCO_OPT_TENSOR_TABLE) ? 512 * (uint64_t)count : 512 * chunks;
         total->seek_bytes = 8 * (chunks + 1);
         total->payload_capacity = cap;
     }
@@ -530,7 +645,7 @@ int wco_encode_batch(int dtype, const void *const *in, const uint64_t *n, uint32
                      uint8_t *raw, uint16_t *tables, uint64_t *seek, uint8_t *payload,
                      uint64_t payload_capacity, int threads)
 {
-    if (dtype != WCO_BF16 && dtype != WCO_FP32) return WCO_ERR_ARG;
+    if (layout_of(dtype) < 0) return WCO_ERR_ARG;
     uint64_t *cb = (uint64_t *)malloc(sizeof(uint64_t) * (count + 1));
     uint64_t *rb = (uint64_t *)malloc(sizeof(uint64_t) * (count + 1));
     wco_layout total;
@@ -541,11 +656,16 @@ int wco_encode_batch(int dtype, const void *const *in, const uint64_t *n, uint32
     for (uint32_t i = 0; i < count && status == WCO_OK; i++) {
         uint64_t base = seek[cb[i]];
         uint64_t c = (n[i] + ORC_CHUNK - 1) / ORC_CHUNK;
-        if (c == 0) continue;
+        /* tables: tensor i's own table (one per tensor), or its chunks' */
+        uint16_t *tab = tables + 256 * ((dtype & WCO_OPT_TENSOR_TABLE) ? i : cb[i]);
+        if (c == 0) {
+            if (dtype & WCO_OPT_TENSOR_TABLE) memset(tab, 0, 512);
+            continue;
+        }
         /* the tensor's own seek table starts at 0; shift it by the payload
          * written so far */
         uint64_t *local = (uint64_t *)malloc(sizeof(uint64_t) * (c + 1));
-        status = wco_encode(dtype, in[i], n[i], raw + rb[i], tables + 256 * cb[i], local,
+        status = wco_encode(dtype, in[i], n[i], raw + rb[i], tab, local,
                             payload + base, payload_capacity - base, threads);
         for (uint64_t k = 1; k <= c; k++) seek[cb[i] + k] = base + local[k];
         free(local);
@@ -561,7 +681,7 @@ int wco_decode_batch(int dtype, void *const *out, const uint64_t *n, uint32_t co
                      uint32_t *err_bits)
 {
     if (err_bits) *err_bits = 0;
-    if (dtype != WCO_BF16 && dtype != WCO_FP32) return WCO_ERR_ARG;
+    if (layout_of(dtype) < 0) return WCO_ERR_ARG;
     uint64_t *cb = (uint64_t *)malloc(sizeof(uint64_t) * (count + 1));
     uint64_t *rb = (uint64_t *)malloc(sizeof(uint64_t) * (count + 1));
     wco_plan_batch(dtype, n, count, cb, rb, NULL);
@@ -579,7 +699,8 @@ int wco_decode_batch(int dtype, void *const *out, const uint64_t *n, uint32_t co
         if (payload_bytes < base || base % 4 != 0) {
             e = WCO_EF_BAD_SEEK;
         } else {
-            wco_decode(dtype, raw + rb[i], tables + 256 * cb[i], local, payload + base, avail, n[i],
+            wco_decode(dtype, raw + rb[i], tables + 256 * ((dtype & WCO_OPT_TENSOR_TABLE) ? i : cb[i]),
+                       local, payload + base, avail, n[i],
                        out[i], threads, &e);
         }
         err |= e;

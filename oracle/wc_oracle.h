@@ -30,9 +30,17 @@
 extern "C" {
 #endif
 
-/* dtype codes */
-#define WCO_BF16 0
-#define WCO_FP32 1
+/* Format word = plane layout (low byte) | option bits.
+ * Layouts: */
+#define WCO_BF16 0         /* hi = sign + exponent bits 7..1 coded, lo raw */
+#define WCO_FP32 1         /* exponent byte coded; sign bits, m0, m1, m2 raw */
+#define WCO_BF16_REORDER 2 /* "PTWM" README, "How it works" 1: exponent byte coded, sign + 7 mantissa bits raw */
+#define WCO_FP16 3         /* 2-plane byte split of the IEEE half: hi = sign, exponent, 2 mantissa bits */
+#define WCO_FP16_REORDER 4 /* same page: hi = 5 exponent bits, sign, 2 mantissa bits; lo = 8 mantissa bits */
+#define WCO_LAYOUT_MASK 0xFF
+/* Options: */
+#define WCO_OPT_TENSOR_TABLE 0x100 /* one frequency table per tensor (its whole coded plane), not per chunk */
+#define WCO_OPT_RAW_FALLBACK 0x200 /* a chunk whose code is not shorter than its symbols stores them raw */
 
 /* status codes */
 #define WCO_OK 0
@@ -51,16 +59,20 @@ typedef struct {
     uint64_t n;                /* elements */
     uint64_t num_chunks;       /* ceil(n / 65536) */
     uint64_t raw_bytes;        /* bytes of the raw (uncoded) planes */
-    uint64_t table_bytes;      /* 512 per chunk */
+    uint64_t table_bytes;      /* 512 per chunk, or 512 with WCO_OPT_TENSOR_TABLE */
     uint64_t seek_bytes;       /* 8 * (chunks + 1) */
     uint64_t payload_capacity; /* worst-case payload bytes */
 } wco_layout;
 
+/* `dtype` arguments below take a whole format word. */
 int wco_query_layout(int dtype, uint64_t n, wco_layout *out);
 
 /* Plane split / merge (byte-plane transform). */
 void wco_split_bf16(const uint16_t *v, uint64_t n, uint8_t *hi, uint8_t *lo);
 void wco_merge_bf16(const uint8_t *hi, const uint8_t *lo, uint64_t n, uint16_t *v);
+/* Any of the 16-bit layouts (BF16, BF16_REORDER, FP16, FP16_REORDER). */
+void wco_split_u16(int layout, const uint16_t *v, uint64_t n, uint8_t *hi, uint8_t *lo);
+void wco_merge_u16(int layout, const uint8_t *hi, const uint8_t *lo, uint64_t n, uint16_t *v);
 /* FP32: exp coded; raw = sign bits (LSB-first, ceil(n/8) B) | m0 | m1 | m2. */
 void wco_split_fp32(const uint32_t *u, uint64_t n, uint8_t *exp, uint8_t *raw);
 void wco_merge_fp32(const uint8_t *exp, const uint8_t *raw, uint64_t n, uint32_t *u);
@@ -68,6 +80,8 @@ void wco_merge_fp32(const uint8_t *exp, const uint8_t *raw, uint64_t n, uint32_t
 /* One chunk. */
 void wco_histogram(const uint8_t *sym, uint32_t n, uint32_t counts[256]);
 void wco_normalize(const uint32_t counts[256], uint32_t total, uint16_t freq[256]);
+/* The same normalisation for counts of a whole tensor (total < 2^52). */
+void wco_normalize64(const uint64_t counts[256], uint64_t total, uint16_t freq[256]);
 /* Encodes n (1..65536) symbols with table freq into out (capacity >= 128 +
  * 2*n + 2).  Returns the chunk payload size in bytes. */
 uint32_t wco_encode_chunk(const uint8_t *sym, uint32_t n, const uint16_t freq[256], uint8_t *out);
