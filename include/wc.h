@@ -22,6 +22,25 @@
  *   - Chunk payload = 32 final states (u32 LE) + words (u16 LE) + one zero
  *     word if the word count is odd.  seek[0] = 0, seek[k+1] = seek[k] +
  *     payload size of chunk k (u64).  tables = 256 u16 per chunk.
+ * Format variants, selected by a format word (plane layout | option bits):
+ *   - WC_BF16_REORDER ("PTWM" README, "How it works" step 1, bit reorder:
+ *     the exponent moves to the top, the sign right below it): the coded
+ *     byte is the 8-bit exponent, the raw byte the sign and 7 mantissa bits.
+ *   - WC_FP16 ("PTWM" README, dtype table: float16 takes a 2-plane byte
+ *     split): the IEEE half's high byte (sign, 5 exponent bits, 2 mantissa
+ *     bits) is coded, its low byte raw.  WC_FP16_REORDER applies the bit
+ *     reorder first: the coded byte is the 5 exponent bits, the sign and 2
+ *     mantissa bits; the raw byte the other 8 mantissa bits.
+ *   - WC_OPT_TENSOR_TABLE: one frequency table per tensor, normalised from
+ *     the histogram of its whole coded plane, codes all of its chunks
+ *     (tables = 256 u16 per tensor; a tensor without elements gets an
+ *     all-zero table).
+ *   - WC_OPT_RAW_FALLBACK ("PTWM" README, "Configuration": store raw bytes
+ *     when compression does not pay; here per chunk): a chunk whose coded
+ *     payload would be at least its symbol count rounded up to 4 bytes is
+ *     stored as its symbols plus zero padding to that size; a payload of
+ *     exactly that size marks such a chunk.
+ *   Format word 0 (WC_BF16) and 1 (WC_FP32) without options is format v1.
  * The result is bit-exact: decode(encode(x)) reproduces every bit pattern,
  * NaN payloads, infinities, subnormals and -0 included (Split12 README: the
  * bar is an exact round trip).
@@ -56,11 +75,25 @@
 extern "C" {
 #endif
 
-typedef enum { WC_BF16 = 0, WC_FP32 = 1 } wc_dtype;
+/* Plane layouts: the low byte of a format word. */
+typedef enum {
+    WC_BF16 = 0,
+    WC_FP32 = 1,
+    WC_BF16_REORDER = 2,
+    WC_FP16 = 3,
+    WC_FP16_REORDER = 4
+} wc_dtype;
+/* Option bits of a format word. */
+#define WC_LAYOUT_MASK 0xFFu
+#define WC_OPT_TENSOR_TABLE 0x100u
+#define WC_OPT_RAW_FALLBACK 0x200u
+/* A plane layout OR-ed with option bits.  Encoder and decoder must be given
+ * the same format word; any other bit set is WC_ERR_ARG. */
+typedef uint32_t wc_format;
 
 typedef enum {
     WC_OK = 0,
-    WC_ERR_ARG = 1,      /* null / misaligned pointer, bad dtype, size out of range */
+    WC_ERR_ARG = 1,      /* null / misaligned pointer, bad format word, size out of range */
     WC_ERR_CAPACITY = 2, /* a buffer is smaller than the layout requires */
     WC_ERR_CORRUPT = 3,  /* (reserved for host-side checks) */
     WC_ERR_HIP = 4       /* a kernel launch failed */
@@ -81,9 +114,10 @@ typedef struct {
     uint64_t n;                /* elements */
     uint64_t num_chunks;       /* ceil(n / 65536) (summed over a batch) */
     uint64_t raw_bytes;        /* raw planes */
-    uint64_t table_bytes;      /* 512 * num_chunks */
+    uint64_t table_bytes;      /* 512 * num_chunks; with WC_OPT_TENSOR_TABLE 512 per tensor */
     uint64_t seek_bytes;       /* 8 * (num_chunks + 1) */
-    uint64_t payload_capacity; /* worst-case payload: 128 + 2 * (len + len % 2) per chunk */
+    uint64_t payload_capacity; /* worst-case payload: 128 + 2 * (len + len % 2) per chunk;
+                                  with WC_OPT_RAW_FALLBACK len rounded up to 4 per chunk */
     uint64_t scratch_bytes;    /* encoder scratch */
 } wc_layout;
 
@@ -117,36 +151,38 @@ int wc_version(void);
 const char *wc_status_string(wc_status s);
 
 /* Layout of one tensor of n elements.  Pure host function. */
-wc_status wc_query_layout(wc_dtype dtype, uint64_t n, wc_layout *out);
+wc_status wc_query_layout(wc_format format, uint64_t n, wc_layout *out);
 
 /* Fills chunk_base and raw_base of segs[0..nseg) (host array; ptr and n are
  * read) and the batch's total layout.  Pure host function. */
-wc_status wc_plan_batch(wc_dtype dtype, wc_segment *segs, uint32_t nseg, wc_layout *total);
+wc_status wc_plan_batch(wc_format format, wc_segment *segs, uint32_t nseg, wc_layout *total);
 
-/* Encode one tensor of n elements at d_in (BF16 as u16 patterns, FP32 as
- * u32 patterns).  Writes out->raw (layout.raw_bytes), out->tables,
+/* Encode one tensor of n elements at d_in (FP32 as u32 patterns, the 16-bit
+ * layouts as u16 patterns).  Writes out->raw (layout.raw_bytes), out->tables,
  * out->seek and out->payload (at most out->payload_bytes; layout's
  * payload_capacity always suffices).  d_scratch must hold
  * layout.scratch_bytes.  stage_events may be NULL or point to 5 events that
  * are recorded on `stream` before the split, after the split, after the rANS
  * kernel, after the scan and after the compaction. */
-wc_status wc_encode(wc_dtype dtype, const void *d_in, uint64_t n, const wc_buffers *out,
+wc_status wc_encode(wc_format format, const void *d_in, uint64_t n, const wc_buffers *out,
                     void *d_scratch, uint64_t scratch_bytes, uint32_t *d_err,
                     hipStream_t stream, hipEvent_t *stage_events);
 
-/* Decode one tensor of n elements into d_out (u16 / u32 bit patterns). */
-wc_status wc_decode(wc_dtype dtype, const wc_buffers *in, uint64_t n, void *d_out,
+/* Decode one tensor of n elements into d_out (u16 / u32 bit patterns).
+ * With WC_OPT_RAW_FALLBACK a chunk stored raw is copied; its padding must be
+ * zero (else WC_EF_BAD_TAIL). */
+wc_status wc_decode(wc_format format, const wc_buffers *in, uint64_t n, void *d_out,
                     uint32_t *d_err, hipStream_t stream);
 
 /* Batched forms: one launch sequence over all chunks of all tensors.
  * h_segs is the host copy of the planned segment array (for validation);
  * d_segs holds the same bytes in device memory (read by the kernels).
  * The scratch size is the batch layout's scratch_bytes. */
-wc_status wc_encode_batch(wc_dtype dtype, const wc_segment *h_segs, const wc_segment *d_segs,
+wc_status wc_encode_batch(wc_format format, const wc_segment *h_segs, const wc_segment *d_segs,
                           uint32_t nseg, const wc_buffers *out, void *d_scratch,
                           uint64_t scratch_bytes, uint32_t *d_err, hipStream_t stream,
                           hipEvent_t *stage_events);
-wc_status wc_decode_batch(wc_dtype dtype, const wc_segment *h_segs, const wc_segment *d_segs,
+wc_status wc_decode_batch(wc_format format, const wc_segment *h_segs, const wc_segment *d_segs,
                           uint32_t nseg, const wc_buffers *in, uint32_t *d_err,
                           hipStream_t stream);
 

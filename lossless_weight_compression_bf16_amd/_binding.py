@@ -14,9 +14,11 @@ from dataclasses import dataclass
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libwc.so")
 
-WC_BF16 = 0
-WC_FP32 = 1
-DTYPE_CODES = {"bf16": WC_BF16, "fp32": WC_FP32}
+WC_BF16, WC_FP32, WC_BF16_REORDER, WC_FP16, WC_FP16_REORDER = 0, 1, 2, 3, 4
+DTYPE_CODES = {"bf16": WC_BF16, "fp32": WC_FP32, "bf16r": WC_BF16_REORDER, "fp16": WC_FP16,
+               "fp16r": WC_FP16_REORDER}
+WC_OPT_TENSOR_TABLE = 0x100
+WC_OPT_RAW_FALLBACK = 0x200
 
 WC_OK, WC_ERR_ARG, WC_ERR_CAPACITY, WC_ERR_CORRUPT, WC_ERR_HIP = 0, 1, 2, 3, 4
 EF_BAD_TABLE = 1
@@ -114,7 +116,18 @@ def _stream(stream) -> int:
 
 
 def _code(dtype) -> int:
+    """Format word of a layout name, or an int format word as given."""
     return DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def format_word(dtype, tensor_table: bool = False, raw_fallback: bool = False) -> int:
+    """A plane layout (name or code) OR-ed with the option bits."""
+    return (_code(dtype) | (WC_OPT_TENSOR_TABLE if tensor_table else 0)
+            | (WC_OPT_RAW_FALLBACK if raw_fallback else 0))
+
+
+def elem_bytes(fmt) -> int:
+    return 4 if (_code(fmt) & 0xFF) == WC_FP32 else 2
 
 
 def error_names(bits: int):

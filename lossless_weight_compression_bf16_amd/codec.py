@@ -1,11 +1,15 @@
-"""Tensor-level API over the C ABI: lossless encode / decode of BF16 and FP32
-weights on the GPU.
+"""Tensor-level API over the C ABI: lossless encode / decode of BF16, FP16 and
+FP32 weights on the GPU.
 
 BF16 is split into its high byte (sign + 7 exponent bits), which is rANS
 coded per 65536-element chunk, and its low byte, which is stored raw (the
 weight-compression / Split12 README's byte split); FP32 keeps sign bits and
 three mantissa bytes raw and codes the exponent byte (the SMEF README's
-sign / exponent / mantissa streams).  Tensors are handled as bit patterns
+sign / exponent / mantissa streams); FP16 takes the same 2-plane byte split
+as BF16.  Options: ``reorder`` applies the PTWM README's bit reorder first
+(16-bit layouts: the coded byte starts with the whole exponent), and
+``tensor_table`` / ``raw_fallback`` select one table per tensor and raw
+storage of chunks that do not shrink.  Tensors are handled as bit patterns
 (uint16 / int32 views), never converted, so every pattern round-trips.
 """
 from __future__ import annotations
@@ -17,17 +21,19 @@ import torch
 from . import _binding as B
 
 
-def _dtype_of(t: torch.Tensor) -> str:
+def _dtype_of(t: torch.Tensor, reorder: bool = False) -> str:
     if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
-        return "bf16"
+        return "bf16r" if reorder else "bf16"
+    if t.dtype == torch.float16:
+        return "fp16r" if reorder else "fp16"
     if t.dtype in (torch.float32, torch.int32, torch.uint32):
         return "fp32"
-    raise TypeError(f"unsupported dtype {t.dtype}: expected bfloat16 or float32")
+    raise TypeError(f"unsupported dtype {t.dtype}: expected bfloat16, float16 or float32")
 
 
-def _bits(t: torch.Tensor, dtype: str) -> torch.Tensor:
+def _bits(t: torch.Tensor, dtype) -> torch.Tensor:
     t = t.contiguous().reshape(-1)
-    t = t.view(torch.int16) if dtype == "bf16" else t.view(torch.int32)
+    t = t.view(torch.int32) if B.elem_bytes(dtype) == 4 else t.view(torch.int16)
     if t.numel() and t.data_ptr() % 16:
         t = t.clone()
     return t
@@ -41,7 +47,7 @@ def _check_device(t: torch.Tensor):
 @dataclass
 class Encoded:
     """One encoded tensor; every buffer is a device tensor."""
-    dtype: str                 # "bf16" or "fp32"
+    dtype: str                 # layout: "bf16", "bf16r", "fp16", "fp16r" or "fp32"
     n: int                     # elements
     shape: tuple
     torch_dtype: torch.dtype
@@ -49,6 +55,7 @@ class Encoded:
     tables: torch.Tensor       # int16 (u16 bit patterns), chunks x 256
     seek: torch.Tensor         # int64 (u64), chunks + 1
     payload: torch.Tensor      # uint8, seek[-1] bytes
+    fmt: int = 0               # format word (layout | options)
 
     @property
     def num_chunks(self) -> int:
@@ -60,7 +67,7 @@ class Encoded:
 
     @property
     def raw_input_bytes(self) -> int:
-        return self.n * (2 if self.dtype == "bf16" else 4)
+        return self.n * B.elem_bytes(self.dtype)
 
     @property
     def ratio(self) -> float:
@@ -79,28 +86,30 @@ def _raise_bits(bits: int, what: str):
         raise B.WcError(f"{what}: device reported {', '.join(B.error_names(bits))} (bits {bits:#x})")
 
 
-def encode(t: torch.Tensor, stream=None) -> Encoded:
-    """Losslessly encode a bf16 / fp32 device tensor (synchronises once to
-    size the payload)."""
+def encode(t: torch.Tensor, stream=None, reorder: bool = False, tensor_table: bool = False,
+           raw_fallback: bool = False) -> Encoded:
+    """Losslessly encode a bf16 / fp16 / fp32 device tensor (synchronises once
+    to size the payload)."""
     _check_device(t)
-    dtype = _dtype_of(t)
+    dtype = _dtype_of(t, reorder)
+    fmt = B.format_word(dtype, tensor_table, raw_fallback)
     x = _bits(t, dtype)
     n = x.numel()
     dev = x.device
-    lay = B.wc_query_layout(dtype, n)
+    lay = B.wc_query_layout(fmt, n)
     raw = torch.empty(max(lay.raw_bytes, 1), dtype=torch.uint8, device=dev)
-    tables = torch.empty(max(lay.num_chunks * 256, 8), dtype=torch.int16, device=dev)
+    tables = torch.empty(max(lay.table_bytes // 2, 8), dtype=torch.int16, device=dev)
     seek = torch.empty(lay.num_chunks + 1, dtype=torch.int64, device=dev)
     payload = torch.empty(max(lay.payload_capacity, 16), dtype=torch.uint8, device=dev)
     scratch = torch.empty(max(lay.scratch_bytes, 256), dtype=torch.uint8, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     bufs = B.make_buffers(raw, tables, seek, payload, lay.payload_capacity)
-    B.wc_encode(dtype, x, n, bufs, scratch, scratch.numel(), err, stream)
+    B.wc_encode(fmt, x, n, bufs, scratch, scratch.numel(), err, stream)
     total = int(seek[-1].item())
     _raise_bits(int(err.item()), "encode")
     del scratch
     return Encoded(dtype, n, tuple(t.shape), t.dtype, raw[: lay.raw_bytes],
-                   tables[: lay.num_chunks * 256].view(-1, 256), seek, payload[:total].clone())
+                   tables[: lay.table_bytes // 2].view(-1, 256), seek, payload[:total].clone(), fmt)
 
 
 def decode(e: Encoded, out: torch.Tensor | None = None, stream=None, check: bool = True) -> torch.Tensor:
@@ -112,7 +121,7 @@ def decode(e: Encoded, out: torch.Tensor | None = None, stream=None, check: bool
     if x is None or x.data_ptr() != out.data_ptr():
         raise ValueError("out must be a contiguous, 16-byte aligned tensor")
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    B.wc_decode(e.dtype, e.buffers(), e.n, x, err, stream)
+    B.wc_decode(e.fmt or e.dtype, e.buffers(), e.n, x, err, stream)
     if check:
         _raise_bits(int(err.item()), "decode")
     return out
@@ -131,6 +140,7 @@ class EncodedBatch:
     seek: torch.Tensor
     payload: torch.Tensor
     h_segs: object = field(repr=False, default=None)
+    fmt: int = 0
 
     @property
     def compressed_bytes(self) -> int:
@@ -138,7 +148,7 @@ class EncodedBatch:
 
     @property
     def raw_input_bytes(self) -> int:
-        return sum(self.ns) * (2 if self.dtype == "bf16" else 4)
+        return sum(self.ns) * B.elem_bytes(self.dtype)
 
     @property
     def ratio(self) -> float:
@@ -164,32 +174,34 @@ def segments_to_device(h_segs, nseg: int, dev) -> torch.Tensor:
     return host.to(dev)
 
 
-def encode_batch(ts, stream=None) -> EncodedBatch:
+def encode_batch(ts, stream=None, reorder: bool = False, tensor_table: bool = False,
+                 raw_fallback: bool = False) -> EncodedBatch:
     """Encode a list of same-dtype device tensors in one launch sequence."""
     if not ts:
         raise ValueError("empty batch")
     for t in ts:
         _check_device(t)
-    dtype = _dtype_of(ts[0])
-    if any(_dtype_of(t) != dtype for t in ts):
+    dtype = _dtype_of(ts[0], reorder)
+    if any(_dtype_of(t, reorder) != dtype for t in ts):
         raise TypeError("all tensors of a batch must share a dtype")
+    fmt = B.format_word(dtype, tensor_table, raw_fallback)
     xs = [_bits(t, dtype) for t in ts]
     dev = xs[0].device
-    h_segs, d_segs, tot = _segments(dtype, xs, dev)
+    h_segs, d_segs, tot = _segments(fmt, xs, dev)
     raw = torch.empty(max(tot.raw_bytes, 16), dtype=torch.uint8, device=dev)
-    tables = torch.empty(max(tot.num_chunks * 256, 8), dtype=torch.int16, device=dev)
+    tables = torch.empty(max(tot.table_bytes // 2, 8), dtype=torch.int16, device=dev)
     seek = torch.empty(tot.num_chunks + 1, dtype=torch.int64, device=dev)
     payload = torch.empty(max(tot.payload_capacity, 16), dtype=torch.uint8, device=dev)
     scratch = torch.empty(max(tot.scratch_bytes, 256), dtype=torch.uint8, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     bufs = B.make_buffers(raw, tables, seek, payload, tot.payload_capacity)
-    B.wc_encode_batch(dtype, h_segs, d_segs, len(xs), bufs, scratch, scratch.numel(), err, stream)
+    B.wc_encode_batch(fmt, h_segs, d_segs, len(xs), bufs, scratch, scratch.numel(), err, stream)
     total = int(seek[-1].item())
     _raise_bits(int(err.item()), "encode_batch")
     del scratch
     return EncodedBatch(dtype, [x.numel() for x in xs], [tuple(t.shape) for t in ts], ts[0].dtype,
-                        raw[: tot.raw_bytes], tables[: tot.num_chunks * 256].view(-1, 256), seek,
-                        payload[:total].clone(), h_segs)
+                        raw[: tot.raw_bytes], tables[: tot.table_bytes // 2].view(-1, 256), seek,
+                        payload[:total].clone(), h_segs, fmt)
 
 
 def decode_batch(e: EncodedBatch, outs=None, stream=None, check: bool = True):
@@ -201,9 +213,10 @@ def decode_batch(e: EncodedBatch, outs=None, stream=None, check: bool = True):
     for o, x in zip(outs, xs):
         if x.numel() and x.data_ptr() != o.data_ptr():
             raise ValueError("outputs must be contiguous and 16-byte aligned")
-    h_segs, d_segs, _ = _segments(e.dtype, xs, dev)
+    fmt = e.fmt or e.dtype
+    h_segs, d_segs, _ = _segments(fmt, xs, dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    B.wc_decode_batch(e.dtype, h_segs, d_segs, len(xs), e.buffers(), err, stream)
+    B.wc_decode_batch(fmt, h_segs, d_segs, len(xs), e.buffers(), err, stream)
     if check:
         _raise_bits(int(err.item()), "decode_batch")
     return outs

@@ -25,10 +25,64 @@ constexpr uint64_t kMaxElems = 1ull << 40;
 
 inline __host__ __device__ uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
-inline __host__ __device__ uint64_t raw_bytes_of(int dtype, uint64_t n)
+// Raw plane bytes of n elements: one raw byte per element for the 16-bit
+// layouts; sign bits plus three mantissa bytes for FP32.
+inline __host__ __device__ uint64_t raw_bytes_of(int layout, uint64_t n)
 {
-    return dtype == WC_BF16 ? n : (n + 7) / 8 + 3 * n;
+    return layout != WC_FP32 ? n : (n + 7) / 8 + 3 * n;
 }
+
+// Payload of a chunk of len symbols stored raw (WC_OPT_RAW_FALLBACK).
+inline __host__ __device__ uint32_t raw_chunk_bytes(uint32_t len) { return (len + 3u) & ~3u; }
+
+// The 16-bit layouts.  Their coded byte is the high byte and their raw byte
+// the low byte of a rearrangement of the value's 16 bits: none for BF16 and
+// FP16; for the _REORDER layouts the bit reorder of the "PTWM" README ("How
+// it works", step 1), which moves the exponent field to the top and the sign
+// right below it, i.e. rotates the sign + exponent field left by one bit.
+// Both directions work on two values packed in a u32 (a shift pair and two
+// bit selects); a lone value zero-extended to 32 bits stays below 2^16.
+inline __host__ __device__ uint32_t bitsel(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+template <int DT>
+struct Bits16 {
+    __host__ __device__ static uint32_t to_coded(uint32_t v) { return v; }
+    __host__ __device__ static uint32_t from_coded(uint32_t t) { return t; }
+};
+
+// s e8 m7 <-> e8 s m7
+template <>
+struct Bits16<WC_BF16_REORDER> {
+    __host__ __device__ static uint32_t to_coded(uint32_t v)
+    {
+        return bitsel(0x007F007Fu, v, bitsel(0x00800080u, v >> 8, v << 1));
+    }
+    __host__ __device__ static uint32_t from_coded(uint32_t t)
+    {
+        return bitsel(0x007F007Fu, t, bitsel(0x80008000u, t << 8, t >> 1));
+    }
+};
+
+// s e5 m10 <-> e5 s m10
+template <>
+struct Bits16<WC_FP16_REORDER> {
+    __host__ __device__ static uint32_t to_coded(uint32_t v)
+    {
+        return bitsel(0x03FF03FFu, v, bitsel(0x04000400u, v >> 5, v << 1));
+    }
+    __host__ __device__ static uint32_t from_coded(uint32_t t)
+    {
+        return bitsel(0x03FF03FFu, t, bitsel(0x80008000u, t << 5, t >> 1));
+    }
+};
+
+// Kernel options (the option bits of the format word, passed as a uniform
+// kernel argument).
+struct Opts {
+    uint32_t bits;
+    __host__ __device__ bool tensor_table() const { return bits & WC_OPT_TENSOR_TABLE; }
+    __host__ __device__ bool raw_fallback() const { return bits & WC_OPT_RAW_FALLBACK; }
+};
 
 // Device addresses held as integers (segment tables) are always global
 // memory; saying so lets the compiler emit global_* instead of flat_*
@@ -59,14 +113,20 @@ struct SegTable {
 
 // The segment that owns global chunk k: the last one whose chunk_base <= k
 // (empty segments share their chunk_base with the next one and are skipped).
-__device__ inline wc_segment find_segment(const SegTable &st, uint64_t k)
+// idx receives its index (0 for a single tensor): its table with
+// WC_OPT_TENSOR_TABLE.
+__device__ inline wc_segment find_segment(const SegTable &st, uint64_t k, uint32_t *idx = nullptr)
 {
-    if (st.nseg == 0) return st.single;
+    if (st.nseg == 0) {
+        if (idx) *idx = 0;
+        return st.single;
+    }
     uint32_t lo = 0, hi = st.nseg;
     while (hi - lo > 1) {
         uint32_t mid = (lo + hi) >> 1;
         if (st.segs[mid].chunk_base <= k) lo = mid; else hi = mid;
     }
+    if (idx) *idx = lo;
     return st.segs[lo];
 }
 

@@ -30,7 +30,9 @@
 // At the end of a group each lane joins 8 consecutive decoded bytes with 8
 // raw bytes (loaded with one 8-byte load issued two groups earlier) and
 // writes 8 BF16 values with one 16-byte store: the output is written once,
-// coalesced, straight to HBM.
+// coalesced, straight to HBM.  The reordered 16-bit layouts undo their bit
+// rearrangement on the joined pairs before that store.  Chunks stored raw
+// (WC_OPT_RAW_FALLBACK) are skipped here and copied by k_decode_raw.
 #pragma once
 
 #include <type_traits>
@@ -144,10 +146,8 @@ __device__ __forceinline__ void refill_sync(Stream &st, uint32_t lane, bool ok, 
 // early); flush(): joins them with the 8 decoded bytes and stores.
 
 template <int DT>
-struct RawView;
-
-template <>
-struct RawView<WC_BF16> {
+struct RawView {  // the 16-bit layouts
+    using B = Bits16<DT>;
     const WC_GLOBAL uint8_t *lo;
     WC_GLOBAL uint16_t *out;
     struct Pre {
@@ -166,12 +166,13 @@ struct RawView<WC_BF16> {
     }
     __device__ void flush(uint32_t e, uint2 sym, const Pre &p) const
     {
-        // out[i] = sym[i] << 8 | lo[i]: interleave the bytes pairwise
+        // out[i] = sym[i] << 8 | lo[i]: interleave the bytes pairwise, then
+        // undo the layout's bit rearrangement (nothing for BF16 / FP16)
         u32x4 o;
-        o.x = __builtin_amdgcn_perm(sym.x, p.v.x, 0x05010400u);
-        o.y = __builtin_amdgcn_perm(sym.x, p.v.x, 0x07030602u);
-        o.z = __builtin_amdgcn_perm(sym.y, p.v.y, 0x05010400u);
-        o.w = __builtin_amdgcn_perm(sym.y, p.v.y, 0x07030602u);
+        o.x = B::from_coded(__builtin_amdgcn_perm(sym.x, p.v.x, 0x05010400u));
+        o.y = B::from_coded(__builtin_amdgcn_perm(sym.x, p.v.x, 0x07030602u));
+        o.z = B::from_coded(__builtin_amdgcn_perm(sym.y, p.v.y, 0x05010400u));
+        o.w = B::from_coded(__builtin_amdgcn_perm(sym.y, p.v.y, 0x07030602u));
         *reinterpret_cast<WC_GLOBAL u32x4 *>(out + e) = o;
     }
     // tail chunks: only elements below len exist
@@ -194,7 +195,7 @@ struct RawView<WC_BF16> {
             const uint32_t sh = 8 * (i & 3);
             const uint32_t sb = ((i < 4 ? sym.x : sym.y) >> sh) & 0xFF;
             const uint32_t lb = ((i < 4 ? p.v.x : p.v.y) >> sh) & 0xFF;
-            out[e + i] = (uint16_t)((sb << 8) | lb);
+            out[e + i] = (uint16_t)B::from_coded((sb << 8) | lb);
         }
     }
 };
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
                                                     const uint64_t *__restrict__ seek,
                                                     const uint8_t *__restrict__ payload,
                                                     uint64_t payload_bytes, uint64_t total_chunks,
-                                                    uint32_t *err)
+                                                    uint32_t *err, Opts opts)
 {
     using Sh = typename std::conditional<kL1, DecSharedL1<kH>, DecSharedL2<kH>>::type;
     __shared__ Sh sh;
@@ -379,16 +380,25 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     bool ok = true;
     uint32_t bits = 0;
 
-    const wc_segment sg = find_segment(st, k);
+    uint32_t sidx;
+    const wc_segment sg = find_segment(st, k, &sidx);
     const uint64_t start = (k - sg.chunk_base) * kChunk;
     const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
+    const uint64_t tix = opts.tensor_table() ? sidx : k;
     // A half with a bad seek entry still issues its refill loads (never
     // used): they read the first dword at base, here the chunk's own table.
-    Stream cs{gptr(reinterpret_cast<const uint8_t *>(tables + k * 256)), 0, 0, 0, 0, 0};
+    Stream cs{gptr(reinterpret_cast<const uint8_t *>(tables + tix * 256)), 0, 0, 0, 0, 0};
     uint32_t x = kL;
+    // a chunk stored raw (WC_OPT_RAW_FALLBACK) takes no part in the rANS
+    // loop (like a bad one, but reports nothing): k_decode_raw copies it
     {
         const uint64_t a = seek[k], b = seek[k + 1];
-        if (a > b || b > payload_bytes || b - a < 128 || ((b - a) & 3) || (a & 3)) {
+        if (a > b || b > payload_bytes || (a & 3)) {
+            bits |= WC_EF_BAD_SEEK;
+            ok = false;
+        } else if (opts.raw_fallback() && b - a == raw_chunk_bytes(len)) {
+            ok = false;
+        } else if (b - a < 128 || ((b - a) & 3)) {
             bits |= WC_EF_BAD_SEEK;
             ok = false;
         } else {
@@ -400,7 +410,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     // table: 8 symbols per lane, validated (sum 4096) before it is used
     uint32_t f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (ok) {
-        const u32x4 fv = gptr(reinterpret_cast<const u32x4 *>(tables + k * 256))[lane];
+        const u32x4 fv = gptr(reinterpret_cast<const u32x4 *>(tables + tix * 256))[lane];
         f[0] = fv.x & 0xFFFF; f[1] = fv.x >> 16; f[2] = fv.y & 0xFFFF; f[3] = fv.y >> 16;
         f[4] = fv.z & 0xFFFF; f[5] = fv.z >> 16; f[6] = fv.w & 0xFFFF; f[7] = fv.w >> 16;
     }
@@ -596,6 +606,41 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     // OR the half's bits into lane 0 of the half; a shadow half reports nothing
     for (int o = 16; o > 0; o >>= 1) bits |= __shfl_xor(bits, o, 32);
     if (lane == 0 && bits && real && err) atomicOr(err, bits);
+}
+
+// Chunks stored raw (WC_OPT_RAW_FALLBACK), after k_decode (which skips
+// them): one 256-thread block per chunk; a block whose chunk is coded, or
+// whose seek entries are bad (k_decode reports those), exits at once.  The
+// payload holds the chunk's symbols, zero-padded to a multiple of 4 bytes;
+// they are joined with the raw plane exactly like decoded ones.
+template <int DT>
+__global__ __launch_bounds__(256) void k_decode_raw(SegTable st, const uint8_t *__restrict__ raw,
+                                                    const uint64_t *__restrict__ seek,
+                                                    const uint8_t *__restrict__ payload, uint64_t payload_bytes,
+                                                    uint32_t *err)
+{
+    const uint64_t k = blockIdx.x;
+    const wc_segment sg = find_segment(st, k);
+    const uint64_t start = (k - sg.chunk_base) * kChunk;
+    const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
+    const uint64_t a = seek[k], b = seek[k + 1];
+    if (a > b || b > payload_bytes || (a & 3) || b - a != raw_chunk_bytes(len)) return;
+    RawView<DT> rv;
+    rv.init(raw, sg, start);
+    const WC_GLOBAL uint8_t *pl = gptr(payload) + a;
+    const WC_GLOBAL uint32_t *pw = reinterpret_cast<const WC_GLOBAL uint32_t *>(pl);
+    for (uint32_t e = 8 * threadIdx.x; e < len; e += 8 * 256) {
+        uint2 sy;
+        if (e + 8 <= len) {
+            sy = make_uint2(pw[e / 4], pw[e / 4 + 1]);
+        } else {
+            uint32_t v[2] = {0, 0};
+            for (uint32_t i = 0; e + i < len; i++) v[i >> 2] |= (uint32_t)pl[e + i] << (8 * (i & 3));
+            sy = make_uint2(v[0], v[1]);
+        }
+        rv.flush_checked(e, sy, rv.fetch_checked(e, len), len);
+    }
+    if (len + threadIdx.x < raw_chunk_bytes(len) && pl[len + threadIdx.x] != 0 && err) atomicOr(err, WC_EF_BAD_TAIL);
 }
 
 }  // namespace wc

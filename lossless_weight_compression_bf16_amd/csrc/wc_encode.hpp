@@ -61,21 +61,23 @@ __device__ inline uint32_t block_rank256(bool p, uint32_t *red, uint32_t *total)
 // largest f, smaller symbol on ties" repeated E times would remove it,
 // computed in closed form: every f is cut to a level v+1 and the smallest
 // symbols at that level drop to v, where v is the largest level whose cut
-// removes at least E.
-__device__ inline uint32_t normalize256(uint32_t c, uint32_t T, uint32_t *red, uint32_t *keys)
+// removes at least E.  C is the count type: 32 bits for a chunk (c 4096 <=
+// 2^28), 64 bits for a whole tensor's histogram (T < 2^52).
+template <typename C>
+__device__ inline uint32_t normalize256(C c, C T, uint32_t *red, C *keys)
 {
     const uint32_t s = threadIdx.x;
-    const uint32_t scaled = c * kM;  // <= 2^28
-    const uint32_t q = scaled / T;
-    const uint32_t r = scaled - q * T;
+    const C scaled = c * (C)kM;
+    const C q = scaled / T;  // <= 4096
+    const C r = scaled - q * T;
     const bool regular = q >= 1;
-    uint32_t f = c ? (regular ? q : 1u) : 0u;
+    uint32_t f = c ? (regular ? (uint32_t)q : 1u) : 0u;
     const int32_t d = (int32_t)kM - (int32_t)block_sum256(f, red);
 
     if (d > 0) {
         uint32_t m;
         uint32_t pos = block_rank256(regular, red, &m);
-        const uint32_t key = r * 256u + (255u - s);  // r < 65536: unique, fits 24 bits
+        const C key = r * 256u + (255u - s);  // unique per symbol
         if (regular) keys[pos] = key;
         __syncthreads();
         if (regular) {
@@ -120,16 +122,22 @@ __device__ inline void hist_add(uint32_t *my, uint32_t b)
     atomicAdd(&my[b >> 1], 1u << ((b & 1u) << 4));
 }
 
+// With a tensor-wide table (WC_OPT_TENSOR_TABLE) the chunk's counts are
+// added to its tensor's 64-bit histogram in acc instead, and k_tensor_table
+// normalises those.
 template <int DT>
 __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__restrict__ raw,
-                                                    uint16_t *__restrict__ tables, uint64_t raw_total)
+                                                    uint16_t *__restrict__ tables, uint64_t raw_total, Opts opts,
+                                                    unsigned long long *__restrict__ acc)
 {
     __shared__ uint32_t hist[kHistCopies * kHistStride];
     __shared__ uint32_t red[4];
     __shared__ uint32_t keys[256];
+    using B = Bits16<DT>;
 
     const uint64_t k = blockIdx.x;
-    const wc_segment sg = find_segment(st, k);
+    uint32_t sidx;
+    const wc_segment sg = find_segment(st, k, &sidx);
     const uint64_t start = (k - sg.chunk_base) * kChunk;
     const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
     const uint32_t tid = threadIdx.x;
@@ -144,7 +152,9 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
     __syncthreads();
     uint32_t *my = hist + (tid & (kHistCopies - 1)) * kHistStride;
 
-    if constexpr (DT == WC_BF16) {
+    if constexpr (DT != WC_FP32) {
+        // 16-bit layouts: the coded / raw bytes are the high / low bytes of
+        // the layout's rearrangement of each value
         const WC_GLOBAL uint16_t *in = gptr<uint16_t>(sg.ptr) + start;
         WC_GLOBAL uint8_t *lo = gptr(raw) + sg.raw_base + start;
         const uint32_t ng = len / 8;  // groups of 8 elements = 16 bytes
@@ -157,6 +167,7 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
             for (uint32_t u = 0; u < U; u++) v[u] = reinterpret_cast<const WC_GLOBAL u32x4 *>(in)[g + 256 * u];
 #pragma unroll
             for (uint32_t u = 0; u < U; u++) {
+                v[u] = u32x4{B::to_coded(v[u].x), B::to_coded(v[u].y), B::to_coded(v[u].z), B::to_coded(v[u].w)};
                 const u32x2 l = u32x2{__builtin_amdgcn_perm(v[u].y, v[u].x, 0x06040200u),
                                       __builtin_amdgcn_perm(v[u].w, v[u].z, 0x06040200u)};
                 reinterpret_cast<WC_GLOBAL u32x2 *>(lo)[g + 256 * u] = l;
@@ -169,7 +180,8 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
             }
         }
         for (; g < ng; g += 256) {
-            const u32x4 v = reinterpret_cast<const WC_GLOBAL u32x4 *>(in)[g];
+            u32x4 v = reinterpret_cast<const WC_GLOBAL u32x4 *>(in)[g];
+            v = u32x4{B::to_coded(v.x), B::to_coded(v.y), B::to_coded(v.z), B::to_coded(v.w)};
             const u32x2 l = u32x2{__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
                                   __builtin_amdgcn_perm(v.w, v.z, 0x06040200u)};
             reinterpret_cast<WC_GLOBAL u32x2 *>(lo)[g] = l;
@@ -179,7 +191,7 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
             for (uint32_t i = 0; i < 4; i++) hist_add(my, (h1 >> (8 * i)) & 0xFF);
         }
         for (uint32_t i = ng * 8 + tid; i < len; i += 256) {
-            const uint32_t e = in[i];
+            const uint32_t e = B::to_coded(in[i]);
             lo[i] = (uint8_t)(e & 0xFF);
             hist_add(my, e >> 8);
         }
@@ -216,8 +228,32 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
     const uint32_t word = tid >> 1, shift = (tid & 1) << 4;
 #pragma unroll 8
     for (uint32_t i = 0; i < kHistCopies; i++) c += (hist[i * kHistStride + word] >> shift) & 0xFFFF;
-    const uint32_t f = normalize256(c, len, red, keys);
+    if (opts.tensor_table()) {
+        if (c) atomicAdd(&acc[256ull * sidx + tid], (unsigned long long)c);
+        return;
+    }
+    const uint32_t f = normalize256<uint32_t>(c, len, red, keys);
     tables[k * 256 + tid] = (uint16_t)f;
+}
+
+// Tensor-wide tables: zero the 64-bit histograms, then (after k_split_hist)
+// one block per tensor normalises its histogram with T = its element count;
+// a tensor without elements gets an all-zero table.
+__global__ __launch_bounds__(256) void k_zero_u64(unsigned long long *__restrict__ p, uint64_t n)
+{
+    for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (uint64_t)gridDim.x * 256) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_tensor_table(SegTable st, const unsigned long long *__restrict__ acc,
+                                                      uint16_t *__restrict__ tables)
+{
+    __shared__ uint32_t red[4];
+    __shared__ uint64_t keys[256];
+    const uint32_t i = blockIdx.x, tid = threadIdx.x;
+    const uint64_t n = st.nseg ? st.segs[i].n : st.single.n;
+    uint32_t f = 0;
+    if (n) f = normalize256<uint64_t>(acc[256ull * i + tid], n, red, keys);
+    tables[256ull * i + tid] = (uint16_t)f;
 }
 
 // ------------------------------------------------------------------ encoder
@@ -239,7 +275,7 @@ constexpr uint32_t kEncBlk = kLanes * kEncGroup;
 // groups ahead of use.
 template <int DT>
 struct SymView {
-    using Elem = typename std::conditional<DT == WC_BF16, uint16_t, uint32_t>::type;
+    using Elem = typename std::conditional<DT != WC_FP32, uint16_t, uint32_t>::type;
     const WC_GLOBAL Elem *in;
     struct Pre {
         uint32_t e[kEncGroup];
@@ -258,7 +294,7 @@ struct SymView {
     }
     __device__ static uint32_t symbol(uint32_t e)
     {
-        if constexpr (DT == WC_BF16) return e >> 8;
+        if constexpr (DT != WC_FP32) return Bits16<DT>::to_coded(e) >> 8;
         else return (e >> 23) & 0xFF;
     }
 };
@@ -267,20 +303,19 @@ struct SymView {
 // wide loads; their coded bytes pass through an LDS stage to the lanes that
 // encode them (step i of lane l encodes element 32 i + l of the group).
 template <int DT>
-struct WideView;
-
-template <>
-struct WideView<WC_BF16> {
+struct WideView {  // the 16-bit layouts
     const WC_GLOBAL u32x4 *in;  // the chunk; 16 bytes = 8 elements per lane per group
     struct Pre {
         u32x4 v;
     };
     __device__ Pre fetch(uint32_t g, uint32_t lane) const { return Pre{in[kLanes * g + lane]}; }
-    // the high bytes of the 8 elements, in element order
+    // the coded (high) bytes of the 8 elements, in element order
     __device__ static uint2 bytes(const Pre &p)
     {
-        return make_uint2(__builtin_amdgcn_perm(p.v.y, p.v.x, 0x07050301u),
-                          __builtin_amdgcn_perm(p.v.w, p.v.z, 0x07050301u));
+        using B = Bits16<DT>;
+        const uint32_t x = B::to_coded(p.v.x), y = B::to_coded(p.v.y);
+        const uint32_t z = B::to_coded(p.v.z), w = B::to_coded(p.v.w);
+        return make_uint2(__builtin_amdgcn_perm(y, x, 0x07050301u), __builtin_amdgcn_perm(w, z, 0x07050301u));
     }
 };
 
@@ -332,10 +367,14 @@ __device__ __forceinline__ void enc_step(uint32_t &x, uint32_t &p, bool active, 
     if (!CHECK || active) x = xn;
 }
 
+// meta[k].y of a chunk stored raw (WC_OPT_RAW_FALLBACK): its slot holds the
+// symbols from offset 0 and meta[k].x their padded size.
+constexpr uint32_t kRawMark = 0xFFFFFFFFu;
+
 template <int DT>
 __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__restrict__ tables,
                                                uint8_t *__restrict__ slots, uint2 *__restrict__ meta,
-                                               uint64_t total_chunks)
+                                               uint64_t total_chunks, Opts opts)
 {
     __shared__ EncSym enc[2][256];
     __shared__ uint32_t estage[2][kEncBlk / 4];  // one full group's coded bytes per half
@@ -346,12 +385,14 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     const bool real = k_own < total_chunks;
     const uint64_t k = real ? k_own : k_own - 1;
 
-    const wc_segment sg = find_segment(st, k);
+    uint32_t sidx;
+    const wc_segment sg = find_segment(st, k, &sidx);
     const uint64_t start = (k - sg.chunk_base) * kChunk;
     const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
+    const uint64_t tix = opts.tensor_table() ? sidx : k;
     {
         // table: 8 symbols per lane, cumulative start by a scan over the half
-        const u32x4 fv = gptr(reinterpret_cast<const u32x4 *>(tables + k * 256))[lane];
+        const u32x4 fv = gptr(reinterpret_cast<const u32x4 *>(tables + tix * 256))[lane];
         uint32_t f[8] = {fv.x & 0xFFFF, fv.x >> 16, fv.y & 0xFFFF, fv.y >> 16,
                          fv.z & 0xFFFF, fv.z >> 16, fv.w & 0xFFFF, fv.w >> 16};
         uint32_t local = 0;
@@ -468,10 +509,24 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     }
 
     if (real) {
-        reinterpret_cast<WC_GLOBAL uint32_t *>(slot)[lane] = x;
-        if (lane == 0) {
-            const uint32_t nw = kMaxWords - p_w;
-            meta[k] = make_uint2(128u + 2u * nw + 2u * (nw & 1u), p_w);
+        const uint32_t nw = kMaxWords - p_w;  // equal in the half's lanes
+        const uint32_t size = 128u + 2u * nw + 2u * (nw & 1u);
+        const uint32_t rsize = raw_chunk_bytes(len);
+        if (opts.raw_fallback() && size >= rsize) {
+            // not worth coding: the slot takes the symbols, zero-padded
+            for (uint32_t g = 0; g * kEncBlk < len; g++) {
+                const Pre cur = sv.template fetch<true>(g, lane, len);
+#pragma unroll
+                for (uint32_t i = 0; i < kEncGroup; i++) {
+                    const uint32_t j = kEncBlk * g + kLanes * i + lane;
+                    if (j < len) slot[j] = (uint8_t)SymView<DT>::symbol(cur.e[i]);
+                }
+            }
+            if (len + lane < rsize) slot[len + lane] = 0;
+            if (lane == 0) meta[k] = make_uint2(rsize, kRawMark);
+        } else {
+            reinterpret_cast<WC_GLOBAL uint32_t *>(slot)[lane] = x;
+            if (lane == 0) meta[k] = make_uint2(size, p_w);
         }
     }
 }
@@ -557,10 +612,14 @@ __global__ __launch_bounds__(256) void k_compact(const uint8_t *__restrict__ slo
     const uint2 mk = meta[k];
     const uint64_t dst_off = seek[k];
     if (dst_off + mk.x > capacity) return;  // reported by the scan
-    const uint32_t p = mk.y, nw = kMaxWords - p, ndw = (nw + 1) / 2;
     const WC_GLOBAL uint32_t *src = reinterpret_cast<const WC_GLOBAL uint32_t *>(gptr(slots) + k * kSlotBytes);
     WC_GLOBAL uint32_t *dst = reinterpret_cast<WC_GLOBAL uint32_t *>(gptr(payload) + dst_off);
     const uint32_t tid = threadIdx.x;
+    if (mk.y == kRawMark) {  // a chunk stored raw: its padded symbols, as dwords
+        for (uint32_t i = tid; i < mk.x / 4; i += 256) dst[i] = src[i];
+        return;
+    }
+    const uint32_t p = mk.y, nw = kMaxWords - p, ndw = (nw + 1) / 2;
     if (tid < 32) dst[tid] = src[tid];
     // word area as dwords: word j is half (j & 1) of dword j / 2; output
     // dword i holds words p + 2 i and p + 2 i + 1.  Up to 16 dwords per

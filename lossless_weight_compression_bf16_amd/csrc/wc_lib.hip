@@ -2,7 +2,8 @@
 //
 // Host side: argument validation, buffer layout, and the launch sequence
 //   encode: k_split_hist -> k_encode -> k_scan_tiles, k_scan_apply -> k_compact
-//   decode: k_decode
+//           (tensor-wide tables: k_zero_u64 before the split, k_tensor_table after)
+//   decode: k_decode (then k_decode_raw for chunks stored raw)
 // on the caller's stream.  No allocation, no synchronisation, no global state.
 #include <hip/hip_runtime.h>
 
@@ -18,36 +19,48 @@ using namespace wc;
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0: format variants
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 uint64_t chunk_capacity(uint64_t len) { return 128 + 2 * (len + (len & 1)); }
 
-void layout_of(int dtype, uint64_t n, wc_layout *out)
+bool valid_format(uint32_t f)
+{
+    return (f & WC_LAYOUT_MASK) <= WC_FP16_REORDER &&
+           (f & ~(WC_LAYOUT_MASK | WC_OPT_TENSOR_TABLE | WC_OPT_RAW_FALLBACK)) == 0;
+}
+int layout_code(uint32_t f) { return (int)(f & WC_LAYOUT_MASK); }
+Opts opts_of(uint32_t f) { return Opts{f & (WC_OPT_TENSOR_TABLE | WC_OPT_RAW_FALLBACK)}; }
+
+void layout_of(uint32_t format, uint64_t n, wc_layout *out)
 {
     const uint64_t c = (n + kChunk - 1) / kChunk;
+    const bool rawfb = opts_of(format).raw_fallback();
+    auto cap = [&](uint64_t len) { return rawfb ? (uint64_t)raw_chunk_bytes((uint32_t)len) : chunk_capacity(len); };
     out->n = n;
     out->num_chunks = c;
-    out->raw_bytes = raw_bytes_of(dtype, n);
-    out->table_bytes = 512 * c;
+    out->raw_bytes = raw_bytes_of(layout_code(format), n);
+    out->table_bytes = opts_of(format).tensor_table() ? 512 : 512 * c;
     out->seek_bytes = 8 * (c + 1);
     out->payload_capacity = 0;
-    if (c) out->payload_capacity = (c - 1) * chunk_capacity(kChunk) + chunk_capacity(n - (c - 1) * kChunk);
+    if (c) out->payload_capacity = (c - 1) * cap(kChunk) + cap(n - (c - 1) * kChunk);
     out->scratch_bytes = 0;
 }
 
-uint64_t scratch_bytes_for(uint64_t chunks)
+// Encoder scratch: 8 bytes of meta per chunk, one slot per chunk plus a
+// spare one (written by the idle half of the last wavefront when the chunk
+// count is odd; the scan's tile sums go there afterwards), and with
+// tensor-wide tables a 256 x u64 histogram per tensor.
+uint64_t hist_offset(uint64_t chunks) { return align_up(8 * chunks, 256) + (chunks + 1) * kSlotBytes; }
+uint64_t scratch_bytes_for(uint64_t chunks, uint64_t tensor_tables)
 {
-    // one slot per chunk plus a spare one written by the idle half of the
-    // last wavefront when the chunk count is odd
-    return chunks ? align_up(8 * chunks, 256) + (chunks + 1) * kSlotBytes : 0;
+    return chunks ? hist_offset(chunks) + 2048 * tensor_tables : 0;
 }
 
-bool valid_dtype(int d) { return d == WC_BF16 || d == WC_FP32; }
-
 // Checks a batch's host segment array against the planning rule.
-wc_status check_plan(int dtype, const wc_segment *segs, uint32_t nseg, wc_layout *total, bool need_ptrs = true)
+wc_status check_plan(uint32_t format, const wc_segment *segs, uint32_t nseg, wc_layout *total,
+                     bool need_ptrs = true)
 {
     uint64_t chunks = 0, raw = 0, cap = 0, elems = 0;
     for (uint32_t i = 0; i < nseg; i++) {
@@ -56,7 +69,7 @@ wc_status check_plan(int dtype, const wc_segment *segs, uint32_t nseg, wc_layout
         if (s.chunk_base != chunks || s.raw_base != raw) return WC_ERR_ARG;
         if (need_ptrs && s.n && (s.ptr == 0 || (s.ptr % 16) != 0)) return WC_ERR_ARG;
         wc_layout one;
-        layout_of(dtype, s.n, &one);
+        layout_of(format, s.n, &one);
         chunks += one.num_chunks;
         raw += one.raw_bytes;
         if (i + 1 < nseg) raw = align_up(raw, 256);
@@ -66,18 +79,19 @@ wc_status check_plan(int dtype, const wc_segment *segs, uint32_t nseg, wc_layout
     total->n = elems;
     total->num_chunks = chunks;
     total->raw_bytes = raw;
-    total->table_bytes = 512 * chunks;
+    const bool tt = opts_of(format).tensor_table();
+    total->table_bytes = tt ? 512ull * nseg : 512 * chunks;
     total->seek_bytes = 8 * (chunks + 1);
     total->payload_capacity = cap;
-    total->scratch_bytes = scratch_bytes_for(chunks);
+    total->scratch_bytes = scratch_bytes_for(chunks, tt ? nseg : 0);
     return WC_OK;
 }
 
-wc_status check_buffers(const wc_buffers *b, uint64_t chunks, uint64_t raw_bytes)
+wc_status check_buffers(const wc_buffers *b, uint64_t chunks, uint64_t raw_bytes, uint64_t table_bytes)
 {
     if (!b || !b->seek || !aligned(b->seek, 8)) return WC_ERR_ARG;
+    if (table_bytes && (!b->tables || !aligned(b->tables, 16))) return WC_ERR_ARG;
     if (chunks == 0) return WC_OK;
-    if (!b->tables || !aligned(b->tables, 16)) return WC_ERR_ARG;
     if (!b->payload || !aligned(b->payload, 16)) return WC_ERR_ARG;
     if (raw_bytes && (!b->raw || !aligned(b->raw, 16))) return WC_ERR_ARG;
     return WC_OK;
@@ -85,19 +99,33 @@ wc_status check_buffers(const wc_buffers *b, uint64_t chunks, uint64_t raw_bytes
 
 template <int DT>
 wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, const wc_buffers *out,
-                      void *d_scratch, uint32_t *d_err, hipStream_t stream, hipEvent_t *ev)
+                      void *d_scratch, uint32_t *d_err, hipStream_t stream, hipEvent_t *ev, Opts opts)
 {
     uint2 *meta = reinterpret_cast<uint2 *>(d_scratch);
     uint8_t *slots = reinterpret_cast<uint8_t *>(d_scratch) + align_up(8 * chunks, 256);
+    const uint32_t ntab = st.nseg ? st.nseg : 1;  // tensors (tensor-wide tables)
+    unsigned long long *hist =
+        chunks ? reinterpret_cast<unsigned long long *>(reinterpret_cast<uint8_t *>(d_scratch) + hist_offset(chunks))
+               : nullptr;
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return WC_ERR_HIP;
+    if (chunks && opts.tensor_table()) {
+        const uint64_t words = 256ull * ntab;
+        const uint64_t blocks = (words + 255) / 256;
+        hipLaunchKernelGGL(k_zero_u64, dim3((uint32_t)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, hist,
+                           words);
+    }
     if (chunks) {
         hipLaunchKernelGGL(k_split_hist<DT>, dim3((uint32_t)chunks), dim3(256), 0, stream, st, out->raw,
-                           out->tables, raw_total);
+                           out->tables, raw_total, opts, hist);
+    }
+    if (opts.tensor_table()) {
+        // every tensor's table, also those of tensors without elements
+        hipLaunchKernelGGL(k_tensor_table, dim3(ntab), dim3(256), 0, stream, st, hist, out->tables);
     }
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return WC_ERR_HIP;
     if (chunks) {
         hipLaunchKernelGGL(k_encode<DT>, dim3((uint32_t)((chunks + 1) / 2)), dim3(64), 0, stream, st,
-                           out->tables, slots, meta, chunks);
+                           out->tables, slots, meta, chunks, opts);
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return WC_ERR_HIP;
     {
@@ -133,17 +161,48 @@ bool use_wide_table(uint64_t chunks)
 
 template <int DT>
 wc_status decode_impl(const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err,
-                      hipStream_t stream)
+                      hipStream_t stream, Opts opts)
 {
     if (chunks == 0) return WC_OK;
     if (use_wide_table(chunks)) {
         hipLaunchKernelGGL((k_decode<DT, true, 1>), dim3((uint32_t)chunks), dim3(32), 0, stream, st, in->raw,
-                           in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err);
+                           in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts);
     } else {
         hipLaunchKernelGGL((k_decode<DT, false, 2>), dim3((uint32_t)((chunks + 1) / 2)), dim3(64), 0, stream, st,
-                           in->raw, in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err);
+                           in->raw, in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts);
+    }
+    if (opts.raw_fallback()) {
+        hipLaunchKernelGGL(k_decode_raw<DT>, dim3((uint32_t)chunks), dim3(256), 0, stream, st, in->raw, in->seek,
+                           in->payload, in->payload_bytes, d_err);
     }
     return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
+}
+
+// The kernels of a layout: BF16 and FP16 share the plain byte split.
+wc_status encode_any(uint32_t format, const SegTable &st, uint64_t chunks, uint64_t raw_total,
+                     const wc_buffers *out, void *d_scratch, uint32_t *d_err, hipStream_t stream, hipEvent_t *ev)
+{
+    const Opts o = opts_of(format);
+    switch (layout_code(format)) {
+    case WC_FP32: return encode_impl<WC_FP32>(st, chunks, raw_total, out, d_scratch, d_err, stream, ev, o);
+    case WC_BF16_REORDER:
+        return encode_impl<WC_BF16_REORDER>(st, chunks, raw_total, out, d_scratch, d_err, stream, ev, o);
+    case WC_FP16_REORDER:
+        return encode_impl<WC_FP16_REORDER>(st, chunks, raw_total, out, d_scratch, d_err, stream, ev, o);
+    default: return encode_impl<WC_BF16>(st, chunks, raw_total, out, d_scratch, d_err, stream, ev, o);
+    }
+}
+
+wc_status decode_any(uint32_t format, const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err,
+                     hipStream_t stream)
+{
+    const Opts o = opts_of(format);
+    switch (layout_code(format)) {
+    case WC_FP32: return decode_impl<WC_FP32>(st, chunks, in, d_err, stream, o);
+    case WC_BF16_REORDER: return decode_impl<WC_BF16_REORDER>(st, chunks, in, d_err, stream, o);
+    case WC_FP16_REORDER: return decode_impl<WC_FP16_REORDER>(st, chunks, in, d_err, stream, o);
+    default: return decode_impl<WC_BF16>(st, chunks, in, d_err, stream, o);
+    }
 }
 
 }  // namespace
@@ -164,92 +223,88 @@ const char *wc_status_string(wc_status s)
     return "unknown status";
 }
 
-wc_status wc_query_layout(wc_dtype dtype, uint64_t n, wc_layout *out)
+wc_status wc_query_layout(wc_format format, uint64_t n, wc_layout *out)
 {
-    if (!out || !valid_dtype(dtype) || n > kMaxElems) return WC_ERR_ARG;
-    layout_of(dtype, n, out);
-    out->scratch_bytes = scratch_bytes_for(out->num_chunks);
+    if (!out || !valid_format(format) || n > kMaxElems) return WC_ERR_ARG;
+    layout_of(format, n, out);
+    out->scratch_bytes = scratch_bytes_for(out->num_chunks, opts_of(format).tensor_table() ? 1 : 0);
     return WC_OK;
 }
 
-wc_status wc_plan_batch(wc_dtype dtype, wc_segment *segs, uint32_t nseg, wc_layout *total)
+wc_status wc_plan_batch(wc_format format, wc_segment *segs, uint32_t nseg, wc_layout *total)
 {
-    if (!valid_dtype(dtype) || (nseg && !segs) || !total) return WC_ERR_ARG;
+    if (!valid_format(format) || (nseg && !segs) || !total) return WC_ERR_ARG;
     uint64_t chunks = 0, raw = 0;
     for (uint32_t i = 0; i < nseg; i++) {
         if (segs[i].n > kMaxElems) return WC_ERR_ARG;
         segs[i].chunk_base = chunks;
         segs[i].raw_base = raw;
         chunks += (segs[i].n + kChunk - 1) / kChunk;
-        raw += raw_bytes_of(dtype, segs[i].n);
+        raw += raw_bytes_of(layout_code(format), segs[i].n);
         if (i + 1 < nseg) raw = align_up(raw, 256);
     }
-    return check_plan(dtype, segs, nseg, total, false);
+    return check_plan(format, segs, nseg, total, false);
 }
 
-wc_status wc_encode(wc_dtype dtype, const void *d_in, uint64_t n, const wc_buffers *out, void *d_scratch,
+wc_status wc_encode(wc_format format, const void *d_in, uint64_t n, const wc_buffers *out, void *d_scratch,
                     uint64_t scratch_bytes, uint32_t *d_err, hipStream_t stream, hipEvent_t *stage_events)
 {
-    if (!valid_dtype(dtype) || n > kMaxElems) return WC_ERR_ARG;
+    if (!valid_format(format) || n > kMaxElems) return WC_ERR_ARG;
     wc_layout lay;
-    wc_query_layout(dtype, n, &lay);
-    wc_status s = check_buffers(out, lay.num_chunks, lay.raw_bytes);
+    wc_query_layout(format, n, &lay);
+    wc_status s = check_buffers(out, lay.num_chunks, lay.raw_bytes, lay.table_bytes);
     if (s != WC_OK) return s;
     if (n && (!d_in || !aligned(d_in, 16))) return WC_ERR_ARG;
     if (lay.num_chunks && (!d_scratch || !aligned(d_scratch, 256))) return WC_ERR_ARG;
     if (scratch_bytes < lay.scratch_bytes) return WC_ERR_CAPACITY;
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{nullptr, 0, {reinterpret_cast<uint64_t>(d_in), n, 0, 0}};
-    return dtype == WC_BF16 ? encode_impl<WC_BF16>(st, lay.num_chunks, lay.raw_bytes, out, d_scratch, d_err, stream, stage_events)
-                            : encode_impl<WC_FP32>(st, lay.num_chunks, lay.raw_bytes, out, d_scratch, d_err, stream, stage_events);
+    return encode_any(format, st, lay.num_chunks, lay.raw_bytes, out, d_scratch, d_err, stream, stage_events);
 }
 
-wc_status wc_decode(wc_dtype dtype, const wc_buffers *in, uint64_t n, void *d_out, uint32_t *d_err,
+wc_status wc_decode(wc_format format, const wc_buffers *in, uint64_t n, void *d_out, uint32_t *d_err,
                     hipStream_t stream)
 {
-    if (!valid_dtype(dtype) || n > kMaxElems) return WC_ERR_ARG;
+    if (!valid_format(format) || n > kMaxElems) return WC_ERR_ARG;
     wc_layout lay;
-    wc_query_layout(dtype, n, &lay);
-    wc_status s = check_buffers(in, lay.num_chunks, lay.raw_bytes);
+    wc_query_layout(format, n, &lay);
+    wc_status s = check_buffers(in, lay.num_chunks, lay.raw_bytes, lay.num_chunks ? lay.table_bytes : 0);
     if (s != WC_OK) return s;
     if (n && (!d_out || !aligned(d_out, 16))) return WC_ERR_ARG;
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{nullptr, 0, {reinterpret_cast<uint64_t>(d_out), n, 0, 0}};
-    return dtype == WC_BF16 ? decode_impl<WC_BF16>(st, lay.num_chunks, in, d_err, stream)
-                            : decode_impl<WC_FP32>(st, lay.num_chunks, in, d_err, stream);
+    return decode_any(format, st, lay.num_chunks, in, d_err, stream);
 }
 
-wc_status wc_encode_batch(wc_dtype dtype, const wc_segment *h_segs, const wc_segment *d_segs, uint32_t nseg,
+wc_status wc_encode_batch(wc_format format, const wc_segment *h_segs, const wc_segment *d_segs, uint32_t nseg,
                           const wc_buffers *out, void *d_scratch, uint64_t scratch_bytes, uint32_t *d_err,
                           hipStream_t stream, hipEvent_t *stage_events)
 {
-    if (!valid_dtype(dtype) || nseg == 0 || !h_segs || !d_segs || !aligned(d_segs, 8)) return WC_ERR_ARG;
+    if (!valid_format(format) || nseg == 0 || !h_segs || !d_segs || !aligned(d_segs, 8)) return WC_ERR_ARG;
     wc_layout tot;
-    wc_status s = check_plan(dtype, h_segs, nseg, &tot);
+    wc_status s = check_plan(format, h_segs, nseg, &tot);
     if (s != WC_OK) return s;
-    s = check_buffers(out, tot.num_chunks, tot.raw_bytes);
+    s = check_buffers(out, tot.num_chunks, tot.raw_bytes, tot.table_bytes);
     if (s != WC_OK) return s;
     if (tot.num_chunks && (!d_scratch || !aligned(d_scratch, 256))) return WC_ERR_ARG;
     if (scratch_bytes < tot.scratch_bytes) return WC_ERR_CAPACITY;
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{d_segs, nseg, {0, 0, 0, 0}};
-    return dtype == WC_BF16 ? encode_impl<WC_BF16>(st, tot.num_chunks, tot.raw_bytes, out, d_scratch, d_err, stream, stage_events)
-                            : encode_impl<WC_FP32>(st, tot.num_chunks, tot.raw_bytes, out, d_scratch, d_err, stream, stage_events);
+    return encode_any(format, st, tot.num_chunks, tot.raw_bytes, out, d_scratch, d_err, stream, stage_events);
 }
 
-wc_status wc_decode_batch(wc_dtype dtype, const wc_segment *h_segs, const wc_segment *d_segs, uint32_t nseg,
+wc_status wc_decode_batch(wc_format format, const wc_segment *h_segs, const wc_segment *d_segs, uint32_t nseg,
                           const wc_buffers *in, uint32_t *d_err, hipStream_t stream)
 {
-    if (!valid_dtype(dtype) || nseg == 0 || !h_segs || !d_segs || !aligned(d_segs, 8)) return WC_ERR_ARG;
+    if (!valid_format(format) || nseg == 0 || !h_segs || !d_segs || !aligned(d_segs, 8)) return WC_ERR_ARG;
     wc_layout tot;
-    wc_status s = check_plan(dtype, h_segs, nseg, &tot);
+    wc_status s = check_plan(format, h_segs, nseg, &tot);
     if (s != WC_OK) return s;
-    s = check_buffers(in, tot.num_chunks, tot.raw_bytes);
+    s = check_buffers(in, tot.num_chunks, tot.raw_bytes, tot.num_chunks ? tot.table_bytes : 0);
     if (s != WC_OK) return s;
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{d_segs, nseg, {0, 0, 0, 0}};
-    return dtype == WC_BF16 ? decode_impl<WC_BF16>(st, tot.num_chunks, in, d_err, stream)
-                            : decode_impl<WC_FP32>(st, tot.num_chunks, in, d_err, stream);
+    return decode_any(format, st, tot.num_chunks, in, d_err, stream);
 }
 
 uint64_t wc_check_division(uint32_t samples_per_divisor)

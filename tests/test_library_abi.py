@@ -64,6 +64,39 @@ def test_plan_batch_matches_oracle(L, oracle_lib):
         assert tot.payload_capacity == otot.payload_capacity
 
 
+FORMATS = [(lay, opts) for lay in ("bf16", "bf16r", "fp16", "fp16r", "fp32") for opts in (0, 0x100, 0x200, 0x300)]
+
+
+@pytest.mark.parametrize("lay,opts", FORMATS)
+@pytest.mark.parametrize("n", [0, 5, 65536, 3 * 65536 + 5])
+def test_variant_layouts_match_oracle(L, oracle_lib, lay, opts, n):
+    a = wc.wc_query_layout(B.format_word(lay) | opts, n).as_dict()
+    b = oracle_lib.query_layout(lay, n, opts)
+    for k in ("n", "num_chunks", "raw_bytes", "table_bytes", "seek_bytes", "payload_capacity"):
+        assert a[k] == getattr(b, k), k
+    c = a["num_chunks"]
+    hist = 2048 if (opts & 0x100) and c else 0
+    assert a["scratch_bytes"] == (0 if c == 0 else ((8 * c + 255) // 256) * 256 + (c + 1) * 131200 + hist)
+
+
+@pytest.mark.parametrize("lay,opts", FORMATS)
+def test_variant_plan_batch_matches_oracle(L, oracle_lib, lay, opts):
+    ns = [65536 * 2 + 5, 1, 0, 70000, 300]
+    segs, tot = wc.wc_plan_batch(B.format_word(lay) | opts, ns)
+    cb, rb, otot = oracle_lib.plan_batch(lay, ns, opts)
+    assert [segs[i].chunk_base for i in range(len(ns))] == list(cb)
+    assert [segs[i].raw_base for i in range(len(ns))] == list(rb)
+    for k in ("num_chunks", "raw_bytes", "table_bytes", "payload_capacity"):
+        assert getattr(tot, k) == getattr(otot, k), k
+
+
+def test_bad_format_words_are_rejected(L):
+    for f in (5, 0xFF, 0x400, 0x10000, 0x80000000):
+        with pytest.raises(B.WcError):
+            wc.wc_query_layout(f, 100)
+        assert L.wc_query_layout(f, 100, ctypes.byref(B.wc_layout())) == B.WC_ERR_ARG
+
+
 def test_division_by_reciprocal(L):
     # every divisor 1..4096, boundary and sampled dividends below 2^32
     assert wc.wc_check_division(512) == 0
