@@ -37,6 +37,10 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--layout", default=None, choices=["bf16", "bf16r", "fp16", "fp16r", "fp32"],
+                   help="plane layout (default: the set's own type; fp16* store the set as IEEE half)")
+    p.add_argument("--tensor-table", action="store_true", help="one frequency table per tensor")
+    p.add_argument("--raw-fallback", action="store_true", help="store chunks that do not shrink raw")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU work for the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -89,7 +93,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(w, xs, target_s):
+def cpu_baseline(w, xs, target_s, layout, opts):
     """The oracle, as it stands, on a bounded sample of the same set: with
     one thread per host core available (at most 16), and with one thread on a
     smaller piece of the same sample."""
@@ -99,7 +103,7 @@ def cpu_baseline(w, xs, target_s):
     # calibrate on one tensor-sized piece
     probe = xs[0][: min(xs[0].size, 4 * 65536)]
     t = time.perf_counter()
-    e = oracle.encode(probe, w.dtype, threads=threads)
+    e = oracle.encode(probe, layout, threads=threads, opts=opts)
     oracle.decode(e, threads=threads)
     rate = probe.size / max(time.perf_counter() - t, 1e-6)  # elements / s, round trip
     want = max(int(rate * target_s), 1)
@@ -114,7 +118,7 @@ def cpu_baseline(w, xs, target_s):
     nbytes = 0
     for x in sample:
         t = time.perf_counter()
-        e = oracle.encode(x, w.dtype, threads=threads)
+        e = oracle.encode(x, layout, threads=threads, opts=opts)
         t_enc += time.perf_counter() - t
         t = time.perf_counter()
         y, _ = oracle.decode(e, threads=threads)
@@ -125,7 +129,7 @@ def cpu_baseline(w, xs, target_s):
     # one thread, on the first ~1/threads of the same sample (whole chunks)
     one = sample[0][: max(65536, (count // threads) // 65536 * 65536)]
     t = time.perf_counter()
-    e = oracle.encode(one, w.dtype, threads=1)
+    e = oracle.encode(one, layout, threads=1, opts=opts)
     t1_enc = time.perf_counter() - t
     t = time.perf_counter()
     y, _ = oracle.decode(e, threads=1)
@@ -149,27 +153,36 @@ def cpu_baseline(w, xs, target_s):
     }
 
 
-def coded_plane_entropy(w, xs, tables, seek, max_chunks=4096):
+def coded_symbols(layout, seg):
+    """The coded byte of each element under a plane layout (for reporting)."""
+    if layout == "fp32":
+        return ((seg.view(np.uint32) >> 23) & 0xFF).astype(np.uint8)
+    v = seg.view(np.uint16)
+    if layout == "bf16r":
+        return ((v >> 7) & 0xFF).astype(np.uint8)
+    if layout == "fp16r":
+        return (((v >> 7) & 0xF8) | ((v >> 13) & 0x04) | ((v >> 8) & 0x03)).astype(np.uint8)
+    return (v >> 8).astype(np.uint8)
+
+
+def coded_plane_entropy(xs, tables, seek, layout, tensor_table, max_chunks=4096):
     """Bits per coded symbol over a strided sample of chunks: the empirical
     entropy of each chunk's coded bytes, their cross-entropy under the chunk's
     12-bit table (the ideal rANS length for that table), and the payload the
     encoder actually produced (states, words and padding)."""
-    C = tables.shape[0]
+    C = seek.size - 1
     stride = max(1, -(-C // max_chunks))
     h_emp = h_q = 0.0
     syms = pay = 0
     k = 0
-    for x in xs:
+    for ti, x in enumerate(xs):
         for c0 in range(0, x.size, 65536):
             if k % stride == 0:
                 seg = x[c0:c0 + 65536]
-                if w.dtype == "bf16":
-                    sym = (seg.view(np.uint16) >> 8).astype(np.uint8)
-                else:
-                    sym = ((seg.view(np.uint32) >> 23) & 0xFF).astype(np.uint8)
+                sym = coded_symbols(layout, seg)
                 cnt = np.bincount(sym, minlength=256).astype(np.float64)
                 nz = cnt > 0
-                f = tables[k].astype(np.float64)
+                f = tables[ti if tensor_table else k].astype(np.float64)
                 h_emp += float(-(cnt[nz] * np.log2(cnt[nz] / seg.size)).sum())
                 h_q += float(-(cnt[nz] * np.log2(f[nz] / 4096.0)).sum())
                 syms += seg.size
@@ -195,25 +208,32 @@ def main():
     wc.lib()
     dev = torch.device("cuda:0")
     w = S.workload(args.workload)
+    layout = args.layout or w.dtype
+    if layout.startswith("fp16"):
+        w = S.with_dtype(w, "fp16")
+    elif (layout == "fp32") != (w.dtype == "fp32"):
+        raise SystemExit(f"layout {layout} does not fit the {w.dtype} set {w.name}")
+    opts = (B.WC_OPT_TENSOR_TABLE if args.tensor_table else 0) | (B.WC_OPT_RAW_FALLBACK if args.raw_fallback else 0)
+    fmt = B.format_word(layout) | opts
     log(f"[bench] generating {w.name}: {len(w.shapes)} tensors, {w.n} elements")
     t0 = time.perf_counter()
     xs = S.set_bits(w)
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading")
-    ity = torch.int16 if w.dtype == "bf16" else torch.int32
-    nty = np.int16 if w.dtype == "bf16" else np.int32
+    ity = torch.int32 if w.dtype == "fp32" else torch.int16
+    nty = np.int32 if w.dtype == "fp32" else np.int16
     ins = [torch.from_numpy(x.view(nty)).to(dev) for x in xs]
     outs = [torch.empty_like(t) for t in ins]
     ns = [t.numel() for t in ins]
 
-    h_in, tot = B.wc_plan_batch(w.dtype, ns)
-    h_out, _ = B.wc_plan_batch(w.dtype, ns)
+    h_in, tot = B.wc_plan_batch(fmt, ns)
+    h_out, _ = B.wc_plan_batch(fmt, ns)
     for i in range(len(ins)):
         h_in[i].ptr = ins[i].data_ptr()
         h_out[i].ptr = outs[i].data_ptr()
     d_in = codec.segments_to_device(h_in, len(ins), dev)
     d_out = codec.segments_to_device(h_out, len(ins), dev)
     raw = torch.empty(tot.raw_bytes, dtype=torch.uint8, device=dev)
-    tables = torch.empty(tot.num_chunks * 256, dtype=torch.int16, device=dev)
+    tables = torch.empty(max(tot.table_bytes // 2, 8), dtype=torch.int16, device=dev)
     seek = torch.empty(tot.num_chunks + 1, dtype=torch.int64, device=dev)
     payload = torch.empty(tot.payload_capacity, dtype=torch.uint8, device=dev)
     scratch = torch.empty(tot.scratch_bytes, dtype=torch.uint8, device=dev)
@@ -230,12 +250,12 @@ def main():
 
     def step(i=None):
         sev = evs[i] if i is not None else None
-        B.wc_encode_batch(w.dtype, h_in, d_in, len(ins), enc_bufs, scratch, scratch.numel(), err,
+        B.wc_encode_batch(fmt, h_in, d_in, len(ins), enc_bufs, scratch, scratch.numel(), err,
                           stream, sev)
         if sev is not None:
             sev.record(5, stream)
         dec_bufs = B.make_buffers(raw, tables, seek, payload, payload_bytes)
-        B.wc_decode_batch(w.dtype, h_out, d_out, len(outs), dec_bufs, err, stream)
+        B.wc_decode_batch(fmt, h_out, d_out, len(outs), dec_bufs, err, stream)
         if sev is not None:
             sev.record(6, stream)
 
@@ -255,7 +275,8 @@ def main():
                 raise RuntimeError("round trip is not bit-exact")
         checked = True
         log("[bench] round trip bit-exact")
-    compressed = int(raw.numel() + tables.numel() * 2 + seek.numel() * 8 + payload_bytes)
+    table_bytes = int(tot.table_bytes)
+    compressed = int(tot.raw_bytes + table_bytes + seek.numel() * 8 + payload_bytes)
     ratio = compressed / raw_in_bytes
 
     # timed region
@@ -278,13 +299,13 @@ def main():
     enc_ms = sum(stage_ms.values())
 
     # algorithmic bytes (the minimum the method moves), per launch
-    side = payload_bytes + 512 * C + 8 * (C + 1)
+    side = payload_bytes + table_bytes + 8 * (C + 1)
     raw_plane = int(tot.raw_bytes)
     alg = {
         "rans_decode": side + raw_plane + raw_in_bytes,           # read compressed + raw plane, write BF16
         "encode_total": raw_in_bytes + raw_plane + side,          # read BF16, write raw plane + compressed
-        "split_hist": raw_in_bytes + raw_plane + 512 * C,
-        "rans_encode": raw_in_bytes + 512 * C + payload_bytes,
+        "split_hist": raw_in_bytes + raw_plane + table_bytes,
+        "rans_encode": raw_in_bytes + table_bytes + payload_bytes,
         "compact": 2 * payload_bytes,
     }
     times = {"split_hist": stage_ms["split_hist"], "rans_encode": stage_ms["rans_encode"],
@@ -317,7 +338,9 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": w.name, "tensors": len(w.shapes), "elements": n,
-                   "raw_bytes": raw_in_bytes, "chunks": C, "weights": w.dtype},
+                   "raw_bytes": raw_in_bytes, "chunks": C, "weights": w.dtype,
+                   "layout": layout, "tensor_table": bool(args.tensor_table),
+                   "raw_fallback": bool(args.raw_fallback)},
         "ratio": round(ratio, 5),
         "round_trip_bit_exact": checked,
         "encode_GBps": round(raw_in_bytes / (enc_ms / 1e3) / 1e9, 3),
@@ -341,7 +364,7 @@ def main():
                 if mode == "cold":
                     flush.fill_(1)
                 ev[0].record(stream)
-                B.wc_decode_batch(w.dtype, h_out, d_out, len(outs), dec_bufs, err, stream)
+                B.wc_decode_batch(fmt, h_out, d_out, len(outs), dec_bufs, err, stream)
                 ev[1].record(stream)
                 torch.cuda.synchronize()
                 (warm if mode == "warm" else cold).append(ev[0].elapsed_time(ev[1]))
@@ -354,7 +377,8 @@ def main():
                 "ms_median": round(med, 5), "ms_min": round(min(ts), 5), "reps": len(ts),
                 "hbm_frac_median": round(alg["rans_decode"] / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
     result["entropy"] = coded_plane_entropy(
-        w, xs, tables.cpu().numpy().view(np.uint16).reshape(C, 256), seek.cpu().numpy().view(np.uint64))
+        xs, tables.cpu().numpy().view(np.uint16)[: table_bytes // 2].reshape(-1, 256),
+        seek.cpu().numpy().view(np.uint64), layout, args.tensor_table)
 
     # achievable bandwidth on this GPU: a plain device copy, 1 GiB each way
     # (larger than the 256 MB Infinity Cache), in the same run
@@ -381,7 +405,7 @@ def main():
         log(f"[bench] copy reference: {COPY_REF_BYTES} B read, {COPY_REF_BYTES} B written")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")
-        result["cpu_baseline"] = cpu_baseline(w, xs, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, xs, args.cpu_seconds, layout, opts)
     print(json.dumps(result), flush=True)
 
 

@@ -22,6 +22,8 @@ Recipe
 * BF16: round-to-nearest-even of the float32 bit pattern,
   ``(u + 0x7FFF + ((u >> 16) & 1)) >> 16`` (what ``torch.to(bfloat16)`` does
   for finite values).
+* FP16 (``with_dtype(w, "fp16")``): the same float32 values rounded to IEEE
+  half by numpy (round to nearest even).
 """
 from __future__ import annotations
 
@@ -49,7 +51,7 @@ class Dist:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str                  # "bf16" or "fp32"
+    dtype: str                  # "bf16", "fp16" or "fp32"
     shapes: tuple               # tuple of (rows, cols) in set order
     dist: Dist
     seed: int = 0
@@ -65,7 +67,7 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        return 4 if self.dtype == "fp32" else 2
 
     @property
     def raw_bytes(self) -> int:
@@ -119,6 +121,15 @@ def workload(name: str) -> Workload:
     return WORKLOADS[name]
 
 
+def with_dtype(w: Workload, dtype: str) -> Workload:
+    """The same set (shapes, distribution, seed) stored as another float type."""
+    if dtype == w.dtype:
+        return w
+    if w.dtype == "fp32" or dtype not in ("bf16", "fp16"):
+        raise ValueError(f"{w.name} cannot be stored as {dtype}")
+    return Workload(f"{w.name}-as-{dtype}", dtype, w.shapes, w.dist, w.seed, w.note)
+
+
 def _rng(seed: int, key: tuple) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=key)))
 
@@ -163,17 +174,19 @@ def block_f32(w: Workload, i: int, j: int) -> np.ndarray:
 
 
 def block_bits(w: Workload, i: int, j: int) -> np.ndarray:
-    """Bit patterns (uint16 for bf16, uint32 for fp32) of block j of tensor i."""
+    """Bit patterns (uint16 for bf16 / fp16, uint32 for fp32) of block j of tensor i."""
     v = block_f32(w, i, j)
     if w.dtype == "fp32":
         return v.view(np.uint32)
+    if w.dtype == "fp16":
+        return v.astype(np.float16).view(np.uint16)
     return f32_to_bf16_bits(v)
 
 
 def tensor_bits(w: Workload, i: int, threads: int | None = None, out: np.ndarray | None = None):
     """All bit patterns of tensor i (flat)."""
     n = w.numels[i]
-    dt = np.uint16 if w.dtype == "bf16" else np.uint32
+    dt = np.uint32 if w.dtype == "fp32" else np.uint16
     if out is None:
         out = np.empty(n, dt)
     nblk = (n + GEN_BLOCK - 1) // GEN_BLOCK
