@@ -43,30 +43,47 @@ namespace wc {
 
 constexpr uint32_t kGroup = 8;                       // steps per group
 constexpr uint32_t kGroupWords = kLanes * kGroup;    // most words one group consumes
-constexpr uint32_t kBlk = 2 * kLanes;                // words per refill block, one dword per lane
-constexpr uint32_t kRingWords = kGroupWords + kBlk;  // 320
 constexpr uint32_t kApron = 2 * kLanes;              // ring words 0..63 repeated after the end
-constexpr uint32_t kRingAlloc = kRingWords + kApron;
-// A block is issued only while fewer than kAhead words are issued and
-// unconsumed; it lands at least one group later, when the read position
-// has not moved back, so it never covers an unconsumed word.
-constexpr uint32_t kAhead = kRingWords - kBlk;
 constexpr uint32_t kStageBytes = kLanes * kGroup;    // decoded bytes per group per half
 
+// Ring geometry for refills of kB dwords per lane.  A refill moves a block
+// of 64 kB words, at most one per group, issued while fewer than kAhead
+// words are issued and unconsumed, and lands two groups later; so about
+// kAhead - 2 r words have landed ahead of a group that consumes r words per
+// group, and that must exceed r.  kB = 1 (320-word ring, kAhead 256) covers
+// weights (r about 45); kB = 2 (512-word ring, kAhead 384, 128-word blocks)
+// covers coded bytes of up to 8 bits, e.g. the FP16 high byte (r about 88),
+// which would otherwise outrun the refills and take the second pass.
+// A block never covers an unconsumed word: at issue fewer than kAhead words
+// are unconsumed, so with the block fewer than kWords.
+template <int kB>
+struct Ring {
+    static constexpr uint32_t kBlk = 2 * kLanes * kB;
+    static constexpr uint32_t kWords = kB == 1 ? kGroupWords + kBlk : 512;
+    static constexpr uint32_t kAlloc = kWords + kApron;
+    static constexpr uint32_t kAhead = kWords - kBlk;
+    static_assert(kWords % kBlk == 0, "blocks must not wrap the ring");
+    static_assert(kAhead >= kGroupWords, "a synchronous fill must land a whole group's worst case");
+};
+
 // H = chunks per wavefront (one per 32-lane half)
-template <int H>
+template <int H, int kB>
 struct DecSharedL1 {
+    static constexpr int kRefill = kB;
+    static constexpr uint32_t kRingWords = Ring<kB>::kWords;
     uint32_t tab[H][kM];                    // per slot: sym | (f-1) << 8 | (slot-b) << 20
     uint32_t fbtmp[H][256];                 // (b, f) while the table is built
-    uint32_t ring[H][kRingAlloc / 2];
+    uint32_t ring[H][Ring<kB>::kAlloc / 2];
     uint32_t stage[H][kStageBytes / 4];
 };
 
-template <int H>
+template <int H, int kB>
 struct DecSharedL2 {
+    static constexpr int kRefill = kB;
+    static constexpr uint32_t kRingWords = Ring<kB>::kWords;
     uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
     uint32_t fb[H][256];                    // b | (f - 4096) << 16
-    uint32_t ring[H][kRingAlloc / 2];
+    uint32_t ring[H][Ring<kB>::kAlloc / 2];
     uint32_t stage[H][kStageBytes / 4];
 };
 
@@ -84,61 +101,88 @@ struct Stream {
     }
 };
 
-// A refill moves the next 64-word block into the ring, one dword per lane.
-// Its load is issued unconditionally, so the compiler can count outstanding
-// memory operations exactly: when no refill is due it reads the chunk's
-// first state, and a lane whose dword lies past the stream end reads the
-// last one in bounds (a valid stream never consumes a word past its end).
+// A refill moves the next block into the ring, kB dwords per lane.  Its
+// loads are issued unconditionally, so the compiler can count outstanding
+// memory operations exactly: when no refill is due they read the chunk's
+// first states, and dwords past the stream end are replaced by ones in
+// bounds (a valid stream never consumes a word past its end).
 struct Refill {
-    uint32_t v;
-    uint32_t pos;  // ring dword the lane writes
+    uint32_t v, v1;  // the lane's dwords (v1 with kB = 2)
+    uint32_t pos;    // first ring dword the lane writes
     bool go;
+    bool first;      // kB = 2: v holds the lane's first dword (else v1 does)
 };
 
 __device__ __forceinline__ Refill refill_none()
 {
-    return Refill{0u, 0u, false};
+    return Refill{0u, 0u, 0u, false, true};
 }
 
+template <int kB>
 __device__ __forceinline__ Refill refill_issue(Stream &st, uint32_t lane, bool on)
 {
+    using R = Ring<kB>;
     Refill r;
-    r.go = on && st.fill - st.ptr < kAhead && st.fill < st.nw;
-    // with go, nw >= 2: the clamp stays inside the stream
-    const uint32_t d = min(st.fill / 2 + lane, st.nw / 2 - 1);
-    const uint32_t off = r.go ? 128 + 4 * d : 0u;
-    r.v = *reinterpret_cast<const WC_GLOBAL uint32_t *>(st.base + off);
-    r.pos = st.fpos / 2 + lane;
+    r.go = on && st.fill - st.ptr < R::kAhead && st.fill < st.nw;
+    if constexpr (kB == 1) {
+        // with go, nw >= 2: the clamp stays inside the stream
+        const uint32_t d = min(st.fill / 2 + lane, st.nw / 2 - 1);
+        const uint32_t off = r.go ? 128 + 4 * d : 0u;
+        r.v = *reinterpret_cast<const WC_GLOBAL uint32_t *>(st.base + off);
+        r.v1 = 0;
+        r.first = true;
+    } else {
+        // dwords d, d + 1 from d0 = min(d, nw/2 - 2): with go, nw >= 2, so
+        // d0 >= -1 and the pair starts at most one dword into the states
+        const int32_t d = (int32_t)(st.fill / 2 + 2 * lane);
+        const int32_t d0 = min(d, (int32_t)(st.nw / 2) - 2);
+        const uint32_t off = r.go ? (uint32_t)(128 + 4 * d0) : 0u;
+        const WC_GLOBAL uint32_t *p = reinterpret_cast<const WC_GLOBAL uint32_t *>(st.base + off);
+        r.v = p[0];
+        r.v1 = p[1];
+        r.first = d0 == d;
+    }
+    r.pos = st.fpos / 2 + kB * lane;
     if (r.go) {
-        st.fill += kBlk;
-        st.fpos = st.fpos + kBlk < kRingWords ? st.fpos + kBlk : 0u;
+        st.fill += R::kBlk;
+        st.fpos = st.fpos + R::kBlk < R::kWords ? st.fpos + R::kBlk : 0u;
     }
     return r;
 }
 
+template <int kB>
 __device__ __forceinline__ void refill_commit(Stream &st, Refill &r, uint32_t *ring)
 {
+    using R = Ring<kB>;
     if (r.go) {
-        ring[r.pos] = r.v;
-        // the cursor wraps every second step, so the 32 reads of a step
-        // start below kRingWords + 32 and never wrap
-        if (r.pos < kApron / 2) ring[kRingWords / 2 + r.pos] = r.v;
-        st.land += kBlk;
+        // the cursor wraps every second step, so the reads of a step start
+        // below R::kWords + 32 and never wrap
+        if constexpr (kB == 1) {
+            ring[r.pos] = r.v;
+            if (r.pos < kApron / 2) ring[R::kWords / 2 + r.pos] = r.v;
+        } else {
+            // d0 < d: dword d is the pair's second (or past the end), d + 1 is past the end
+            const uint2 w = make_uint2(r.first ? r.v : r.v1, r.v1);
+            *reinterpret_cast<uint2 *>(&ring[r.pos]) = w;
+            if (r.pos < kApron / 2) *reinterpret_cast<uint2 *>(&ring[R::kWords / 2 + r.pos]) = w;
+        }
+        st.land += R::kBlk;
         r.go = false;
     }
 }
 
 // Lands what the next group may need (256 words, or the rest of the
-// stream): up to four blocks, loaded together and then written.  Only
-// called with nothing in flight, so issued equals landed.
+// stream): up to 256 / block blocks, loaded together and then written.
+// Only called with nothing in flight, so issued equals landed.
+template <int kB>
 __device__ __forceinline__ void refill_sync(Stream &st, uint32_t lane, bool ok, uint32_t *ring)
 {
-    Refill r[kGroupWords / kBlk];
+    constexpr uint32_t n = kGroupWords / Ring<kB>::kBlk;
+    Refill r[n];
 #pragma unroll
-    for (uint32_t j = 0; j < kGroupWords / kBlk; j++)
-        r[j] = refill_issue(st, lane, ok && st.fill - st.ptr < kGroupWords);
+    for (uint32_t j = 0; j < n; j++) r[j] = refill_issue<kB>(st, lane, ok && st.fill - st.ptr < kGroupWords);
 #pragma unroll
-    for (uint32_t j = 0; j < kGroupWords / kBlk; j++) refill_commit(st, r[j], ring);
+    for (uint32_t j = 0; j < n; j++) refill_commit<kB>(st, r[j], ring);
 }
 
 // ----------------------------------------------------------- raw plane views
@@ -301,14 +345,14 @@ __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, ui
         half = (uint32_t)(m >> hs);
     }
     const uint16_t *ring = reinterpret_cast<const uint16_t *>(&sh.ring[h][0]);
-    const uint32_t w = ring[widx];  // widx < kRingWords + 64
+    const uint32_t w = ring[widx];  // widx < Sh::kRingWords + 64
     // x = need ? xd << 16 | w : xd, as one byte permute of (xd, w)
     const uint32_t sel = need ? 0x05040100u : 0x07060504u;
     const uint32_t xn = __builtin_amdgcn_perm(xd, w, sel);
     // the cursor is reduced modulo the ring size every second step (after
     // one unreduced step it is below kRingWords + 32)
     rpos += __popc(half);
-    if (i & 1) rpos = rpos < kRingWords ? rpos : rpos - kRingWords;
+    if (i & 1) rpos = rpos < Sh::kRingWords ? rpos : rpos - Sh::kRingWords;
     asm volatile("" : "+v"(rpos));
     if (!CHECK || active) x = xn;
 }
@@ -363,7 +407,7 @@ __device__ inline void build_table(Sh &sh, uint32_t h, uint32_t lane, const uint
 // a lone wavefront's serial chain has no per-half selects).  kH = 2: two
 // chunks per wavefront; with an odd chunk count the last wavefront's second
 // half shadows the first half's chunk (same unchecked code, nothing stored).
-template <int DT, bool kL1, int kH>
+template <int DT, bool kL1, int kH, int kB>
 __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *__restrict__ raw,
                                                     const uint16_t *__restrict__ tables,
                                                     const uint64_t *__restrict__ seek,
@@ -371,7 +415,8 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
                                                     uint64_t payload_bytes, uint64_t total_chunks,
                                                     uint32_t *err, Opts opts)
 {
-    using Sh = typename std::conditional<kL1, DecSharedL1<kH>, DecSharedL2<kH>>::type;
+    using Sh = typename std::conditional<kL1, DecSharedL1<kH, kB>, DecSharedL2<kH, kB>>::type;
+    constexpr uint32_t kRingWords = Sh::kRingWords;
     __shared__ Sh sh;
     const uint32_t lane = threadIdx.x & 31, h = kH == 1 ? 0u : threadIdx.x >> 5;
     const uint64_t k_own = (uint64_t)kH * blockIdx.x + h;
@@ -433,7 +478,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         build_table<kL1>(sh, h, lane, f, incl - local, fbtmp);
     }
     __syncthreads();
-    refill_sync(cs, lane, ok, sh.ring[h]);
+    refill_sync<kB>(cs, lane, ok, sh.ring[h]);
     __syncthreads();
 
     RawView<DT> rv;
@@ -467,8 +512,8 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     auto group = [&](auto check_tag, uint32_t gg, uint32_t g_last, const Pre &cur, Pre &ahead, Refill &due,
                      Refill &next, bool refills = true) {
         constexpr bool CHECK = decltype(check_tag)::value;
-        refill_commit(cs, due, sh.ring[h]);
-        next = refill_issue(cs, lane, ok && refills);
+        refill_commit<kB>(cs, due, sh.ring[h]);
+        next = refill_issue<kB>(cs, lane, ok && refills);
         // the value loaded for a group past the last is never used
         const uint32_t gn = gg + 2 <= g_last ? gg + 2 : g_last;
         if constexpr (CHECK) ahead = put ? rv.fetch_checked(kGroupWords * gn + 8 * lane, len) : Pre{};
@@ -510,7 +555,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     };
     auto fast = [&](auto prev_tag, uint32_t gg, uint32_t g_last, Pre &pv, Refill &due, Refill &next, Pend &pd) {
         constexpr bool PREV = decltype(prev_tag)::value;
-        refill_commit(cs, due, sh.ring[h]);
+        refill_commit<kB>(cs, due, sh.ring[h]);
         const Pend mine{cs.land, rpos};
         uint2 sprev = make_uint2(0u, 0u);
         wave_lds_order();
@@ -525,7 +570,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
                     rv.flush(kGroupWords * (gg - 1) + 8 * lane, sprev, pv);
                     settle(pd, mine.r0);
                 }
-                next = refill_issue(cs, lane, ok);
+                next = refill_issue<kB>(cs, lane, ok);
                 // the value loaded for a group past the last is never used
                 pv = rv.fetch(kGroupWords * (gg + 2 <= g_last ? gg + 2 : g_last) + 8 * lane);
             }
@@ -568,8 +613,8 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     // What is left (at most two full groups and a partial one) runs checked,
     // with refills committed one group after they are issued: first the ones
     // still in flight land, oldest first.
-    refill_commit(cs, q1, sh.ring[h]);
-    refill_commit(cs, q2, sh.ring[h]);
+    refill_commit<kB>(cs, q1, sh.ring[h]);
+    refill_commit<kB>(cs, q2, sh.ring[h]);
     for (uint32_t g = n3; g < ng; g++) {
         Pre cur = put ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
         Pre dummy;
@@ -579,12 +624,12 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     // every group checked and preceded by a synchronous fill, and its
     // output written again.
     if (__ballot(overrun)) {
-        refill_commit(cs, q0, sh.ring[h]);
+        refill_commit<kB>(cs, q0, sh.ring[h]);
         cs.ptr = cs.fill = cs.land = cs.fpos = 0;
         rpos = 0;
         if (ok) x = reinterpret_cast<const WC_GLOBAL uint32_t *>(cs.base)[lane];
         for (uint32_t g = 0; g < ng; g++) {
-            refill_sync(cs, lane, ok, sh.ring[h]);
+            refill_sync<kB>(cs, lane, ok, sh.ring[h]);
             Pre cur = put ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
             Pre dummy;
             Refill none = refill_none();

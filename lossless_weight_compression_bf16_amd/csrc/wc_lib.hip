@@ -159,18 +159,37 @@ bool use_wide_table(uint64_t chunks)
     return chunks <= 8ull * (uint64_t)cus;
 }
 
+// Refill block (dwords per lane): the stream's words per 8-step group are
+// about (bits per coded symbol) * 16; one-dword blocks supply 64 per group.
+// Above 3.25 bits per symbol on average (52 words per group) the two-dword
+// blocks keep speculative groups from outrunning the refills.
+bool use_wide_refills(uint64_t payload_bytes, uint64_t n)
+{
+    return n && payload_bytes * 8 > n * 13 / 4;
+}
+
+template <int DT, int kB>
+void launch_decode(const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err,
+                   hipStream_t stream, Opts opts)
+{
+    if (use_wide_table(chunks)) {
+        hipLaunchKernelGGL((k_decode<DT, true, 1, kB>), dim3((uint32_t)chunks), dim3(32), 0, stream, st, in->raw,
+                           in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts);
+    } else {
+        hipLaunchKernelGGL((k_decode<DT, false, 2, kB>), dim3((uint32_t)((chunks + 1) / 2)), dim3(64), 0, stream,
+                           st, in->raw, in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts);
+    }
+}
+
 template <int DT>
-wc_status decode_impl(const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err,
+wc_status decode_impl(const SegTable &st, uint64_t chunks, uint64_t n, const wc_buffers *in, uint32_t *d_err,
                       hipStream_t stream, Opts opts)
 {
     if (chunks == 0) return WC_OK;
-    if (use_wide_table(chunks)) {
-        hipLaunchKernelGGL((k_decode<DT, true, 1>), dim3((uint32_t)chunks), dim3(32), 0, stream, st, in->raw,
-                           in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts);
-    } else {
-        hipLaunchKernelGGL((k_decode<DT, false, 2>), dim3((uint32_t)((chunks + 1) / 2)), dim3(64), 0, stream, st,
-                           in->raw, in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts);
-    }
+    if (use_wide_refills(in->payload_bytes, n))
+        launch_decode<DT, 2>(st, chunks, in, d_err, stream, opts);
+    else
+        launch_decode<DT, 1>(st, chunks, in, d_err, stream, opts);
     if (opts.raw_fallback()) {
         hipLaunchKernelGGL(k_decode_raw<DT>, dim3((uint32_t)chunks), dim3(256), 0, stream, st, in->raw, in->seek,
                            in->payload, in->payload_bytes, d_err);
@@ -193,15 +212,15 @@ wc_status encode_any(uint32_t format, const SegTable &st, uint64_t chunks, uint6
     }
 }
 
-wc_status decode_any(uint32_t format, const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err,
-                     hipStream_t stream)
+wc_status decode_any(uint32_t format, const SegTable &st, uint64_t chunks, uint64_t n, const wc_buffers *in,
+                     uint32_t *d_err, hipStream_t stream)
 {
     const Opts o = opts_of(format);
     switch (layout_code(format)) {
-    case WC_FP32: return decode_impl<WC_FP32>(st, chunks, in, d_err, stream, o);
-    case WC_BF16_REORDER: return decode_impl<WC_BF16_REORDER>(st, chunks, in, d_err, stream, o);
-    case WC_FP16_REORDER: return decode_impl<WC_FP16_REORDER>(st, chunks, in, d_err, stream, o);
-    default: return decode_impl<WC_BF16>(st, chunks, in, d_err, stream, o);
+    case WC_FP32: return decode_impl<WC_FP32>(st, chunks, n, in, d_err, stream, o);
+    case WC_BF16_REORDER: return decode_impl<WC_BF16_REORDER>(st, chunks, n, in, d_err, stream, o);
+    case WC_FP16_REORDER: return decode_impl<WC_FP16_REORDER>(st, chunks, n, in, d_err, stream, o);
+    default: return decode_impl<WC_BF16>(st, chunks, n, in, d_err, stream, o);
     }
 }
 
@@ -273,7 +292,7 @@ wc_status wc_decode(wc_format format, const wc_buffers *in, uint64_t n, void *d_
     if (n && (!d_out || !aligned(d_out, 16))) return WC_ERR_ARG;
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{nullptr, 0, {reinterpret_cast<uint64_t>(d_out), n, 0, 0}};
-    return decode_any(format, st, lay.num_chunks, in, d_err, stream);
+    return decode_any(format, st, lay.num_chunks, n, in, d_err, stream);
 }
 
 wc_status wc_encode_batch(wc_format format, const wc_segment *h_segs, const wc_segment *d_segs, uint32_t nseg,
@@ -304,7 +323,7 @@ wc_status wc_decode_batch(wc_format format, const wc_segment *h_segs, const wc_s
     if (s != WC_OK) return s;
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{d_segs, nseg, {0, 0, 0, 0}};
-    return decode_any(format, st, tot.num_chunks, in, d_err, stream);
+    return decode_any(format, st, tot.num_chunks, tot.n, in, d_err, stream);
 }
 
 uint64_t wc_check_division(uint32_t samples_per_divisor)

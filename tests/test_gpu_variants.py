@@ -218,3 +218,20 @@ def test_empty_tensor_with_tensor_table(dev):
     e = codec.encode(torch.empty(0, dtype=torch.bfloat16, device=dev), tensor_table=True)
     assert tuple(e.tables.shape) == (1, 256) and not e.tables.cpu().numpy().any()
 
+
+
+def test_wide_refills_with_uniform_chunks(dev, oracle_lib):
+    """FP16 weights (about 5.5 bits per coded byte) select the two-dword
+    refills; every fifth chunk has uniform coded bytes (8 bits: 128 words per
+    group, the refills' full rate), so some groups outrun the landed words
+    and their chunk is decoded a second time; 2,401 chunks put them in
+    two-chunk wavefronts next to ordinary ones, and short chunks at the end
+    clamp the paired loads at the stream end."""
+    g = np.random.default_rng(31)
+    n_chunks = 2401
+    x = _weights16("fp16", n_chunks * 65536, 32)
+    for k in range(0, n_chunks, 5):
+        hi = g.permutation(np.repeat(np.arange(256, dtype=np.uint16), 256))
+        x[k * 65536:(k + 1) * 65536] = (hi << 8) | g.integers(0, 256, 65536).astype(np.uint16)
+    x = np.concatenate([x, _weights16("fp16", 77, 33)])
+    _one("fp16", 0, x, dev, oracle_lib, "fp16 2402 chunks, uniform every fifth")
