@@ -22,8 +22,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "wc_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libwc_oracle.so")
 
-BF16, FP32, BF16_REORDER, FP16, FP16_REORDER = 0, 1, 2, 3, 4
-DTYPES = {"bf16": BF16, "fp32": FP32, "bf16r": BF16_REORDER, "fp16": FP16, "fp16r": FP16_REORDER}
+BF16, FP32, BF16_REORDER, FP16, FP16_REORDER, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4, 5, 6
+DTYPES = {"bf16": BF16, "fp32": FP32, "bf16r": BF16_REORDER, "fp16": FP16, "fp16r": FP16_REORDER,
+          "fp8e4m3": FP8_E4M3, "fp8e5m2": FP8_E5M2}
 # option bits of a format word
 OPT_TENSOR_TABLE = 0x100  # one table per tensor
 OPT_RAW_FALLBACK = 0x200  # chunks that do not shrink are stored raw
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.wco_normalize.argtypes = [P, U32, P]
         L.wco_normalize64.argtypes = [P, U64, P]
         L.wco_split_u16.argtypes = [I, P, U64, P, P]
+        L.wco_split_fp8.argtypes = [I, P, U64, P, P]
+        L.wco_merge_fp8.argtypes = [I, P, P, U64, P]
         L.wco_merge_u16.argtypes = [I, P, P, U64, P]
         L.wco_encode_chunk.argtypes = [P, U32, P, P]
         L.wco_encode_chunk.restype = U32
@@ -98,7 +101,11 @@ def options(tensor_table: bool = False, raw_fallback: bool = False) -> int:
 
 
 def elem_type(dtype):
-    return np.uint32 if dtype in ("fp32", FP32) else np.uint16
+    if dtype in ("fp32", FP32):
+        return np.uint32
+    if dtype in ("fp8e4m3", "fp8e5m2", FP8_E4M3, FP8_E5M2):
+        return np.uint8
+    return np.uint16
 
 
 @dataclass
@@ -152,6 +159,23 @@ def merge_u16(layout, hi: np.ndarray, lo: np.ndarray) -> np.ndarray:
     lo = np.ascontiguousarray(lo, np.uint8)
     v = np.empty(hi.size, np.uint16)
     lib().wco_merge_u16(_dt(layout), _p(hi), _p(lo), hi.size, _p(v))
+    return v
+
+
+def split_fp8(layout, v: np.ndarray):
+    """FP8 layouts ("fp8e4m3", "fp8e5m2"): (coded nibbles, packed raw nibbles)."""
+    v = np.ascontiguousarray(v, dtype=np.uint8).ravel()
+    coded = np.empty(v.size, np.uint8)
+    raw = np.empty((v.size + 1) // 2, np.uint8)
+    lib().wco_split_fp8(_dt(layout), _p(v), v.size, _p(coded), _p(raw))
+    return coded, raw
+
+
+def merge_fp8(layout, coded: np.ndarray, raw: np.ndarray) -> np.ndarray:
+    coded = np.ascontiguousarray(coded, np.uint8)
+    raw = np.ascontiguousarray(raw, np.uint8)
+    v = np.empty(coded.size, np.uint8)
+    lib().wco_merge_fp8(_dt(layout), _p(coded), _p(raw), coded.size, _p(v))
     return v
 
 

@@ -48,6 +48,12 @@
  *     low byte raw.  FP16_REORDER applies the same page's bit reorder first:
  *     the coded byte holds the 5 exponent bits, then the sign, then the top
  *     2 mantissa bits; the raw byte the other 8 mantissa bits.
+ *   - FP8_E4M3, FP8_E5M2 (the same page: for 8-bit floats the reorder moves
+ *     the exponent into the high nibble; then a 2-plane nibble split): the
+ *     byte s e4 m3 becomes e4 s m3, the byte s e5 m2 becomes e5 s m2; the
+ *     high nibble is coded (symbols 0..15, through the same tables and
+ *     coder), the low nibble stored raw, two per byte, element 2j in the low
+ *     nibble of byte j (a last odd element leaves the high nibble zero).
  *   - TENSOR_TABLE (reading: the per-tensor codec records of the "PTWM"
  *     README's container, one table for a tensor's chunks): a single table,
  *     normalised from the histogram of the tensor's whole coded plane, codes
@@ -77,15 +83,18 @@
 static int layout_of(int format)
 {
     int layout = format & WCO_LAYOUT_MASK;
-    if (layout > WCO_FP16_REORDER) return -1;
+    if (layout > WCO_FP8_E5M2) return -1;
     if (format & ~(WCO_LAYOUT_MASK | WCO_OPT_TENSOR_TABLE | WCO_OPT_RAW_FALLBACK)) return -1;
     return layout;
 }
 
+static int is_fp8(int layout) { return layout == WCO_FP8_E4M3 || layout == WCO_FP8_E5M2; }
+
 static uint64_t raw_bytes_of(int layout, uint64_t n)
 {
-    if (layout != WCO_FP32) return n;
-    return (n + 7) / 8 + 3 * n;
+    if (layout == WCO_FP32) return (n + 7) / 8 + 3 * n;
+    if (is_fp8(layout)) return (n + 1) / 2;
+    return n;
 }
 
 /* Payload size of a chunk of len symbols stored raw. */
@@ -171,6 +180,42 @@ void wco_merge_u16(int layout, const uint8_t *hi, const uint8_t *lo, uint64_t n,
             x = r;
         }
         v[i] = (uint16_t)x;
+    }
+}
+
+/* FP8, one element at a time: take the byte apart into sign, exponent and
+ * mantissa, put the exponent first and the sign right after it, and cut the
+ * byte into its coded high nibble and its raw low nibble. */
+void wco_split_fp8(int layout, const uint8_t *v, uint64_t n, uint8_t *coded, uint8_t *raw)
+{
+    memset(raw, 0, (n + 1) / 2);
+    for (uint64_t i = 0; i < n; i++) {
+        uint32_t b = v[i], r;
+        uint32_t sign = b >> 7;
+        if (layout == WCO_FP8_E4M3) {
+            uint32_t e = (b >> 3) & 0xF, m = b & 0x7; /* 4 exponent, 3 mantissa bits */
+            r = (e << 4) | (sign << 3) | m;
+        } else {
+            uint32_t e = (b >> 2) & 0x1F, m = b & 0x3; /* 5 exponent, 2 mantissa bits */
+            r = (e << 3) | (sign << 2) | m;
+        }
+        coded[i] = (uint8_t)(r >> 4);
+        raw[i / 2] |= (uint8_t)((r & 0xF) << (4 * (i % 2)));
+    }
+}
+
+void wco_merge_fp8(int layout, const uint8_t *coded, const uint8_t *raw, uint64_t n, uint8_t *v)
+{
+    for (uint64_t i = 0; i < n; i++) {
+        uint32_t r = ((uint32_t)coded[i] << 4) | ((raw[i / 2] >> (4 * (i % 2))) & 0xF), x;
+        if (layout == WCO_FP8_E4M3) {
+            uint32_t e = r >> 4, sign = (r >> 3) & 1, m = r & 0x7;
+            x = (sign << 7) | (e << 3) | m;
+        } else {
+            uint32_t e = r >> 3, sign = (r >> 2) & 1, m = r & 0x3;
+            x = (sign << 7) | (e << 2) | m;
+        }
+        v[i] = (uint8_t)x;
     }
 }
 
@@ -488,6 +533,8 @@ int wco_encode(int dtype, const void *in, uint64_t n, uint8_t *raw, uint16_t *ta
     uint8_t *coded = (uint8_t *)malloc(n);
     if (layout == WCO_FP32)
         wco_split_fp32((const uint32_t *)in, n, coded, raw);
+    else if (is_fp8(layout))
+        wco_split_fp8(layout, (const uint8_t *)in, n, coded, raw);
     else
         wco_split_u16(layout, (const uint16_t *)in, n, coded, raw);
     if (dtype & WCO_OPT_TENSOR_TABLE) {
@@ -604,6 +651,8 @@ int wco_decode(int dtype, const uint8_t *raw, const uint16_t *tables, const uint
 
     if (layout == WCO_FP32)
         wco_merge_fp32(coded, raw, n, (uint32_t *)out);
+    else if (is_fp8(layout))
+        wco_merge_fp8(layout, coded, raw, n, (uint8_t *)out);
     else
         wco_merge_u16(layout, coded, raw, n, (uint16_t *)out);
     free(jobs);

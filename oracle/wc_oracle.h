@@ -37,6 +37,12 @@ extern "C" {
 #define WCO_BF16_REORDER 2 /* "PTWM" README, "How it works" 1: exponent byte coded, sign + 7 mantissa bits raw */
 #define WCO_FP16 3         /* 2-plane byte split of the IEEE half: hi = sign, exponent, 2 mantissa bits */
 #define WCO_FP16_REORDER 4 /* same page: hi = 5 exponent bits, sign, 2 mantissa bits; lo = 8 mantissa bits */
+/* FP8 ("PTWM" README: bit reorder puts the exponent in the high nibble, then a
+ * 2-plane nibble split): the high nibble of the reordered byte is coded (16
+ * symbols), the low nibble stored raw, two per byte (element 2j in the low
+ * nibble of byte j). */
+#define WCO_FP8_E4M3 5     /* s e4 m3 -> e4 | s m3 */
+#define WCO_FP8_E5M2 6     /* s e5 m2 -> e5[4:1] | e5[0] s m2 */
 #define WCO_LAYOUT_MASK 0xFF
 /* Options: */
 #define WCO_OPT_TENSOR_TABLE 0x100 /* one frequency table per tensor (its whole coded plane), not per chunk */
@@ -75,6 +81,9 @@ void wco_split_u16(int layout, const uint16_t *v, uint64_t n, uint8_t *hi, uint8
 void wco_merge_u16(int layout, const uint8_t *hi, const uint8_t *lo, uint64_t n, uint16_t *v);
 /* FP32: exp coded; raw = sign bits (LSB-first, ceil(n/8) B) | m0 | m1 | m2. */
 void wco_split_fp32(const uint32_t *u, uint64_t n, uint8_t *exp, uint8_t *raw);
+/* FP8 layouts: coded nibbles (one per byte, 0..15) and ceil(n/2) raw bytes. */
+void wco_split_fp8(int layout, const uint8_t *v, uint64_t n, uint8_t *coded, uint8_t *raw);
+void wco_merge_fp8(int layout, const uint8_t *coded, const uint8_t *raw, uint64_t n, uint8_t *v);
 void wco_merge_fp32(const uint8_t *exp, const uint8_t *raw, uint64_t n, uint32_t *u);
 
 /* One chunk. */
