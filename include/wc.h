@@ -31,6 +31,12 @@
  *     bits) is coded, its low byte raw.  WC_FP16_REORDER applies the bit
  *     reorder first: the coded byte is the 5 exponent bits, the sign and 2
  *     mantissa bits; the raw byte the other 8 mantissa bits.
+ *   - WC_FP8_E4M3, WC_FP8_E5M2 ("PTWM" README: for 8-bit floats the bit
+ *     reorder moves the exponent into the high nibble, then a 2-plane nibble
+ *     split): byte s e4 m3 -> e4 s m3, byte s e5 m2 -> e5 s m2; the high
+ *     nibble is coded (16 symbols, same tables and coder), the low nibbles
+ *     are raw, two per byte (element 2j in the low nibble of byte j), so the
+ *     raw plane is ceil(n/2) bytes.
  *   - WC_OPT_TENSOR_TABLE: one frequency table per tensor, normalised from
  *     the histogram of its whole coded plane, codes all of its chunks
  *     (tables = 256 u16 per tensor; a tensor without elements gets an
@@ -81,7 +87,9 @@ typedef enum {
     WC_FP32 = 1,
     WC_BF16_REORDER = 2,
     WC_FP16 = 3,
-    WC_FP16_REORDER = 4
+    WC_FP16_REORDER = 4,
+    WC_FP8_E4M3 = 5,
+    WC_FP8_E5M2 = 6
 } wc_dtype;
 /* Option bits of a format word. */
 #define WC_LAYOUT_MASK 0xFFu
@@ -158,7 +166,7 @@ wc_status wc_query_layout(wc_format format, uint64_t n, wc_layout *out);
 wc_status wc_plan_batch(wc_format format, wc_segment *segs, uint32_t nseg, wc_layout *total);
 
 /* Encode one tensor of n elements at d_in (FP32 as u32 patterns, the 16-bit
- * layouts as u16 patterns).  Writes out->raw (layout.raw_bytes), out->tables,
+ * layouts as u16 patterns, FP8 as bytes).  Writes out->raw (layout.raw_bytes), out->tables,
  * out->seek and out->payload (at most out->payload_bytes; layout's
  * payload_capacity always suffices).  d_scratch must hold
  * layout.scratch_bytes.  stage_events may be NULL or point to 5 events that
@@ -168,7 +176,7 @@ wc_status wc_encode(wc_format format, const void *d_in, uint64_t n, const wc_buf
                     void *d_scratch, uint64_t scratch_bytes, uint32_t *d_err,
                     hipStream_t stream, hipEvent_t *stage_events);
 
-/* Decode one tensor of n elements into d_out (u16 / u32 bit patterns).
+/* Decode one tensor of n elements into d_out (u32 / u16 / u8 bit patterns).
  * With WC_OPT_RAW_FALLBACK a chunk stored raw is copied; its padding must be
  * zero (else WC_EF_BAD_TAIL). */
 wc_status wc_decode(wc_format format, const wc_buffers *in, uint64_t n, void *d_out,

@@ -14,9 +14,9 @@ from dataclasses import dataclass
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libwc.so")
 
-WC_BF16, WC_FP32, WC_BF16_REORDER, WC_FP16, WC_FP16_REORDER = 0, 1, 2, 3, 4
+WC_BF16, WC_FP32, WC_BF16_REORDER, WC_FP16, WC_FP16_REORDER, WC_FP8_E4M3, WC_FP8_E5M2 = 0, 1, 2, 3, 4, 5, 6
 DTYPE_CODES = {"bf16": WC_BF16, "fp32": WC_FP32, "bf16r": WC_BF16_REORDER, "fp16": WC_FP16,
-               "fp16r": WC_FP16_REORDER}
+               "fp16r": WC_FP16_REORDER, "fp8e4m3": WC_FP8_E4M3, "fp8e5m2": WC_FP8_E5M2}
 WC_OPT_TENSOR_TABLE = 0x100
 WC_OPT_RAW_FALLBACK = 0x200
 
@@ -127,7 +127,8 @@ def format_word(dtype, tensor_table: bool = False, raw_fallback: bool = False) -
 
 
 def elem_bytes(fmt) -> int:
-    return 4 if (_code(fmt) & 0xFF) == WC_FP32 else 2
+    layout = _code(fmt) & 0xFF
+    return 4 if layout == WC_FP32 else 1 if layout in (WC_FP8_E4M3, WC_FP8_E5M2) else 2
 
 
 def error_names(bits: int):

@@ -1,12 +1,13 @@
 """Tensor-level API over the C ABI: lossless encode / decode of BF16, FP16 and
-FP32 weights on the GPU.
+FP32 weights (and FP8) on the GPU.
 
 BF16 is split into its high byte (sign + 7 exponent bits), which is rANS
 coded per 65536-element chunk, and its low byte, which is stored raw (the
 weight-compression / Split12 README's byte split); FP32 keeps sign bits and
 three mantissa bytes raw and codes the exponent byte (the SMEF README's
 sign / exponent / mantissa streams); FP16 takes the same 2-plane byte split
-as BF16.  Options: ``reorder`` applies the PTWM README's bit reorder first
+as BF16; FP8 (E4M3, E5M2) is split into the exponent nibble, which is coded,
+and the other nibble, stored raw two per byte.  Options: ``reorder`` applies the PTWM README's bit reorder first
 (16-bit layouts: the coded byte starts with the whole exponent), and
 ``tensor_table`` / ``raw_fallback`` select one table per tensor and raw
 storage of chunks that do not shrink.  Tensors are handled as bit patterns
@@ -28,12 +29,16 @@ def _dtype_of(t: torch.Tensor, reorder: bool = False) -> str:
         return "fp16r" if reorder else "fp16"
     if t.dtype in (torch.float32, torch.int32, torch.uint32):
         return "fp32"
-    raise TypeError(f"unsupported dtype {t.dtype}: expected bfloat16, float16 or float32")
+    if t.dtype == torch.float8_e4m3fn:
+        return "fp8e4m3"
+    if t.dtype == torch.float8_e5m2:
+        return "fp8e5m2"
+    raise TypeError(f"unsupported dtype {t.dtype}: expected bfloat16, float16, float32 or float8")
 
 
 def _bits(t: torch.Tensor, dtype) -> torch.Tensor:
     t = t.contiguous().reshape(-1)
-    t = t.view(torch.int32) if B.elem_bytes(dtype) == 4 else t.view(torch.int16)
+    t = t.view({4: torch.int32, 2: torch.int16, 1: torch.uint8}[B.elem_bytes(dtype)])
     if t.numel() and t.data_ptr() % 16:
         t = t.clone()
     return t
@@ -86,12 +91,24 @@ def _raise_bits(bits: int, what: str):
         raise B.WcError(f"{what}: device reported {', '.join(B.error_names(bits))} (bits {bits:#x})")
 
 
+def _layout_for(t: torch.Tensor, layout, reorder: bool) -> str:
+    """The plane layout: named explicitly (for tensors of raw bit patterns,
+    e.g. uint8 holding FP8), or from the tensor's float type."""
+    if layout is None:
+        return _dtype_of(t, reorder)
+    if layout not in B.DTYPE_CODES:
+        raise ValueError(f"unknown layout {layout!r}")
+    if t.element_size() != B.elem_bytes(layout):
+        raise TypeError(f"layout {layout} takes {B.elem_bytes(layout)}-byte elements, not {t.dtype}")
+    return layout
+
+
 def encode(t: torch.Tensor, stream=None, reorder: bool = False, tensor_table: bool = False,
-           raw_fallback: bool = False) -> Encoded:
-    """Losslessly encode a bf16 / fp16 / fp32 device tensor (synchronises once
-    to size the payload)."""
+           raw_fallback: bool = False, layout: str | None = None) -> Encoded:
+    """Losslessly encode a bf16 / fp16 / fp32 / fp8 device tensor (synchronises
+    once to size the payload)."""
     _check_device(t)
-    dtype = _dtype_of(t, reorder)
+    dtype = _layout_for(t, layout, reorder)
     fmt = B.format_word(dtype, tensor_table, raw_fallback)
     x = _bits(t, dtype)
     n = x.numel()
@@ -175,14 +192,14 @@ def segments_to_device(h_segs, nseg: int, dev) -> torch.Tensor:
 
 
 def encode_batch(ts, stream=None, reorder: bool = False, tensor_table: bool = False,
-                 raw_fallback: bool = False) -> EncodedBatch:
+                 raw_fallback: bool = False, layout: str | None = None) -> EncodedBatch:
     """Encode a list of same-dtype device tensors in one launch sequence."""
     if not ts:
         raise ValueError("empty batch")
     for t in ts:
         _check_device(t)
-    dtype = _dtype_of(ts[0], reorder)
-    if any(_dtype_of(t, reorder) != dtype for t in ts):
+    dtype = _layout_for(ts[0], layout, reorder)
+    if any(_layout_for(t, layout, reorder) != dtype for t in ts):
         raise TypeError("all tensors of a batch must share a dtype")
     fmt = B.format_word(dtype, tensor_table, raw_fallback)
     xs = [_bits(t, dtype) for t in ts]

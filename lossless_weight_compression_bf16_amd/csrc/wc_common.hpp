@@ -25,11 +25,16 @@ constexpr uint64_t kMaxElems = 1ull << 40;
 
 inline __host__ __device__ uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
+inline __host__ __device__ constexpr bool is_fp8(int layout) { return layout == WC_FP8_E4M3 || layout == WC_FP8_E5M2; }
+
 // Raw plane bytes of n elements: one raw byte per element for the 16-bit
-// layouts; sign bits plus three mantissa bytes for FP32.
+// layouts; sign bits plus three mantissa bytes for FP32; a nibble per
+// element for FP8.
 inline __host__ __device__ uint64_t raw_bytes_of(int layout, uint64_t n)
 {
-    return layout != WC_FP32 ? n : (n + 7) / 8 + 3 * n;
+    if (layout == WC_FP32) return (n + 7) / 8 + 3 * n;
+    if (is_fp8(layout)) return (n + 1) / 2;
+    return n;
 }
 
 // Payload of a chunk of len symbols stored raw (WC_OPT_RAW_FALLBACK).
@@ -73,6 +78,38 @@ struct Bits16<WC_FP16_REORDER> {
     __host__ __device__ static uint32_t from_coded(uint32_t t)
     {
         return bitsel(0x03FF03FFu, t, bitsel(0x80008000u, t << 5, t >> 1));
+    }
+};
+
+// FP8 layouts: the same reorder within each byte (the "PTWM" README: the
+// exponent moves into the high nibble, the sign right below it), on four
+// bytes packed in a u32.
+template <int DT>
+struct Bits8;
+
+// s e4 m3 <-> e4 s m3
+template <>
+struct Bits8<WC_FP8_E4M3> {
+    __host__ __device__ static uint32_t to_coded(uint32_t v)
+    {
+        return bitsel(0x07070707u, v, bitsel(0x08080808u, v >> 4, v << 1));
+    }
+    __host__ __device__ static uint32_t from_coded(uint32_t t)
+    {
+        return bitsel(0x07070707u, t, bitsel(0x80808080u, t << 4, t >> 1));
+    }
+};
+
+// s e5 m2 <-> e5 s m2
+template <>
+struct Bits8<WC_FP8_E5M2> {
+    __host__ __device__ static uint32_t to_coded(uint32_t v)
+    {
+        return bitsel(0x03030303u, v, bitsel(0x04040404u, v >> 5, v << 1));
+    }
+    __host__ __device__ static uint32_t from_coded(uint32_t t)
+    {
+        return bitsel(0x03030303u, t, bitsel(0x80808080u, t << 5, t >> 1));
     }
 };
 

@@ -190,7 +190,7 @@ __device__ __forceinline__ void refill_sync(Stream &st, uint32_t lane, bool ok, 
 // early); flush(): joins them with the 8 decoded bytes and stores.
 
 template <int DT>
-struct RawView {  // the 16-bit layouts
+struct RawView16 {  // the 16-bit layouts
     using B = Bits16<DT>;
     const WC_GLOBAL uint8_t *lo;
     WC_GLOBAL uint16_t *out;
@@ -244,8 +244,54 @@ struct RawView {  // the 16-bit layouts
     }
 };
 
-template <>
-struct RawView<WC_FP32> {
+// FP8: 8 elements take 4 raw bytes (8 nibbles, element 2j in the low nibble
+// of byte j); each output byte is the decoded nibble over the raw nibble
+// with the layout's reorder undone, 8 bytes stored at once.
+template <int DT>
+struct RawView8 {
+    using B = Bits8<DT>;
+    const WC_GLOBAL uint8_t *lo;
+    WC_GLOBAL uint8_t *out;
+    struct Pre {
+        uint32_t v;
+    };
+    __device__ void init(const uint8_t *raw, const wc_segment &sg, uint64_t start)
+    {
+        lo = gptr(raw) + sg.raw_base + start / 2;
+        out = gptr<uint8_t>(sg.ptr) + start;
+    }
+    // elements [e, e + 8), all inside the chunk, e a multiple of 8
+    __device__ Pre fetch(uint32_t e) const { return Pre{*reinterpret_cast<const WC_GLOBAL uint32_t *>(lo + e / 2)}; }
+    __device__ static u32x2 join(uint2 sym, uint32_t r)
+    {
+        const uint32_t a = r & 0x0F0F0F0Fu, b = (r >> 4) & 0x0F0F0F0Fu;  // elements 0,2,4,6 / 1,3,5,7
+        const uint32_t w0 = __builtin_amdgcn_perm(b, a, 0x05010400u), w1 = __builtin_amdgcn_perm(b, a, 0x07030602u);
+        return u32x2{B::from_coded((sym.x << 4) | w0), B::from_coded((sym.y << 4) | w1)};
+    }
+    __device__ void flush(uint32_t e, uint2 sym, const Pre &p) const
+    {
+        *reinterpret_cast<WC_GLOBAL u32x2 *>(out + e) = join(sym, p.v);
+    }
+    // tail chunks: only elements below len exist
+    __device__ Pre fetch_checked(uint32_t e, uint32_t len) const
+    {
+        if (e + 8 <= len) return fetch(e);
+        uint32_t v = 0;
+        for (uint32_t i = 0; e + 2 * i < len; i++) v |= (uint32_t)lo[e / 2 + i] << (8 * i);
+        return Pre{v};
+    }
+    __device__ void flush_checked(uint32_t e, uint2 sym, const Pre &p, uint32_t len) const
+    {
+        if (e + 8 <= len) {
+            flush(e, sym, p);
+            return;
+        }
+        const u32x2 o = join(sym, p.v);
+        for (uint32_t i = 0; e + i < len; i++) out[e + i] = (uint8_t)(((i < 4 ? o.x : o.y) >> (8 * (i & 3))) & 0xFF);
+    }
+};
+
+struct RawView32 {
     const WC_GLOBAL uint8_t *sign, *m0, *m1, *m2;
     WC_GLOBAL uint32_t *out;
     struct Pre {
@@ -277,6 +323,10 @@ struct RawView<WC_FP32> {
     }
     __device__ void flush(uint32_t e, uint2 sym, const Pre &p) const { flush_checked(e, sym, p, e + 8); }
 };
+
+template <int DT>
+using RawView = typename std::conditional<
+    DT == WC_FP32, RawView32, typename std::conditional<is_fp8(DT), RawView8<DT>, RawView16<DT>>::type>::type;
 
 // -------------------------------------------------------------- table lookup
 

@@ -152,7 +152,52 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
     __syncthreads();
     uint32_t *my = hist + (tid & (kHistCopies - 1)) * kHistStride;
 
-    if constexpr (DT != WC_FP32) {
+    if constexpr (is_fp8(DT)) {
+        // FP8: the reordered byte's high nibble is counted; the low nibbles
+        // are packed two per raw byte (element 2j in the low nibble of byte j)
+        using B8 = Bits8<DT>;
+        const WC_GLOBAL uint8_t *in = gptr<uint8_t>(sg.ptr) + start;
+        WC_GLOBAL uint8_t *lo = gptr(raw) + sg.raw_base + start / 2;
+        const uint32_t ng = len / 16;  // groups of 16 elements: 16 bytes in, 8 raw bytes out
+        auto group16 = [&](u32x4 v, uint32_t g) {
+            const u32x4 t = u32x4{B8::to_coded(v.x), B8::to_coded(v.y), B8::to_coded(v.z), B8::to_coded(v.w)};
+            // bytes 0 and 2 of pk(a) hold the packed pairs of a's four elements
+            auto pk = [](uint32_t a) {
+                const uint32_t l = a & 0x0F0F0F0Fu;
+                return l | (l >> 4);
+            };
+            reinterpret_cast<WC_GLOBAL u32x2 *>(lo)[g] = u32x2{__builtin_amdgcn_perm(pk(t.y), pk(t.x), 0x06040200u),
+                                                               __builtin_amdgcn_perm(pk(t.w), pk(t.z), 0x06040200u)};
+            const uint32_t h[4] = {(t.x >> 4) & 0x0F0F0F0Fu, (t.y >> 4) & 0x0F0F0F0Fu, (t.z >> 4) & 0x0F0F0F0Fu,
+                                   (t.w >> 4) & 0x0F0F0F0Fu};
+#pragma unroll
+            for (uint32_t q = 0; q < 4; q++)
+#pragma unroll
+                for (uint32_t i = 0; i < 4; i++) hist_add(my, (h[q] >> (8 * i)) & 0xFF);
+        };
+        constexpr uint32_t U = 4;
+        uint32_t g = tid;
+        for (; g + 256 * (U - 1) < ng; g += 256 * U) {
+            u32x4 v[U];
+#pragma unroll
+            for (uint32_t u = 0; u < U; u++) v[u] = reinterpret_cast<const WC_GLOBAL u32x4 *>(in)[g + 256 * u];
+#pragma unroll
+            for (uint32_t u = 0; u < U; u++) group16(v[u], g + 256 * u);
+        }
+        for (; g < ng; g += 256) group16(reinterpret_cast<const WC_GLOBAL u32x4 *>(in)[g], g);
+        // the tail by pairs of elements, so one thread owns each raw byte
+        for (uint32_t j = ng * 8 + tid; 2 * j < len; j += 256) {
+            const uint32_t t0 = B8::to_coded(in[2 * j]);
+            hist_add(my, t0 >> 4);
+            uint32_t rb = t0 & 0xF;
+            if (2 * j + 1 < len) {
+                const uint32_t t1 = B8::to_coded(in[2 * j + 1]);
+                hist_add(my, t1 >> 4);
+                rb |= (t1 & 0xF) << 4;
+            }
+            lo[j] = (uint8_t)rb;
+        }
+    } else if constexpr (DT != WC_FP32) {
         // 16-bit layouts: the coded / raw bytes are the high / low bytes of
         // the layout's rearrangement of each value
         const WC_GLOBAL uint16_t *in = gptr<uint16_t>(sg.ptr) + start;
@@ -275,7 +320,8 @@ constexpr uint32_t kEncBlk = kLanes * kEncGroup;
 // groups ahead of use.
 template <int DT>
 struct SymView {
-    using Elem = typename std::conditional<DT != WC_FP32, uint16_t, uint32_t>::type;
+    using Elem = typename std::conditional<
+        DT == WC_FP32, uint32_t, typename std::conditional<is_fp8(DT), uint8_t, uint16_t>::type>::type;
     const WC_GLOBAL Elem *in;
     struct Pre {
         uint32_t e[kEncGroup];
@@ -294,8 +340,9 @@ struct SymView {
     }
     __device__ static uint32_t symbol(uint32_t e)
     {
-        if constexpr (DT != WC_FP32) return Bits16<DT>::to_coded(e) >> 8;
-        else return (e >> 23) & 0xFF;
+        if constexpr (DT == WC_FP32) return (e >> 23) & 0xFF;
+        else if constexpr (is_fp8(DT)) return Bits8<DT>::to_coded(e) >> 4;
+        else return Bits16<DT>::to_coded(e) >> 8;
     }
 };
 
@@ -303,7 +350,7 @@ struct SymView {
 // wide loads; their coded bytes pass through an LDS stage to the lanes that
 // encode them (step i of lane l encodes element 32 i + l of the group).
 template <int DT>
-struct WideView {  // the 16-bit layouts
+struct WideView16 {  // the 16-bit layouts
     const WC_GLOBAL u32x4 *in;  // the chunk; 16 bytes = 8 elements per lane per group
     struct Pre {
         u32x4 v;
@@ -319,8 +366,22 @@ struct WideView {  // the 16-bit layouts
     }
 };
 
-template <>
-struct WideView<WC_FP32> {
+template <int DT>
+struct WideView8 {  // FP8
+    const WC_GLOBAL u32x2 *in;  // the chunk; 8 bytes = 8 elements per lane per group
+    struct Pre {
+        u32x2 v;
+    };
+    __device__ Pre fetch(uint32_t g, uint32_t lane) const { return Pre{in[kLanes * g + lane]}; }
+    // the coded nibbles of the 8 elements, one per byte, in element order
+    __device__ static uint2 bytes(const Pre &p)
+    {
+        return make_uint2((Bits8<DT>::to_coded(p.v.x) >> 4) & 0x0F0F0F0Fu,
+                          (Bits8<DT>::to_coded(p.v.y) >> 4) & 0x0F0F0F0Fu);
+    }
+};
+
+struct WideView32 {  // FP32
     const WC_GLOBAL u32x4 *in;  // 32 bytes = 8 elements per lane per group
     struct Pre {
         u32x4 a, b;
@@ -337,6 +398,10 @@ struct WideView<WC_FP32> {
                           e(p.b.x) | e(p.b.y) << 8 | e(p.b.z) << 16 | e(p.b.w) << 24);
     }
 };
+
+template <int DT>
+using WideView = typename std::conditional<
+    DT == WC_FP32, WideView32, typename std::conditional<is_fp8(DT), WideView8<DT>, WideView16<DT>>::type>::type;
 
 // One encode step for one lane: renormalise (the low 16 bits go to the word
 // list, which grows downwards from index p; the lane's rank among the half's
@@ -469,7 +534,7 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
         // symbols so staged.  Loads and stage traffic overlap the steps.
         using WPre = typename WideView<DT>::Pre;
         WideView<DT> wv;
-        wv.in = reinterpret_cast<const WC_GLOBAL u32x4 *>(sv.in);
+        wv.in = reinterpret_cast<decltype(wv.in)>(sv.in);
         const uint8_t *stg = reinterpret_cast<const uint8_t *>(&estage[h][0]);
         auto transpose = [&](const WPre &d, uint32_t (&sy)[kEncGroup]) {
             const uint2 b = WideView<DT>::bytes(d);

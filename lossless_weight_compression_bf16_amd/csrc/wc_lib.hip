@@ -27,7 +27,7 @@ uint64_t chunk_capacity(uint64_t len) { return 128 + 2 * (len + (len & 1)); }
 
 bool valid_format(uint32_t f)
 {
-    return (f & WC_LAYOUT_MASK) <= WC_FP16_REORDER &&
+    return (f & WC_LAYOUT_MASK) <= WC_FP8_E5M2 &&
            (f & ~(WC_LAYOUT_MASK | WC_OPT_TENSOR_TABLE | WC_OPT_RAW_FALLBACK)) == 0;
 }
 int layout_code(uint32_t f) { return (int)(f & WC_LAYOUT_MASK); }
@@ -208,6 +208,8 @@ wc_status encode_any(uint32_t format, const SegTable &st, uint64_t chunks, uint6
         return encode_impl<WC_BF16_REORDER>(st, chunks, raw_total, out, d_scratch, d_err, stream, ev, o);
     case WC_FP16_REORDER:
         return encode_impl<WC_FP16_REORDER>(st, chunks, raw_total, out, d_scratch, d_err, stream, ev, o);
+    case WC_FP8_E4M3: return encode_impl<WC_FP8_E4M3>(st, chunks, raw_total, out, d_scratch, d_err, stream, ev, o);
+    case WC_FP8_E5M2: return encode_impl<WC_FP8_E5M2>(st, chunks, raw_total, out, d_scratch, d_err, stream, ev, o);
     default: return encode_impl<WC_BF16>(st, chunks, raw_total, out, d_scratch, d_err, stream, ev, o);
     }
 }
@@ -220,6 +222,8 @@ wc_status decode_any(uint32_t format, const SegTable &st, uint64_t chunks, uint6
     case WC_FP32: return decode_impl<WC_FP32>(st, chunks, n, in, d_err, stream, o);
     case WC_BF16_REORDER: return decode_impl<WC_BF16_REORDER>(st, chunks, n, in, d_err, stream, o);
     case WC_FP16_REORDER: return decode_impl<WC_FP16_REORDER>(st, chunks, n, in, d_err, stream, o);
+    case WC_FP8_E4M3: return decode_impl<WC_FP8_E4M3>(st, chunks, n, in, d_err, stream, o);
+    case WC_FP8_E5M2: return decode_impl<WC_FP8_E5M2>(st, chunks, n, in, d_err, stream, o);
     default: return decode_impl<WC_BF16>(st, chunks, n, in, d_err, stream, o);
     }
 }

@@ -64,7 +64,8 @@ def test_plan_batch_matches_oracle(L, oracle_lib):
         assert tot.payload_capacity == otot.payload_capacity
 
 
-FORMATS = [(lay, opts) for lay in ("bf16", "bf16r", "fp16", "fp16r", "fp32") for opts in (0, 0x100, 0x200, 0x300)]
+FORMATS = [(lay, opts) for lay in ("bf16", "bf16r", "fp16", "fp16r", "fp32", "fp8e4m3", "fp8e5m2")
+           for opts in (0, 0x100, 0x200, 0x300)]
 
 
 @pytest.mark.parametrize("lay,opts", FORMATS)
@@ -91,7 +92,7 @@ def test_variant_plan_batch_matches_oracle(L, oracle_lib, lay, opts):
 
 
 def test_bad_format_words_are_rejected(L):
-    for f in (5, 0xFF, 0x400, 0x10000, 0x80000000):
+    for f in (7, 0xFF, 0x400, 0x10000, 0x80000000):
         with pytest.raises(B.WcError):
             wc.wc_query_layout(f, 100)
         assert L.wc_query_layout(f, 100, ctypes.byref(B.wc_layout())) == B.WC_ERR_ARG
