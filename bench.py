@@ -37,8 +37,9 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    p.add_argument("--layout", default=None, choices=["bf16", "bf16r", "fp16", "fp16r", "fp32"],
-                   help="plane layout (default: the set's own type; fp16* store the set as IEEE half)")
+    p.add_argument("--layout", default=None, choices=["bf16", "bf16r", "fp16", "fp16r", "fp32", "fp8e4m3", "fp8e5m2"],
+                   help="plane layout (default: the set's own type; fp16* store the set as IEEE half, "
+                        "fp8* as FP8 scaled per tensor)")
     p.add_argument("--tensor-table", action="store_true", help="one frequency table per tensor")
     p.add_argument("--raw-fallback", action="store_true", help="store chunks that do not shrink raw")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -157,6 +158,8 @@ def coded_symbols(layout, seg):
     """The coded byte of each element under a plane layout (for reporting)."""
     if layout == "fp32":
         return ((seg.view(np.uint32) >> 23) & 0xFF).astype(np.uint8)
+    if layout.startswith("fp8"):
+        return ((seg.view(np.uint8) >> 3) & 0xF).astype(np.uint8)  # the exponent's top 4 bits
     v = seg.view(np.uint16)
     if layout == "bf16r":
         return ((v >> 7) & 0xFF).astype(np.uint8)
@@ -211,6 +214,8 @@ def main():
     layout = args.layout or w.dtype
     if layout.startswith("fp16"):
         w = S.with_dtype(w, "fp16")
+    elif layout.startswith("fp8"):
+        w = S.with_dtype(w, layout)
     elif (layout == "fp32") != (w.dtype == "fp32"):
         raise SystemExit(f"layout {layout} does not fit the {w.dtype} set {w.name}")
     opts = (B.WC_OPT_TENSOR_TABLE if args.tensor_table else 0) | (B.WC_OPT_RAW_FALLBACK if args.raw_fallback else 0)
@@ -219,8 +224,8 @@ def main():
     t0 = time.perf_counter()
     xs = S.set_bits(w)
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s; uploading")
-    ity = torch.int32 if w.dtype == "fp32" else torch.int16
-    nty = np.int32 if w.dtype == "fp32" else np.int16
+    ity = {4: torch.int32, 2: torch.int16, 1: torch.uint8}[w.elem_bytes]
+    nty = {4: np.int32, 2: np.int16, 1: np.uint8}[w.elem_bytes]
     ins = [torch.from_numpy(x.view(nty)).to(dev) for x in xs]
     outs = [torch.empty_like(t) for t in ins]
     ns = [t.numel() for t in ins]

@@ -24,6 +24,11 @@ Recipe
   for finite values).
 * FP16 (``with_dtype(w, "fp16")``): the same float32 values rounded to IEEE
   half by numpy (round to nearest even).
+* FP8 (``with_dtype(w, "fp8e4m3")`` / ``"fp8e5m2"``): per tensor, the float32
+  values scaled so the largest magnitude becomes the format's largest finite
+  value (the usual per-tensor FP8 scaling), rounded by torch's float8 types.
+  The scale depends on the whole tensor, so FP8 sets are generated a tensor
+  at a time (``tensor_bits``), not block by block.
 """
 from __future__ import annotations
 
@@ -35,6 +40,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 GEN_BLOCK = 1 << 20
+FP8_TYPES = {"fp8e4m3": "float8_e4m3fn", "fp8e5m2": "float8_e5m2"}
 
 
 @dataclass(frozen=True)
@@ -51,7 +57,7 @@ class Dist:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str                  # "bf16", "fp16" or "fp32"
+    dtype: str                  # "bf16", "fp16", "fp32", "fp8e4m3" or "fp8e5m2"
     shapes: tuple               # tuple of (rows, cols) in set order
     dist: Dist
     seed: int = 0
@@ -67,7 +73,7 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 4 if self.dtype == "fp32" else 2
+        return 4 if self.dtype == "fp32" else 1 if self.dtype in FP8_TYPES else 2
 
     @property
     def raw_bytes(self) -> int:
@@ -125,7 +131,7 @@ def with_dtype(w: Workload, dtype: str) -> Workload:
     """The same set (shapes, distribution, seed) stored as another float type."""
     if dtype == w.dtype:
         return w
-    if w.dtype == "fp32" or dtype not in ("bf16", "fp16"):
+    if w.dtype == "fp32" or dtype not in ("bf16", "fp16", *FP8_TYPES):
         raise ValueError(f"{w.name} cannot be stored as {dtype}")
     return Workload(f"{w.name}-as-{dtype}", dtype, w.shapes, w.dist, w.seed, w.note)
 
@@ -175,6 +181,8 @@ def block_f32(w: Workload, i: int, j: int) -> np.ndarray:
 
 def block_bits(w: Workload, i: int, j: int) -> np.ndarray:
     """Bit patterns (uint16 for bf16 / fp16, uint32 for fp32) of block j of tensor i."""
+    if w.dtype in FP8_TYPES:
+        raise ValueError("FP8 sets are scaled per tensor: use tensor_bits")
     v = block_f32(w, i, j)
     if w.dtype == "fp32":
         return v.view(np.uint32)
@@ -183,8 +191,28 @@ def block_bits(w: Workload, i: int, j: int) -> np.ndarray:
     return f32_to_bf16_bits(v)
 
 
+def _fp8_tensor(w: Workload, i: int, threads: int | None) -> np.ndarray:
+    import torch
+    f = tensor_bits(with_dtype_f32(w), i, threads)  # float32 values as bit patterns
+    v = torch.from_numpy(f.view(np.float32))
+    dt = getattr(torch, FP8_TYPES[w.dtype])
+    amax = float(v.abs().max()) if v.numel() else 1.0
+    return (v * (torch.finfo(dt).max / max(amax, 1e-30))).to(dt).view(torch.uint8).numpy()
+
+
+def with_dtype_f32(w: Workload) -> Workload:
+    """The same set as float32 values (the draws before any rounding)."""
+    return Workload(w.name, "fp32", w.shapes, w.dist, w.seed, w.note)
+
+
 def tensor_bits(w: Workload, i: int, threads: int | None = None, out: np.ndarray | None = None):
     """All bit patterns of tensor i (flat)."""
+    if w.dtype in FP8_TYPES:
+        v = _fp8_tensor(w, i, threads)
+        if out is not None:
+            out[:] = v
+            return out
+        return v
     n = w.numels[i]
     dt = np.uint32 if w.dtype == "fp32" else np.uint16
     if out is None:
