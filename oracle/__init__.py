@@ -28,9 +28,11 @@ DTYPES = {"bf16": BF16, "fp32": FP32, "bf16r": BF16_REORDER, "fp16": FP16, "fp16
 # option bits of a format word
 OPT_TENSOR_TABLE = 0x100  # one table per tensor
 OPT_RAW_FALLBACK = 0x200  # chunks that do not shrink are stored raw
+OPT_CRC32 = 0x400         # a CRC-32 of every chunk's payload
 
 OK, ERR_ARG, ERR_CAPACITY, ERR_CORRUPT = 0, 1, 2, 3
 EF_BAD_TABLE, EF_WORD_OVERRUN, EF_BAD_FINAL_STATE, EF_BAD_TAIL, EF_BAD_SEEK = 1, 2, 4, 8, 16
+EF_BAD_CRC = 64
 
 CHUNK = 65536
 
@@ -72,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.wco_normalize64.argtypes = [P, U64, P]
         L.wco_split_u16.argtypes = [I, P, U64, P, P]
         L.wco_split_fp8.argtypes = [I, P, U64, P, P]
+        L.wco_crc32.argtypes = [P, U64]
+        L.wco_crc32.restype = U32
+        L.wco_chunk_crc.argtypes = [P, P, U64, P]
         L.wco_merge_fp8.argtypes = [I, P, P, U64, P]
         L.wco_merge_u16.argtypes = [I, P, P, U64, P]
         L.wco_encode_chunk.argtypes = [P, U32, P, P]
@@ -240,6 +245,25 @@ def decode_chunk(payload: np.ndarray, freq: np.ndarray, n: int):
     sym = np.zeros(n, np.uint8)
     err = lib().wco_decode_chunk(_p(payload), payload.size, _p(freq), n, _p(sym))
     return sym, int(err)
+
+
+# ------------------------------------------------------------------ CRC-32
+
+def crc32(data) -> int:
+    a = np.ascontiguousarray(np.frombuffer(bytes(data), np.uint8) if isinstance(data, (bytes, bytearray))
+                             else data, np.uint8)
+    buf = a if a.size else np.zeros(1, np.uint8)
+    return int(lib().wco_crc32(_p(buf), a.size))
+
+
+def chunk_crc(seek: np.ndarray, payload: np.ndarray) -> np.ndarray:
+    """CRC-32 of every chunk's payload bytes."""
+    seek = np.ascontiguousarray(seek, np.uint64)
+    payload = np.ascontiguousarray(payload, np.uint8)
+    pay = payload if payload.size else np.zeros(1, np.uint8)
+    out = np.zeros(max(seek.size - 1, 1), np.uint32)
+    lib().wco_chunk_crc(_p(seek), _p(pay), seek.size - 1, _p(out))
+    return out[: seek.size - 1]
 
 
 # ------------------------------------------------------------ whole tensor

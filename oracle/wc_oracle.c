@@ -54,6 +54,12 @@
  *     high nibble is coded (symbols 0..15, through the same tables and
  *     coder), the low nibble stored raw, two per byte, element 2j in the low
  *     nibble of byte j (a last odd element leaves the high nibble zero).
+ *   - CRC32 (the "SeedPack" README: every chunk of its archive carries a
+ *     CRC32; here every chunk of the coded plane): crc[k] is the CRC-32 of
+ *     chunk k's payload bytes, the common ISO-HDLC / zlib CRC (polynomial
+ *     0x04C11DB7 processed least significant bit first, i.e. 0xEDB88320
+ *     reflected, register preset to all ones, result complemented).  It
+ *     does not change any other byte of the encoding.
  *   - TENSOR_TABLE (reading: the per-tensor codec records of the "PTWM"
  *     README's container, one table for a tensor's chunks): a single table,
  *     normalised from the histogram of the tensor's whole coded plane, codes
@@ -84,7 +90,7 @@ static int layout_of(int format)
 {
     int layout = format & WCO_LAYOUT_MASK;
     if (layout > WCO_FP8_E5M2) return -1;
-    if (format & ~(WCO_LAYOUT_MASK | WCO_OPT_TENSOR_TABLE | WCO_OPT_RAW_FALLBACK)) return -1;
+    if (format & ~(WCO_LAYOUT_MASK | WCO_OPT_TENSOR_TABLE | WCO_OPT_RAW_FALLBACK | WCO_OPT_CRC32)) return -1;
     return layout;
 }
 
@@ -447,6 +453,25 @@ uint32_t wco_decode_chunk(const uint8_t *p, uint64_t size, const uint16_t freq[2
         err |= WCO_EF_BAD_TAIL;
     }
     return err;
+}
+
+/* ------------------------------------------------------------------ CRC-32 */
+
+/* One bit at a time: the register's low bit is the coefficient that leaves
+ * next; a 1 leaving means subtracting (xor) the polynomial. */
+uint32_t wco_crc32(const uint8_t *p, uint64_t n)
+{
+    uint32_t r = 0xFFFFFFFFu;
+    for (uint64_t i = 0; i < n; i++) {
+        r ^= p[i];
+        for (int b = 0; b < 8; b++) r = (r & 1u) ? (r >> 1) ^ 0xEDB88320u : r >> 1;
+    }
+    return r ^ 0xFFFFFFFFu;
+}
+
+void wco_chunk_crc(const uint64_t *seek, const uint8_t *payload, uint64_t chunks, uint32_t *crc)
+{
+    for (uint64_t k = 0; k < chunks; k++) crc[k] = wco_crc32(payload + seek[k], seek[k + 1] - seek[k]);
 }
 
 /* ------------------------------------------------------------ whole tensor */

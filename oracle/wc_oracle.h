@@ -47,6 +47,7 @@ extern "C" {
 /* Options: */
 #define WCO_OPT_TENSOR_TABLE 0x100 /* one frequency table per tensor (its whole coded plane), not per chunk */
 #define WCO_OPT_RAW_FALLBACK 0x200 /* a chunk whose code is not shorter than its symbols stores them raw */
+#define WCO_OPT_CRC32 0x400        /* a CRC-32 of every chunk's payload accompanies the encoding */
 
 /* status codes */
 #define WCO_OK 0
@@ -60,6 +61,7 @@ extern "C" {
 #define WCO_EF_BAD_FINAL_STATE 4u /* a lane did not end at the initial state */
 #define WCO_EF_BAD_TAIL 8u        /* unconsumed words or a non-zero pad word */
 #define WCO_EF_BAD_SEEK 16u       /* seek entries out of order, out of range or misaligned */
+#define WCO_EF_BAD_CRC 64u        /* a chunk's payload does not match its CRC-32 */
 
 typedef struct {
     uint64_t n;                /* elements */
@@ -97,6 +99,12 @@ uint32_t wco_encode_chunk(const uint8_t *sym, uint32_t n, const uint16_t freq[25
 /* Decodes; returns 0 or WCO_EF_* bits.  Never reads outside p[0, size). */
 uint32_t wco_decode_chunk(const uint8_t *p, uint64_t size, const uint16_t freq[256], uint32_t n,
                           uint8_t *sym);
+
+/* CRC-32 (the ISO-HDLC / zlib CRC: reflected polynomial 0xEDB88320, register
+ * preset to all ones, result complemented) of n bytes, bit by bit. */
+uint32_t wco_crc32(const uint8_t *p, uint64_t n);
+/* crc[k] = wco_crc32 of chunk k's payload bytes [seek[k], seek[k+1]). */
+void wco_chunk_crc(const uint64_t *seek, const uint8_t *payload, uint64_t chunks, uint32_t *crc);
 
 /* Whole tensor.  threads <= 1 runs on the calling thread; otherwise chunks
  * are split into contiguous ranges over that many POSIX threads. */

@@ -309,3 +309,30 @@ def test_batch_with_options():
     for i, x in enumerate(xs):
         one = oracle.encode(x, "bf16r", opts=opts)
         assert np.array_equal(e.tables[i], one.tables[0])
+
+
+# ----------------------------------------------------------------- CRC-32
+
+def test_crc32_check_value():
+    # the CRC-32/ISO-HDLC catalogue check value: CRC of the ASCII digits 1..9
+    assert oracle.crc32(b"123456789") == 0xCBF43926
+    assert oracle.crc32(b"") == 0
+
+
+def test_crc32_matches_zlib():
+    import zlib
+    g = np.random.default_rng(41)
+    for n in (1, 3, 4, 63, 64, 65, 1000, 21847, 131200):
+        a = g.integers(0, 256, n).astype(np.uint8)
+        assert oracle.crc32(a) == zlib.crc32(a.tobytes())
+
+
+def test_chunk_crc_of_an_encoding():
+    import zlib
+    v = _bf16_weights(3 * 65536 + 5, seed=42)
+    e = oracle.encode(v, "bf16", opts=oracle.OPT_CRC32)
+    plain = oracle.encode(v, "bf16")
+    assert np.array_equal(e.payload, plain.payload) and np.array_equal(e.seek, plain.seek)
+    crc = oracle.chunk_crc(e.seek, e.payload)
+    for k in range(4):
+        assert crc[k] == zlib.crc32(e.payload[int(e.seek[k]):int(e.seek[k + 1])].tobytes())
