@@ -46,6 +46,10 @@
  *     payload would be at least its symbol count rounded up to 4 bytes is
  *     stored as its symbols plus zero padding to that size; a payload of
  *     exactly that size marks such a chunk.
+ *   - WC_OPT_CRC32 ("SeedPack" README: every chunk carries a CRC32): crc[k]
+ *     = CRC-32 of chunk k's payload bytes (the ISO-HDLC / zlib CRC), written
+ *     by encode, checked by decode before it decodes (WC_EF_BAD_CRC).  No
+ *     other byte changes.
  *   Format word 0 (WC_BF16) and 1 (WC_FP32) without options is format v1.
  * The result is bit-exact: decode(encode(x)) reproduces every bit pattern,
  * NaN payloads, infinities, subnormals and -0 included (Split12 README: the
@@ -95,6 +99,7 @@ typedef enum {
 #define WC_LAYOUT_MASK 0xFFu
 #define WC_OPT_TENSOR_TABLE 0x100u
 #define WC_OPT_RAW_FALLBACK 0x200u
+#define WC_OPT_CRC32 0x400u
 /* A plane layout OR-ed with option bits.  Encoder and decoder must be given
  * the same format word; any other bit set is WC_ERR_ARG. */
 typedef uint32_t wc_format;
@@ -114,6 +119,7 @@ typedef enum {
 #define WC_EF_BAD_TAIL 8u        /* words left over, or a non-zero pad word */
 #define WC_EF_BAD_SEEK 16u       /* seek entries out of order, misaligned or past payload_bytes */
 #define WC_EF_CAPACITY 32u       /* encode: the payload did not fit payload_bytes */
+#define WC_EF_BAD_CRC 64u        /* decode with WC_OPT_CRC32: a chunk's payload does not match crc[k] */
 
 #define WC_CHUNK 65536u
 
@@ -127,6 +133,7 @@ typedef struct {
     uint64_t payload_capacity; /* worst-case payload: 128 + 2 * (len + len % 2) per chunk;
                                   with WC_OPT_RAW_FALLBACK len rounded up to 4 per chunk */
     uint64_t scratch_bytes;    /* encoder scratch */
+    uint64_t crc_bytes;        /* 4 * num_chunks with WC_OPT_CRC32, else 0 */
 } wc_layout;
 
 /* Device buffers of one encoding.  For encode, payload_bytes is the payload
@@ -138,6 +145,7 @@ typedef struct {
     uint64_t *seek;
     uint8_t *payload;
     uint64_t payload_bytes;
+    uint32_t *crc;             /* WC_OPT_CRC32 only (else ignored): num_chunks u32 */
 } wc_buffers;
 
 /* One tensor of a batch.  `ptr` is the device address of the tensor (input

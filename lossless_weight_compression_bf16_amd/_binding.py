@@ -19,6 +19,7 @@ DTYPE_CODES = {"bf16": WC_BF16, "fp32": WC_FP32, "bf16r": WC_BF16_REORDER, "fp16
                "fp16r": WC_FP16_REORDER, "fp8e4m3": WC_FP8_E4M3, "fp8e5m2": WC_FP8_E5M2}
 WC_OPT_TENSOR_TABLE = 0x100
 WC_OPT_RAW_FALLBACK = 0x200
+WC_OPT_CRC32 = 0x400
 
 WC_OK, WC_ERR_ARG, WC_ERR_CAPACITY, WC_ERR_CORRUPT, WC_ERR_HIP = 0, 1, 2, 3, 4
 EF_BAD_TABLE = 1
@@ -27,9 +28,10 @@ EF_BAD_FINAL_STATE = 4
 EF_BAD_TAIL = 8
 EF_BAD_SEEK = 16
 EF_CAPACITY = 32
+EF_BAD_CRC = 64
 EF_NAMES = {EF_BAD_TABLE: "bad table", EF_WORD_OVERRUN: "word overrun",
             EF_BAD_FINAL_STATE: "bad final state", EF_BAD_TAIL: "bad tail",
-            EF_BAD_SEEK: "bad seek", EF_CAPACITY: "payload capacity"}
+            EF_BAD_SEEK: "bad seek", EF_CAPACITY: "payload capacity", EF_BAD_CRC: "CRC mismatch"}
 
 CHUNK = 65536
 
@@ -45,7 +47,7 @@ class wc_layout(ctypes.Structure):
     _fields_ = [("n", ctypes.c_uint64), ("num_chunks", ctypes.c_uint64),
                 ("raw_bytes", ctypes.c_uint64), ("table_bytes", ctypes.c_uint64),
                 ("seek_bytes", ctypes.c_uint64), ("payload_capacity", ctypes.c_uint64),
-                ("scratch_bytes", ctypes.c_uint64)]
+                ("scratch_bytes", ctypes.c_uint64), ("crc_bytes", ctypes.c_uint64)]
 
     def as_dict(self):
         return {k: int(getattr(self, k)) for k, _ in self._fields_}
@@ -53,7 +55,7 @@ class wc_layout(ctypes.Structure):
 
 class wc_buffers(ctypes.Structure):
     _fields_ = [("raw", ctypes.c_void_p), ("tables", ctypes.c_void_p), ("seek", ctypes.c_void_p),
-                ("payload", ctypes.c_void_p), ("payload_bytes", ctypes.c_uint64)]
+                ("payload", ctypes.c_void_p), ("payload_bytes", ctypes.c_uint64), ("crc", ctypes.c_void_p)]
 
 
 class wc_segment(ctypes.Structure):
@@ -120,10 +122,10 @@ def _code(dtype) -> int:
     return DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
 
 
-def format_word(dtype, tensor_table: bool = False, raw_fallback: bool = False) -> int:
+def format_word(dtype, tensor_table: bool = False, raw_fallback: bool = False, crc: bool = False) -> int:
     """A plane layout (name or code) OR-ed with the option bits."""
     return (_code(dtype) | (WC_OPT_TENSOR_TABLE if tensor_table else 0)
-            | (WC_OPT_RAW_FALLBACK if raw_fallback else 0))
+            | (WC_OPT_RAW_FALLBACK if raw_fallback else 0) | (WC_OPT_CRC32 if crc else 0))
 
 
 def elem_bytes(fmt) -> int:
@@ -158,8 +160,8 @@ def wc_plan_batch(dtype, ns):
     return segs, tot
 
 
-def make_buffers(raw, tables, seek, payload, payload_bytes: int) -> wc_buffers:
-    return wc_buffers(_ptr(raw), _ptr(tables), _ptr(seek), _ptr(payload), int(payload_bytes))
+def make_buffers(raw, tables, seek, payload, payload_bytes: int, crc=None) -> wc_buffers:
+    return wc_buffers(_ptr(raw), _ptr(tables), _ptr(seek), _ptr(payload), int(payload_bytes), _ptr(crc))
 
 
 def wc_encode(dtype, d_in, n: int, bufs: wc_buffers, d_scratch, scratch_bytes: int, d_err=None,

@@ -10,7 +10,8 @@ as BF16; FP8 (E4M3, E5M2) is split into the exponent nibble, which is coded,
 and the other nibble, stored raw two per byte.  Options: ``reorder`` applies the PTWM README's bit reorder first
 (16-bit layouts: the coded byte starts with the whole exponent), and
 ``tensor_table`` / ``raw_fallback`` select one table per tensor and raw
-storage of chunks that do not shrink.  Tensors are handled as bit patterns
+storage of chunks that do not shrink; ``crc`` adds a CRC-32 per chunk that
+decode checks on the GPU.  Tensors are handled as bit patterns
 (uint16 / int32 views), never converted, so every pattern round-trips.
 """
 from __future__ import annotations
@@ -61,6 +62,7 @@ class Encoded:
     seek: torch.Tensor         # int64 (u64), chunks + 1
     payload: torch.Tensor      # uint8, seek[-1] bytes
     fmt: int = 0               # format word (layout | options)
+    crc: torch.Tensor | None = None  # int32 (u32 CRC-32 per chunk), with the CRC option
 
     @property
     def num_chunks(self) -> int:
@@ -68,7 +70,8 @@ class Encoded:
 
     @property
     def compressed_bytes(self) -> int:
-        return int(self.raw.numel() + self.tables.numel() * 2 + self.seek.numel() * 8 + self.payload.numel())
+        return int(self.raw.numel() + self.tables.numel() * 2 + self.seek.numel() * 8 + self.payload.numel()
+                   + (self.crc.numel() * 4 if self.crc is not None else 0))
 
     @property
     def raw_input_bytes(self) -> int:
@@ -79,11 +82,14 @@ class Encoded:
         return self.compressed_bytes / max(self.raw_input_bytes, 1)
 
     def buffers(self) -> B.wc_buffers:
-        return B.make_buffers(self.raw, self.tables, self.seek, self.payload, self.payload.numel())
+        return B.make_buffers(self.raw, self.tables, self.seek, self.payload, self.payload.numel(), self.crc)
 
     def to_host(self) -> dict:
-        return {"raw": self.raw.cpu().numpy(), "tables": self.tables.cpu().numpy().view("<u2"),
-                "seek": self.seek.cpu().numpy().view("<u8"), "payload": self.payload.cpu().numpy()}
+        h = {"raw": self.raw.cpu().numpy(), "tables": self.tables.cpu().numpy().view("<u2"),
+             "seek": self.seek.cpu().numpy().view("<u8"), "payload": self.payload.cpu().numpy()}
+        if self.crc is not None:
+            h["crc"] = self.crc.cpu().numpy().view("<u4")
+        return h
 
 
 def _raise_bits(bits: int, what: str):
@@ -104,12 +110,12 @@ def _layout_for(t: torch.Tensor, layout, reorder: bool) -> str:
 
 
 def encode(t: torch.Tensor, stream=None, reorder: bool = False, tensor_table: bool = False,
-           raw_fallback: bool = False, layout: str | None = None) -> Encoded:
+           raw_fallback: bool = False, layout: str | None = None, crc: bool = False) -> Encoded:
     """Losslessly encode a bf16 / fp16 / fp32 / fp8 device tensor (synchronises
     once to size the payload)."""
     _check_device(t)
     dtype = _layout_for(t, layout, reorder)
-    fmt = B.format_word(dtype, tensor_table, raw_fallback)
+    fmt = B.format_word(dtype, tensor_table, raw_fallback, crc)
     x = _bits(t, dtype)
     n = x.numel()
     dev = x.device
@@ -120,13 +126,15 @@ def encode(t: torch.Tensor, stream=None, reorder: bool = False, tensor_table: bo
     payload = torch.empty(max(lay.payload_capacity, 16), dtype=torch.uint8, device=dev)
     scratch = torch.empty(max(lay.scratch_bytes, 256), dtype=torch.uint8, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    bufs = B.make_buffers(raw, tables, seek, payload, lay.payload_capacity)
+    crcs = torch.empty(max(lay.num_chunks, 1), dtype=torch.int32, device=dev) if crc else None
+    bufs = B.make_buffers(raw, tables, seek, payload, lay.payload_capacity, crcs)
     B.wc_encode(fmt, x, n, bufs, scratch, scratch.numel(), err, stream)
     total = int(seek[-1].item())
     _raise_bits(int(err.item()), "encode")
     del scratch
     return Encoded(dtype, n, tuple(t.shape), t.dtype, raw[: lay.raw_bytes],
-                   tables[: lay.table_bytes // 2].view(-1, 256), seek, payload[:total].clone(), fmt)
+                   tables[: lay.table_bytes // 2].view(-1, 256), seek, payload[:total].clone(), fmt,
+                   crcs[: lay.num_chunks] if crc else None)
 
 
 def decode(e: Encoded, out: torch.Tensor | None = None, stream=None, check: bool = True) -> torch.Tensor:
@@ -158,10 +166,12 @@ class EncodedBatch:
     payload: torch.Tensor
     h_segs: object = field(repr=False, default=None)
     fmt: int = 0
+    crc: torch.Tensor | None = None
 
     @property
     def compressed_bytes(self) -> int:
-        return int(self.raw.numel() + self.tables.numel() * 2 + self.seek.numel() * 8 + self.payload.numel())
+        return int(self.raw.numel() + self.tables.numel() * 2 + self.seek.numel() * 8 + self.payload.numel()
+                   + (self.crc.numel() * 4 if self.crc is not None else 0))
 
     @property
     def raw_input_bytes(self) -> int:
@@ -172,7 +182,7 @@ class EncodedBatch:
         return self.compressed_bytes / max(self.raw_input_bytes, 1)
 
     def buffers(self) -> B.wc_buffers:
-        return B.make_buffers(self.raw, self.tables, self.seek, self.payload, self.payload.numel())
+        return B.make_buffers(self.raw, self.tables, self.seek, self.payload, self.payload.numel(), self.crc)
 
 
 def _segments(dtype, xs, dev):
@@ -192,7 +202,7 @@ def segments_to_device(h_segs, nseg: int, dev) -> torch.Tensor:
 
 
 def encode_batch(ts, stream=None, reorder: bool = False, tensor_table: bool = False,
-                 raw_fallback: bool = False, layout: str | None = None) -> EncodedBatch:
+                 raw_fallback: bool = False, layout: str | None = None, crc: bool = False) -> EncodedBatch:
     """Encode a list of same-dtype device tensors in one launch sequence."""
     if not ts:
         raise ValueError("empty batch")
@@ -201,7 +211,7 @@ def encode_batch(ts, stream=None, reorder: bool = False, tensor_table: bool = Fa
     dtype = _layout_for(ts[0], layout, reorder)
     if any(_layout_for(t, layout, reorder) != dtype for t in ts):
         raise TypeError("all tensors of a batch must share a dtype")
-    fmt = B.format_word(dtype, tensor_table, raw_fallback)
+    fmt = B.format_word(dtype, tensor_table, raw_fallback, crc)
     xs = [_bits(t, dtype) for t in ts]
     dev = xs[0].device
     h_segs, d_segs, tot = _segments(fmt, xs, dev)
@@ -211,14 +221,15 @@ def encode_batch(ts, stream=None, reorder: bool = False, tensor_table: bool = Fa
     payload = torch.empty(max(tot.payload_capacity, 16), dtype=torch.uint8, device=dev)
     scratch = torch.empty(max(tot.scratch_bytes, 256), dtype=torch.uint8, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    bufs = B.make_buffers(raw, tables, seek, payload, tot.payload_capacity)
+    crcs = torch.empty(max(tot.num_chunks, 1), dtype=torch.int32, device=dev) if crc else None
+    bufs = B.make_buffers(raw, tables, seek, payload, tot.payload_capacity, crcs)
     B.wc_encode_batch(fmt, h_segs, d_segs, len(xs), bufs, scratch, scratch.numel(), err, stream)
     total = int(seek[-1].item())
     _raise_bits(int(err.item()), "encode_batch")
     del scratch
     return EncodedBatch(dtype, [x.numel() for x in xs], [tuple(t.shape) for t in ts], ts[0].dtype,
                         raw[: tot.raw_bytes], tables[: tot.table_bytes // 2].view(-1, 256), seek,
-                        payload[:total].clone(), h_segs, fmt)
+                        payload[:total].clone(), h_segs, fmt, crcs[: tot.num_chunks] if crc else None)
 
 
 def decode_batch(e: EncodedBatch, outs=None, stream=None, check: bool = True):

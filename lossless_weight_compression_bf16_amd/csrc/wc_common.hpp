@@ -119,6 +119,7 @@ struct Opts {
     uint32_t bits;
     __host__ __device__ bool tensor_table() const { return bits & WC_OPT_TENSOR_TABLE; }
     __host__ __device__ bool raw_fallback() const { return bits & WC_OPT_RAW_FALLBACK; }
+    __host__ __device__ bool crc() const { return bits & WC_OPT_CRC32; }
 };
 
 // Device addresses held as integers (segment tables) are always global

@@ -2,8 +2,10 @@
 //
 // Host side: argument validation, buffer layout, and the launch sequence
 //   encode: k_split_hist -> k_encode -> k_scan_tiles, k_scan_apply -> k_compact
-//           (tensor-wide tables: k_zero_u64 before the split, k_tensor_table after)
-//   decode: k_decode (then k_decode_raw for chunks stored raw)
+//           (tensor-wide tables: k_zero_u64 before the split, k_tensor_table after;
+//           CRC-32 option: k_crc32 after the compaction)
+//   decode: k_decode (then k_decode_raw for chunks stored raw; CRC-32 option:
+//           k_crc32 check before)
 // on the caller's stream.  No allocation, no synchronisation, no global state.
 #include <hip/hip_runtime.h>
 
@@ -12,6 +14,7 @@
 
 #include "wc.h"
 #include "wc_common.hpp"
+#include "wc_crc.hpp"
 #include "wc_decode.hpp"
 #include "wc_encode.hpp"
 
@@ -28,10 +31,11 @@ uint64_t chunk_capacity(uint64_t len) { return 128 + 2 * (len + (len & 1)); }
 bool valid_format(uint32_t f)
 {
     return (f & WC_LAYOUT_MASK) <= WC_FP8_E5M2 &&
-           (f & ~(WC_LAYOUT_MASK | WC_OPT_TENSOR_TABLE | WC_OPT_RAW_FALLBACK)) == 0;
+           (f & ~(WC_LAYOUT_MASK | WC_OPT_TENSOR_TABLE | WC_OPT_RAW_FALLBACK | WC_OPT_CRC32)) == 0;
 }
+bool has_crc(uint32_t f) { return (f & WC_OPT_CRC32) != 0; }
 int layout_code(uint32_t f) { return (int)(f & WC_LAYOUT_MASK); }
-Opts opts_of(uint32_t f) { return Opts{f & (WC_OPT_TENSOR_TABLE | WC_OPT_RAW_FALLBACK)}; }
+Opts opts_of(uint32_t f) { return Opts{f & (WC_OPT_TENSOR_TABLE | WC_OPT_RAW_FALLBACK | WC_OPT_CRC32)}; }
 
 void layout_of(uint32_t format, uint64_t n, wc_layout *out)
 {
@@ -46,6 +50,7 @@ void layout_of(uint32_t format, uint64_t n, wc_layout *out)
     out->payload_capacity = 0;
     if (c) out->payload_capacity = (c - 1) * cap(kChunk) + cap(n - (c - 1) * kChunk);
     out->scratch_bytes = 0;
+    out->crc_bytes = has_crc(format) ? 4 * c : 0;
 }
 
 // Encoder scratch: 8 bytes of meta per chunk, one slot per chunk plus a
@@ -84,14 +89,17 @@ wc_status check_plan(uint32_t format, const wc_segment *segs, uint32_t nseg, wc_
     total->seek_bytes = 8 * (chunks + 1);
     total->payload_capacity = cap;
     total->scratch_bytes = scratch_bytes_for(chunks, tt ? nseg : 0);
+    total->crc_bytes = has_crc(format) ? 4 * chunks : 0;
     return WC_OK;
 }
 
-wc_status check_buffers(const wc_buffers *b, uint64_t chunks, uint64_t raw_bytes, uint64_t table_bytes)
+wc_status check_buffers(const wc_buffers *b, uint64_t chunks, uint64_t raw_bytes, uint64_t table_bytes,
+                        uint64_t crc_bytes)
 {
     if (!b || !b->seek || !aligned(b->seek, 8)) return WC_ERR_ARG;
     if (table_bytes && (!b->tables || !aligned(b->tables, 16))) return WC_ERR_ARG;
     if (chunks == 0) return WC_OK;
+    if (crc_bytes && (!b->crc || !aligned(b->crc, 4))) return WC_ERR_ARG;
     if (!b->payload || !aligned(b->payload, 16)) return WC_ERR_ARG;
     if (raw_bytes && (!b->raw || !aligned(b->raw, 16))) return WC_ERR_ARG;
     return WC_OK;
@@ -142,6 +150,10 @@ wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, c
         hipLaunchKernelGGL(k_compact, dim3((uint32_t)chunks), dim3(256), 0, stream, slots, meta, out->seek,
                            out->payload, out->payload_bytes);
     }
+    if (chunks && opts.crc()) {
+        hipLaunchKernelGGL(k_crc32<false>, dim3((uint32_t)chunks), dim3(256), 0, stream, out->seek, out->payload,
+                           out->payload_bytes, out->crc, d_err);
+    }
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return WC_ERR_HIP;
     return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
@@ -186,6 +198,10 @@ wc_status decode_impl(const SegTable &st, uint64_t chunks, uint64_t n, const wc_
                       hipStream_t stream, Opts opts)
 {
     if (chunks == 0) return WC_OK;
+    if (opts.crc()) {
+        hipLaunchKernelGGL(k_crc32<true>, dim3((uint32_t)chunks), dim3(256), 0, stream, in->seek, in->payload,
+                           in->payload_bytes, in->crc, d_err);
+    }
     if (use_wide_refills(in->payload_bytes, n))
         launch_decode<DT, 2>(st, chunks, in, d_err, stream, opts);
     else
@@ -275,7 +291,7 @@ wc_status wc_encode(wc_format format, const void *d_in, uint64_t n, const wc_buf
     if (!valid_format(format) || n > kMaxElems) return WC_ERR_ARG;
     wc_layout lay;
     wc_query_layout(format, n, &lay);
-    wc_status s = check_buffers(out, lay.num_chunks, lay.raw_bytes, lay.table_bytes);
+    wc_status s = check_buffers(out, lay.num_chunks, lay.raw_bytes, lay.table_bytes, lay.crc_bytes);
     if (s != WC_OK) return s;
     if (n && (!d_in || !aligned(d_in, 16))) return WC_ERR_ARG;
     if (lay.num_chunks && (!d_scratch || !aligned(d_scratch, 256))) return WC_ERR_ARG;
@@ -291,7 +307,8 @@ wc_status wc_decode(wc_format format, const wc_buffers *in, uint64_t n, void *d_
     if (!valid_format(format) || n > kMaxElems) return WC_ERR_ARG;
     wc_layout lay;
     wc_query_layout(format, n, &lay);
-    wc_status s = check_buffers(in, lay.num_chunks, lay.raw_bytes, lay.num_chunks ? lay.table_bytes : 0);
+    wc_status s = check_buffers(in, lay.num_chunks, lay.raw_bytes, lay.num_chunks ? lay.table_bytes : 0,
+                                lay.crc_bytes);
     if (s != WC_OK) return s;
     if (n && (!d_out || !aligned(d_out, 16))) return WC_ERR_ARG;
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
@@ -307,7 +324,7 @@ wc_status wc_encode_batch(wc_format format, const wc_segment *h_segs, const wc_s
     wc_layout tot;
     wc_status s = check_plan(format, h_segs, nseg, &tot);
     if (s != WC_OK) return s;
-    s = check_buffers(out, tot.num_chunks, tot.raw_bytes, tot.table_bytes);
+    s = check_buffers(out, tot.num_chunks, tot.raw_bytes, tot.table_bytes, tot.crc_bytes);
     if (s != WC_OK) return s;
     if (tot.num_chunks && (!d_scratch || !aligned(d_scratch, 256))) return WC_ERR_ARG;
     if (scratch_bytes < tot.scratch_bytes) return WC_ERR_CAPACITY;
@@ -323,7 +340,7 @@ wc_status wc_decode_batch(wc_format format, const wc_segment *h_segs, const wc_s
     wc_layout tot;
     wc_status s = check_plan(format, h_segs, nseg, &tot);
     if (s != WC_OK) return s;
-    s = check_buffers(in, tot.num_chunks, tot.raw_bytes, tot.num_chunks ? tot.table_bytes : 0);
+    s = check_buffers(in, tot.num_chunks, tot.raw_bytes, tot.num_chunks ? tot.table_bytes : 0, tot.crc_bytes);
     if (s != WC_OK) return s;
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{d_segs, nseg, {0, 0, 0, 0}};

@@ -235,3 +235,57 @@ def test_wide_refills_with_uniform_chunks(dev, oracle_lib):
         x[k * 65536:(k + 1) * 65536] = (hi << 8) | g.integers(0, 256, 65536).astype(np.uint16)
     x = np.concatenate([x, _weights16("fp16", 77, 33)])
     _one("fp16", 0, x, dev, oracle_lib, "fp16 2402 chunks, uniform every fifth")
+
+
+def test_crc32_table(dev, oracle_lib):
+    """The CRC option: crc[k] equals the oracle's CRC-32 of chunk k's payload
+    (and zlib's), over chunks of every kind: weights, a raw one, a tail of 70
+    symbols, and a one-symbol chunk whose payload is the 128 bytes of states."""
+    import zlib
+    parts = [_weights16("bf16", 65536, 51), _uniform_chunk(52), _weights16("bf16", 3 * 65536, 53),
+             np.full(65536, 0x3F80, np.uint16), _uniform_chunk(54)[:70]]
+    x = np.concatenate(parts)
+    xt = _tensor("bf16", x, dev)
+    e = codec.encode(xt, raw_fallback=True, crc=True)
+    h = e.to_host()
+    want = oracle_lib.chunk_crc(h["seek"], h["payload"])
+    assert np.array_equal(h["crc"], want)
+    for k in (0, 1, 6):
+        assert int(h["crc"][k]) == zlib.crc32(h["payload"][int(h["seek"][k]):int(h["seek"][k + 1])].tobytes())
+    y = codec.decode(e)
+    assert torch.equal(y.view(torch.int16).cpu(), xt.view(torch.int16).cpu())
+
+
+def test_crc32_detects_a_flipped_byte(dev, oracle_lib):
+    x = _weights16("bf16", 5 * 65536 + 9, 55)
+    o = oracle_lib.encode(x, "bf16", opts=RF)
+    crc = oracle_lib.chunk_crc(o.seek, o.payload)
+    for k in (0, 3, 5):
+        bad = o.payload.copy()
+        pos = int(o.seek[k]) + (int(o.seek[k + 1] - o.seek[k]) // 2 & ~3) + 1
+        bad[pos] ^= 0x10
+        e = _upload(oracle_lib.Encoded(o.dtype, o.n, o.raw, o.tables, o.seek, bad, RF), "bf16", RF | 0x400, dev)
+        e.crc = torch.from_numpy(crc.view(np.int32)).to(dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        out = torch.empty(x.size, dtype=torch.int16, device=dev)
+        B.wc_decode(e.fmt, e.buffers(), e.n, out, err)
+        torch.cuda.synchronize()
+        assert int(err.item()) & B.EF_BAD_CRC, k
+    good = _upload(o, "bf16", RF | 0x400, dev)
+    good.crc = torch.from_numpy(crc.view(np.int32)).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty(x.size, dtype=torch.int16, device=dev)
+    B.wc_decode(good.fmt, good.buffers(), good.n, out, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), x)
+
+
+def test_crc32_batch(dev, oracle_lib):
+    xs = [_weights16("bf16", n, 60 + i) for i, n in enumerate([70000, 0, 65536, 3, 2 * 65536])]
+    ts = [_tensor("bf16", x, dev) for x in xs]
+    e = codec.encode_batch(ts, crc=True, tensor_table=True)
+    seek = e.seek.cpu().numpy().view(np.uint64)
+    assert np.array_equal(e.crc.cpu().numpy().view(np.uint32), oracle_lib.chunk_crc(seek, e.payload.cpu().numpy()))
+    for x, y in zip(xs, codec.decode_batch(e)):
+        assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), x)

@@ -65,7 +65,7 @@ def test_plan_batch_matches_oracle(L, oracle_lib):
 
 
 FORMATS = [(lay, opts) for lay in ("bf16", "bf16r", "fp16", "fp16r", "fp32", "fp8e4m3", "fp8e5m2")
-           for opts in (0, 0x100, 0x200, 0x300)]
+           for opts in (0, 0x100, 0x200, 0x300, 0x700)]
 
 
 @pytest.mark.parametrize("lay,opts", FORMATS)
@@ -78,6 +78,7 @@ def test_variant_layouts_match_oracle(L, oracle_lib, lay, opts, n):
     c = a["num_chunks"]
     hist = 2048 if (opts & 0x100) and c else 0
     assert a["scratch_bytes"] == (0 if c == 0 else ((8 * c + 255) // 256) * 256 + (c + 1) * 131200 + hist)
+    assert a["crc_bytes"] == (4 * c if opts & 0x400 else 0)
 
 
 @pytest.mark.parametrize("lay,opts", FORMATS)
@@ -92,7 +93,7 @@ def test_variant_plan_batch_matches_oracle(L, oracle_lib, lay, opts):
 
 
 def test_bad_format_words_are_rejected(L):
-    for f in (7, 0xFF, 0x400, 0x10000, 0x80000000):
+    for f in (7, 0xFF, 0x800, 0x10000, 0x80000000):
         with pytest.raises(B.WcError):
             wc.wc_query_layout(f, 100)
         assert L.wc_query_layout(f, 100, ctypes.byref(B.wc_layout())) == B.WC_ERR_ARG
