@@ -42,6 +42,7 @@ def parse():
                         "fp8* as FP8 scaled per tensor)")
     p.add_argument("--tensor-table", action="store_true", help="one frequency table per tensor")
     p.add_argument("--raw-fallback", action="store_true", help="store chunks that do not shrink raw")
+    p.add_argument("--crc", action="store_true", help="a CRC-32 per chunk, written by encode, checked by decode")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU work for the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -218,7 +219,8 @@ def main():
         w = S.with_dtype(w, layout)
     elif (layout == "fp32") != (w.dtype == "fp32"):
         raise SystemExit(f"layout {layout} does not fit the {w.dtype} set {w.name}")
-    opts = (B.WC_OPT_TENSOR_TABLE if args.tensor_table else 0) | (B.WC_OPT_RAW_FALLBACK if args.raw_fallback else 0)
+    opts = ((B.WC_OPT_TENSOR_TABLE if args.tensor_table else 0) | (B.WC_OPT_RAW_FALLBACK if args.raw_fallback else 0)
+            | (B.WC_OPT_CRC32 if args.crc else 0))
     fmt = B.format_word(layout) | opts
     log(f"[bench] generating {w.name}: {len(w.shapes)} tensors, {w.n} elements")
     t0 = time.perf_counter()
@@ -243,7 +245,8 @@ def main():
     payload = torch.empty(tot.payload_capacity, dtype=torch.uint8, device=dev)
     scratch = torch.empty(tot.scratch_bytes, dtype=torch.uint8, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    enc_bufs = B.make_buffers(raw, tables, seek, payload, tot.payload_capacity)
+    crc = torch.empty(max(int(tot.num_chunks), 1), dtype=torch.int32, device=dev) if args.crc else None
+    enc_bufs = B.make_buffers(raw, tables, seek, payload, tot.payload_capacity, crc)
     stream = torch.cuda.current_stream()
     C = int(tot.num_chunks)
     n = int(tot.n)
@@ -259,7 +262,7 @@ def main():
                           stream, sev)
         if sev is not None:
             sev.record(5, stream)
-        dec_bufs = B.make_buffers(raw, tables, seek, payload, payload_bytes)
+        dec_bufs = B.make_buffers(raw, tables, seek, payload, payload_bytes, crc)
         B.wc_decode_batch(fmt, h_out, d_out, len(outs), dec_bufs, err, stream)
         if sev is not None:
             sev.record(6, stream)
@@ -281,7 +284,7 @@ def main():
         checked = True
         log("[bench] round trip bit-exact")
     table_bytes = int(tot.table_bytes)
-    compressed = int(tot.raw_bytes + table_bytes + seek.numel() * 8 + payload_bytes)
+    compressed = int(tot.raw_bytes + table_bytes + seek.numel() * 8 + payload_bytes + tot.crc_bytes)
     ratio = compressed / raw_in_bytes
 
     # timed region
@@ -345,7 +348,7 @@ def main():
         "config": {"workload": w.name, "tensors": len(w.shapes), "elements": n,
                    "raw_bytes": raw_in_bytes, "chunks": C, "weights": w.dtype,
                    "layout": layout, "tensor_table": bool(args.tensor_table),
-                   "raw_fallback": bool(args.raw_fallback)},
+                   "raw_fallback": bool(args.raw_fallback), "crc32": bool(args.crc)},
         "ratio": round(ratio, 5),
         "round_trip_bit_exact": checked,
         "encode_GBps": round(raw_in_bytes / (enc_ms / 1e3) / 1e9, 3),
@@ -361,7 +364,7 @@ def main():
     # evicts the 256 MB Infinity Cache and the L2s)
     if args.cold_reps > 0:
         flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
-        dec_bufs = B.make_buffers(raw, tables, seek, payload, payload_bytes)
+        dec_bufs = B.make_buffers(raw, tables, seek, payload, payload_bytes, crc)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         warm, cold = [], []
         for mode in ("warm", "cold"):
