@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.wco_crc32.argtypes = [P, U64]
         L.wco_crc32.restype = U32
         L.wco_chunk_crc.argtypes = [P, P, U64, P]
+        L.wco_tile_order.argtypes = [P, P, U32, U32, I]
+        L.wco_gemm_bf16.argtypes = [P, P, U32, U32, U32, P, P]
         L.wco_merge_fp8.argtypes = [I, P, P, U64, P]
         L.wco_merge_u16.argtypes = [I, P, P, U64, P]
         L.wco_encode_chunk.argtypes = [P, U32, P, P]
@@ -264,6 +266,44 @@ def chunk_crc(seek: np.ndarray, payload: np.ndarray) -> np.ndarray:
     out = np.zeros(max(seek.size - 1, 1), np.uint32)
     lib().wco_chunk_crc(_p(seek), _p(pay), seek.size - 1, _p(out))
     return out[: seek.size - 1]
+
+
+# -------------------------------------------------- tile order and GEMM
+
+def tile_order(w: np.ndarray, inverse: bool = False, shape=None) -> np.ndarray:
+    """The tile order of a rows x cols matrix of 16-bit patterns (flat
+    result), or with inverse the matrix (shape = (rows, cols)) from its
+    tile-ordered values.  Order defined in wc_oracle.c (wco_tile_order)."""
+    if inverse:
+        rows, cols = shape
+        src = np.ascontiguousarray(w, np.uint16).reshape(-1)
+    else:
+        rows, cols = w.shape
+        src = np.ascontiguousarray(w, np.uint16).reshape(-1)
+    if src.size != rows * cols:
+        raise ValueError("size does not match the shape")
+    out = np.empty(rows * cols, np.uint16)
+    if src.size:
+        rc = lib().wco_tile_order(_p(src), _p(out), rows, cols, 1 if inverse else 0)
+        if rc != OK:
+            raise ValueError(f"tile order needs rows and cols that are multiples of 16, got {rows} x {cols}")
+    return out.reshape(rows, cols) if inverse else out
+
+
+def gemm_bf16(x: np.ndarray, w: np.ndarray, magnitude: bool = False):
+    """x W^T in double from BF16 bit patterns (x: m x k, w: n x k); with
+    magnitude also the sums of |x_t w_t| (for rounding-error bounds)."""
+    x = np.ascontiguousarray(x, np.uint16)
+    w = np.ascontiguousarray(w, np.uint16)
+    m, k = x.shape
+    n, k2 = w.shape
+    if k != k2:
+        raise ValueError("inner dimensions differ")
+    y = np.zeros((m, n), np.float64)
+    mag = np.zeros((m, n), np.float64)
+    if y.size and k:
+        lib().wco_gemm_bf16(_p(x), _p(w), m, n, k, _p(y), _p(mag))
+    return (y, mag) if magnitude else y
 
 
 # ------------------------------------------------------------ whole tensor

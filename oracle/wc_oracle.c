@@ -474,6 +474,60 @@ void wco_chunk_crc(const uint64_t *seek, const uint8_t *payload, uint64_t chunks
     for (uint64_t k = 0; k < chunks; k++) crc[k] = wco_crc32(payload + seek[k], seek[k + 1] - seek[k]);
 }
 
+/* ------------------------------------------------- tile order and GEMM */
+
+/* Tile order of a rows x cols matrix (row-major, both multiples of 16): the
+ * matrix is cut into 16 x 16 tiles, panel by panel (panel p = rows 16p ..
+ * 16p+15; within it tile b = columns 16b .. 16b+15), each tile written as
+ * 256 values; value e of a tile (l = e / 8, i = e % 8) is the element at row
+ * l % 16 and column 4 (l / 16) + 8 (i / 4) + i % 4 of the tile.  This is not
+ * from the pages: it is the GPU library's own order for decoding straight
+ * into matrix-core operands, defined here element by element so that the
+ * tests can check the GPU's permutation and the bytes encoded after it. */
+int wco_tile_order(const uint16_t *in, uint16_t *out, uint32_t rows, uint32_t cols, int inverse)
+{
+    if (rows % 16 || cols % 16) return WCO_ERR_ARG;
+    uint64_t s = 0;
+    for (uint32_t p = 0; p < rows / 16; p++)
+        for (uint32_t b = 0; b < cols / 16; b++)
+            for (uint32_t e = 0; e < 256; e++, s++) {
+                const uint32_t l = e / 8, i = e % 8;
+                const uint64_t r = 16ull * p + l % 16;
+                const uint64_t c = 16ull * b + 4 * (l / 16) + 8 * (i / 4) + i % 4;
+                if (inverse) out[r * cols + c] = in[s];
+                else out[s] = in[r * cols + c];
+            }
+    return WCO_OK;
+}
+
+/* A BF16 bit pattern is the high half of an IEEE single. */
+static double bf16_value(uint16_t b)
+{
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* y[i][j] = sum over t of x[i][t] w[j][t] (x: m x k, w: n x k, BF16 bit
+ * patterns, row-major) in double; each product of two BF16 values is exact
+ * in double.  If mag is not NULL, mag[i][j] = sum of |x[i][t] w[j][t]|. */
+void wco_gemm_bf16(const uint16_t *x, const uint16_t *w, uint32_t m, uint32_t n, uint32_t k, double *y,
+                   double *mag)
+{
+    for (uint32_t i = 0; i < m; i++)
+        for (uint32_t j = 0; j < n; j++) {
+            double acc = 0.0, a = 0.0;
+            for (uint32_t t = 0; t < k; t++) {
+                const double p = bf16_value(x[(uint64_t)i * k + t]) * bf16_value(w[(uint64_t)j * k + t]);
+                acc += p;
+                a += p < 0 ? -p : p;
+            }
+            y[(uint64_t)i * n + j] = acc;
+            if (mag) mag[(uint64_t)i * n + j] = a;
+        }
+}
+
 /* ------------------------------------------------------------ whole tensor */
 
 typedef struct {

@@ -106,6 +106,15 @@ uint32_t wco_crc32(const uint8_t *p, uint64_t n);
 /* crc[k] = wco_crc32 of chunk k's payload bytes [seek[k], seek[k+1]). */
 void wco_chunk_crc(const uint64_t *seek, const uint8_t *payload, uint64_t chunks, uint32_t *crc);
 
+/* Tile order of a rows x cols matrix of 16-bit values and its inverse (see
+ * wc_oracle.c); WCO_ERR_ARG unless both are multiples of 16. */
+int wco_tile_order(const uint16_t *in, uint16_t *out, uint32_t rows, uint32_t cols, int inverse);
+
+/* x W^T in double from BF16 patterns (x: m x k, w: n x k); mag (optional)
+ * receives the sums of |products|. */
+void wco_gemm_bf16(const uint16_t *x, const uint16_t *w, uint32_t m, uint32_t n, uint32_t k, double *y,
+                   double *mag);
+
 /* Whole tensor.  threads <= 1 runs on the calling thread; otherwise chunks
  * are split into contiguous ranges over that many POSIX threads. */
 int wco_encode(int dtype, const void *in, uint64_t n, uint8_t *raw, uint16_t *tables,
