@@ -160,6 +160,16 @@ typedef struct {
     uint64_t raw_base;
 } wc_segment;
 
+/* One weight matrix of a fused decode + GEMM batch (wc_decode_gemm_batch).
+ * Its segment holds W (rows x cols BF16) encoded in tile order (see
+ * wc_tile_order); the call adds X W^T into Y. */
+typedef struct {
+    uint64_t x;     /* device address of X: m x cols BF16, row-major, 8-byte aligned */
+    uint64_t y;     /* device address of Y: m x rows fp32, row-major, 4-byte aligned */
+    uint32_t rows;  /* N: rows of W (output features), a multiple of 16 */
+    uint32_t cols;  /* K: columns of W (input features), a multiple of 16 */
+} wc_gemm;
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 int wc_version(void);
 
@@ -201,6 +211,39 @@ wc_status wc_encode_batch(wc_format format, const wc_segment *h_segs, const wc_s
 wc_status wc_decode_batch(wc_format format, const wc_segment *h_segs, const wc_segment *d_segs,
                           uint32_t nseg, const wc_buffers *in, uint32_t *d_err,
                           hipStream_t stream);
+
+/* Tile order of a BF16 (or any 16-bit) matrix W of rows x cols elements,
+ * both multiples of 16 (rows * cols < 2^32): 16 x 16 tiles, panel-major
+ * (panel p = rows 16p..16p+15; tile t = p * cols/16 + b covers its columns
+ * 16b..16b+15), 256 elements per tile, position e of tile (p, b) holding
+ * W[16p + (e/8) % 16][16b + 4 ((e/8) / 16) + 8 ((e%8) / 4) + (e%8) % 4].
+ * The order is this library's own (a layout transform in the sense of the
+ * PTWM docs' Reshape transform): it makes one decoded group of 256 symbols
+ * one tile in the matrix cores' operand order.  inverse = 0: d_in is W
+ * row-major, d_out the tile stream; inverse = 1: the reverse.  Both buffers
+ * 16-byte aligned, rows * cols u16 each, not overlapping.  Enqueued on
+ * `stream`; argument errors return WC_ERR_ARG. */
+wc_status wc_tile_order(const void *d_in, void *d_out, uint32_t rows, uint32_t cols, int inverse,
+                        hipStream_t stream);
+
+/* Decode fused with its consumer (the Split12 README's serving kernels: the
+ * compressed weights are the only copy in HBM).  For every segment i (BF16
+ * or BF16_REORDER layout, encoded from wc_tile_order's stream of a
+ * gemm[i].rows x gemm[i].cols matrix W_i, so segs[i].n = rows * cols):
+ * Y_i += X_i W_i^T, X_i with m rows (1 <= m <= 64), products of BF16 values
+ * summed in fp32 (matrix-core MFMA per 16 x 16 x 16 block, then fp32 adds in
+ * an unspecified order: results are not bitwise reproducible).  No decoded W
+ * is written.  h_gemm / d_gemm: host and device copies of the nseg
+ * descriptors.  Y must be initialised by the caller (zeros for Y = X W^T).
+ * WC_OPT_TENSOR_TABLE and WC_OPT_CRC32 are honoured (the CRC is checked
+ * first); WC_OPT_RAW_FALLBACK is rejected (WC_ERR_ARG), as are a chunk that
+ * touches more panels of 16 rows than the kernel holds accumulators for
+ * (8 / ceil(m/16) rounded down to 2, 4 or 8; cols = 2048 or cols >= 4096
+ * never needs more than 2).  Data errors
+ * set WC_EF_* bits as in wc_decode_batch; Y is then undefined. */
+wc_status wc_decode_gemm_batch(wc_format format, const wc_segment *h_segs, const wc_segment *d_segs, uint32_t nseg,
+                               const wc_gemm *h_gemm, const wc_gemm *d_gemm, uint32_t m, const wc_buffers *in,
+                               uint32_t *d_err, hipStream_t stream);
 
 /* Host-side self check of the exact division by reciprocal that the encoder
  * kernel uses (same inline code, compiled for the CPU): every divisor

@@ -36,7 +36,8 @@ EF_NAMES = {EF_BAD_TABLE: "bad table", EF_WORD_OVERRUN: "word overrun",
 CHUNK = 65536
 
 EXPORTS = ["wc_version", "wc_status_string", "wc_query_layout", "wc_plan_batch", "wc_encode",
-           "wc_decode", "wc_encode_batch", "wc_decode_batch", "wc_check_division"]
+           "wc_decode", "wc_encode_batch", "wc_decode_batch", "wc_check_division", "wc_tile_order",
+           "wc_decode_gemm_batch"]
 
 
 class WcError(RuntimeError):
@@ -63,6 +64,11 @@ class wc_segment(ctypes.Structure):
                 ("raw_base", ctypes.c_uint64)]
 
 
+class wc_gemm(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_uint64), ("y", ctypes.c_uint64), ("rows", ctypes.c_uint32),
+                ("cols", ctypes.c_uint32)]
+
+
 _lib = None
 
 
@@ -87,8 +93,10 @@ def lib() -> ctypes.CDLL:
     L.wc_decode_batch.argtypes = [I, P, P, U32, ctypes.POINTER(wc_buffers), P, P]
     L.wc_check_division.argtypes = [U32]
     L.wc_check_division.restype = U64
+    L.wc_tile_order.argtypes = [P, P, U32, U32, I, P]
+    L.wc_decode_gemm_batch.argtypes = [I, P, P, U32, P, P, U32, ctypes.POINTER(wc_buffers), P, P]
     for name in ("wc_query_layout", "wc_plan_batch", "wc_encode", "wc_decode", "wc_encode_batch",
-                 "wc_decode_batch"):
+                 "wc_decode_batch", "wc_tile_order", "wc_decode_gemm_batch"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -191,6 +199,19 @@ def wc_decode_batch(dtype, h_segs, d_segs, nseg: int, bufs: wc_buffers, d_err=No
     rc = lib().wc_decode_batch(_code(dtype), ctypes.cast(h_segs, ctypes.c_void_p), _ptr(d_segs),
                                int(nseg), ctypes.byref(bufs), _ptr(d_err), _stream(stream))
     _check(rc, "wc_decode_batch")
+
+
+def wc_tile_order(d_in, d_out, rows: int, cols: int, inverse: bool = False, stream=None):
+    rc = lib().wc_tile_order(_ptr(d_in), _ptr(d_out), int(rows), int(cols), 1 if inverse else 0, _stream(stream))
+    _check(rc, "wc_tile_order")
+
+
+def wc_decode_gemm_batch(dtype, h_segs, d_segs, nseg: int, h_gemm, d_gemm, m: int, bufs: wc_buffers, d_err=None,
+                         stream=None):
+    rc = lib().wc_decode_gemm_batch(_code(dtype), ctypes.cast(h_segs, ctypes.c_void_p), _ptr(d_segs), int(nseg),
+                                    ctypes.cast(h_gemm, ctypes.c_void_p), _ptr(d_gemm), int(m), ctypes.byref(bufs),
+                                    _ptr(d_err), _stream(stream))
+    _check(rc, "wc_decode_gemm_batch")
 
 
 def wc_check_division(samples_per_divisor: int = 256) -> int:

@@ -453,18 +453,29 @@ __device__ inline void build_table(Sh &sh, uint32_t h, uint32_t lane, const uint
     }
 }
 
-// kH = 1: one chunk per wavefront (32 lanes; the wide table's variant, so
-// a lone wavefront's serial chain has no per-half selects).  kH = 2: two
-// chunks per wavefront; with an odd chunk count the last wavefront's second
-// half shadows the first half's chunk (same unchecked code, nothing stored).
-template <int DT, bool kL1, int kH, int kB>
-__global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *__restrict__ raw,
-                                                    const uint16_t *__restrict__ tables,
-                                                    const uint64_t *__restrict__ seek,
-                                                    const uint8_t *__restrict__ payload,
-                                                    uint64_t payload_bytes, uint64_t total_chunks,
-                                                    uint32_t *err, Opts opts)
+// Views of a decoded group.  A view has fetch / flush (full groups) and
+// fetch_checked / flush_checked (groups a half may only partly own), and a
+// constexpr kWave: false for the store views above, whose calls are made by
+// the halves that write output only; true for a view whose flush is a
+// wave-wide operation (it exchanges data between the halves), which is then
+// called by both halves always and judges ownership itself; such a view
+// also has reset() (before a chunk is decoded again) and finish() (after
+// the last group).
+template <typename V, typename = void>
+struct is_wave_view : std::false_type {};
+template <typename V>
+struct is_wave_view<V, std::void_t<decltype(V::kWave)>> : std::integral_constant<bool, V::kWave> {};
+
+// The decoder for one wavefront (see k_decode).  make_view(sg, sidx, k,
+// start, len, put) builds the view of the half's chunk once its segment and
+// validity are known.
+template <int DT, bool kL1, int kH, int kB, typename View, typename MakeView>
+__device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restrict__ tables,
+                                            const uint64_t *__restrict__ seek,
+                                            const uint8_t *__restrict__ payload, uint64_t payload_bytes,
+                                            uint64_t total_chunks, uint32_t *err, Opts opts, MakeView make_view)
 {
+    constexpr bool kWave = is_wave_view<View>::value;
     using Sh = typename std::conditional<kL1, DecSharedL1<kH, kB>, DecSharedL2<kH, kB>>::type;
     constexpr uint32_t kRingWords = Sh::kRingWords;
     __shared__ Sh sh;
@@ -531,10 +542,9 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     refill_sync<kB>(cs, lane, ok, sh.ring[h]);
     __syncthreads();
 
-    RawView<DT> rv;
-    rv.init(raw, sg, start);
     const uint2 *stage = reinterpret_cast<const uint2 *>(&sh.stage[h][0]);
     const bool put = ok && real;  // this half writes output
+    View rv = make_view(sg, sidx, k, start, ok ? len : 0u, put);
 
     // Groups of 8 steps, first to last.  Groups where every lane of every
     // half is active (and every table valid) run unchecked; the partial last
@@ -546,7 +556,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     // equal in every lane; read as scalars so the group loops are uniform
     const uint32_t ng = __builtin_amdgcn_readfirstlane((hi_len + kGroupWords - 1) / kGroupWords);
     const uint32_t nfull = __builtin_amdgcn_readfirstlane(lo_len / kGroupWords);
-    using Pre = typename RawView<DT>::Pre;
+    using Pre = typename View::Pre;
     uint32_t b0 = h, b1 = 0, hs = 32 * h;
     if constexpr (!kL1) {
         b0 = h << 12;
@@ -566,7 +576,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         next = refill_issue<kB>(cs, lane, ok && refills);
         // the value loaded for a group past the last is never used
         const uint32_t gn = gg + 2 <= g_last ? gg + 2 : g_last;
-        if constexpr (CHECK) ahead = put ? rv.fetch_checked(kGroupWords * gn + 8 * lane, len) : Pre{};
+        if constexpr (CHECK) ahead = put || kWave ? rv.fetch_checked(kGroupWords * gn + 8 * lane, len) : Pre{};
         else ahead = rv.fetch(kGroupWords * gn + 8 * lane);
         const uint32_t landed = cs.land, r0 = rpos;
         wave_lds_order();
@@ -579,7 +589,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         // unconditional in full groups, so the compiler counts memory
         // operations exactly: a shadow half writes what its sibling does
         if constexpr (CHECK) {
-            if (put) rv.flush_checked(kGroupWords * gg + 8 * lane, stage[lane], cur, len);
+            if (put || kWave) rv.flush_checked(kGroupWords * gg + 8 * lane, stage[lane], cur, len);
         } else {
             rv.flush(kGroupWords * gg + 8 * lane, stage[lane], cur);
         }
@@ -666,7 +676,7 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     refill_commit<kB>(cs, q1, sh.ring[h]);
     refill_commit<kB>(cs, q2, sh.ring[h]);
     for (uint32_t g = n3; g < ng; g++) {
-        Pre cur = put ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
+        Pre cur = put || kWave ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
         Pre dummy;
         group(std::true_type{}, g, g, cur, dummy, q0, q0);
     }
@@ -674,13 +684,14 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
     // every group checked and preceded by a synchronous fill, and its
     // output written again.
     if (__ballot(overrun)) {
+        if constexpr (kWave) rv.reset();
         refill_commit<kB>(cs, q0, sh.ring[h]);
         cs.ptr = cs.fill = cs.land = cs.fpos = 0;
         rpos = 0;
         if (ok) x = reinterpret_cast<const WC_GLOBAL uint32_t *>(cs.base)[lane];
         for (uint32_t g = 0; g < ng; g++) {
             refill_sync<kB>(cs, lane, ok, sh.ring[h]);
-            Pre cur = put ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
+            Pre cur = put || kWave ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
             Pre dummy;
             Refill none = refill_none();
             group(std::true_type{}, g, g, cur, dummy, none, none, false);
@@ -698,9 +709,31 @@ __global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *
         }
         if (x != kL) bits |= WC_EF_BAD_FINAL_STATE;
     }
+    if constexpr (kWave) rv.finish();
     // OR the half's bits into lane 0 of the half; a shadow half reports nothing
     for (int o = 16; o > 0; o >>= 1) bits |= __shfl_xor(bits, o, 32);
     if (lane == 0 && bits && real && err) atomicOr(err, bits);
+}
+
+// kH = 1: one chunk per wavefront (32 lanes; the wide table's variant, so
+// a lone wavefront's serial chain has no per-half selects).  kH = 2: two
+// chunks per wavefront; with an odd chunk count the last wavefront's second
+// half shadows the first half's chunk (same unchecked code, nothing stored).
+template <int DT, bool kL1, int kH, int kB>
+__global__ __launch_bounds__(32 * kH) void k_decode(SegTable st, const uint8_t *__restrict__ raw,
+                                                    const uint16_t *__restrict__ tables,
+                                                    const uint64_t *__restrict__ seek,
+                                                    const uint8_t *__restrict__ payload,
+                                                    uint64_t payload_bytes, uint64_t total_chunks,
+                                                    uint32_t *err, Opts opts)
+{
+    decode_wave<DT, kL1, kH, kB, RawView<DT>>(
+        st, tables, seek, payload, payload_bytes, total_chunks, err, opts,
+        [&](const wc_segment &sg, uint32_t, uint64_t, uint64_t start, uint32_t, bool) {
+            RawView<DT> rv;
+            rv.init(raw, sg, start);
+            return rv;
+        });
 }
 
 // Chunks stored raw (WC_OPT_RAW_FALLBACK), after k_decode (which skips

@@ -6,6 +6,8 @@
 //           CRC-32 option: k_crc32 after the compaction)
 //   decode: k_decode (then k_decode_raw for chunks stored raw; CRC-32 option:
 //           k_crc32 check before)
+//   decode + GEMM: k_decode_gemm (CRC-32 option: k_crc32 check before);
+//           tile order: k_tile_order
 // on the caller's stream.  No allocation, no synchronisation, no global state.
 #include <hip/hip_runtime.h>
 
@@ -17,12 +19,13 @@
 #include "wc_crc.hpp"
 #include "wc_decode.hpp"
 #include "wc_encode.hpp"
+#include "wc_gemm.hpp"
 
 using namespace wc;
 
 namespace {
 
-constexpr int kVersion = 10100;  // 1.1.0: format variants
+constexpr int kVersion = 10200;  // 1.2.0: format variants, CRC-32, fused decode + GEMM
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -244,6 +247,41 @@ wc_status decode_any(uint32_t format, const SegTable &st, uint64_t chunks, uint6
     }
 }
 
+// Most panels (16-row blocks of W) one chunk of a tile-ordered rows x cols
+// matrix touches.
+uint32_t panels_per_chunk(uint64_t n, uint32_t cols)
+{
+    const uint64_t tpp = cols / 16, tiles = n / 256;
+    uint32_t most = 0;
+    for (uint64_t t0 = 0; t0 < tiles; t0 += 256) {
+        const uint64_t t1 = (t0 + 256 < tiles ? t0 + 256 : tiles) - 1;
+        const uint32_t p = (uint32_t)(t1 / tpp - t0 / tpp + 1);
+        most = p > most ? p : most;
+    }
+    return most;
+}
+
+template <int DT, int MT, int P>
+void launch_gemm(const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err, hipStream_t stream,
+                 Opts opts, const wc_gemm *d_gemm, uint32_t m)
+{
+    hipLaunchKernelGGL((k_decode_gemm<DT, MT, P>), dim3((uint32_t)((chunks + 1) / 2)), dim3(64), 0, stream, st,
+                       in->raw, in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts, d_gemm, m);
+}
+
+template <int DT>
+bool launch_gemm_any(uint32_t mt, uint32_t p, const SegTable &st, uint64_t chunks, const wc_buffers *in,
+                     uint32_t *d_err, hipStream_t stream, Opts opts, const wc_gemm *d_gemm, uint32_t m)
+{
+    if (mt == 1 && p <= 2) launch_gemm<DT, 1, 2>(st, chunks, in, d_err, stream, opts, d_gemm, m);
+    else if (mt == 1 && p <= 8) launch_gemm<DT, 1, 8>(st, chunks, in, d_err, stream, opts, d_gemm, m);
+    else if (mt == 2 && p <= 2) launch_gemm<DT, 2, 2>(st, chunks, in, d_err, stream, opts, d_gemm, m);
+    else if (mt == 2 && p <= 4) launch_gemm<DT, 2, 4>(st, chunks, in, d_err, stream, opts, d_gemm, m);
+    else if (mt == 4 && p <= 2) launch_gemm<DT, 4, 2>(st, chunks, in, d_err, stream, opts, d_gemm, m);
+    else return false;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,6 +383,62 @@ wc_status wc_decode_batch(wc_format format, const wc_segment *h_segs, const wc_s
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{d_segs, nseg, {0, 0, 0, 0}};
     return decode_any(format, st, tot.num_chunks, tot.n, in, d_err, stream);
+}
+
+wc_status wc_tile_order(const void *d_in, void *d_out, uint32_t rows, uint32_t cols, int inverse, hipStream_t stream)
+{
+    const uint64_t n = (uint64_t)rows * cols;
+    if ((rows % 16) || (cols % 16) || n >= (1ull << 32)) return WC_ERR_ARG;
+    if (n == 0) return WC_OK;
+    if (!d_in || !d_out || !aligned(d_in, 16) || !aligned(d_out, 16)) return WC_ERR_ARG;
+    const char *a = static_cast<const char *>(d_in), *b = static_cast<const char *>(d_out);
+    if (a < b + 2 * n && b < a + 2 * n) return WC_ERR_ARG;  // overlapping
+    const uint64_t threads = n / 8;
+    hipLaunchKernelGGL(k_tile_order, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(d_in), static_cast<uint16_t *>(d_out), rows, cols,
+                       inverse ? 1u : 0u);
+    return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
+}
+
+wc_status wc_decode_gemm_batch(wc_format format, const wc_segment *h_segs, const wc_segment *d_segs, uint32_t nseg,
+                               const wc_gemm *h_gemm, const wc_gemm *d_gemm, uint32_t m, const wc_buffers *in,
+                               uint32_t *d_err, hipStream_t stream)
+{
+    if (!valid_format(format) || nseg == 0 || !h_segs || !d_segs || !aligned(d_segs, 8)) return WC_ERR_ARG;
+    const int lay = layout_code(format);
+    if ((lay != WC_BF16 && lay != WC_BF16_REORDER) || opts_of(format).raw_fallback()) return WC_ERR_ARG;
+    if (!h_gemm || !d_gemm || !aligned(d_gemm, 8) || m < 1 || m > 64) return WC_ERR_ARG;
+    wc_layout tot;
+    wc_status s = check_plan(format, h_segs, nseg, &tot, false);  // segment ptr unused
+    if (s != WC_OK) return s;
+    s = check_buffers(in, tot.num_chunks, tot.raw_bytes, tot.num_chunks ? tot.table_bytes : 0, tot.crc_bytes);
+    if (s != WC_OK) return s;
+    if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
+    const uint32_t mt = m <= 16 ? 1 : m <= 32 ? 2 : 4;
+    uint32_t most = 0;
+    for (uint32_t i = 0; i < nseg; i++) {
+        const wc_gemm &g = h_gemm[i];
+        const uint64_t n = (uint64_t)g.rows * g.cols;
+        if ((g.rows % 16) || (g.cols % 16) || n != h_segs[i].n || n >= (1ull << 32)) return WC_ERR_ARG;
+        if (n && (!g.x || !g.y || (g.x % 8) || (g.y % 4))) return WC_ERR_ARG;
+        if (n) {
+            const uint32_t p = panels_per_chunk(n, g.cols);
+            most = p > most ? p : most;
+        }
+    }
+    if (tot.num_chunks == 0) return WC_OK;
+    SegTable st{d_segs, nseg, {0, 0, 0, 0}};
+    const Opts o = opts_of(format);
+    if (o.crc()) {
+        hipLaunchKernelGGL(k_crc32<true>, dim3((uint32_t)tot.num_chunks), dim3(256), 0, stream, in->seek,
+                           in->payload, in->payload_bytes, in->crc, d_err);
+    }
+    const bool ok = lay == WC_BF16 ? launch_gemm_any<WC_BF16>(mt, most, st, tot.num_chunks, in, d_err, stream, o,
+                                                              d_gemm, m)
+                                   : launch_gemm_any<WC_BF16_REORDER>(mt, most, st, tot.num_chunks, in, d_err,
+                                                                      stream, o, d_gemm, m);
+    if (!ok) return WC_ERR_ARG;
+    return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 
 uint64_t wc_check_division(uint32_t samples_per_divisor)
