@@ -7,6 +7,12 @@ encode, seek-table scan, compaction) followed by batched fused decode back to
 BF16.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+With --fused-gemm M it measures instead the decode fused with its consumer
+(Y += X W^T from the compressed weights, M rows of X) against torch's BF16
+batched GEMM on the uncompressed weights and against decode-then-GEMM, on
+the expert down projections of the MoE set by default, and prints that
+line.
 """
 from __future__ import annotations
 
@@ -50,6 +56,8 @@ def parse():
     p.add_argument("--cold-reps", type=int, default=5,
                    help="decode-only repetitions after a 1 GiB write that evicts the Infinity Cache and L2 "
                         "(and as many back-to-back warm ones); 0 skips both")
+    p.add_argument("--fused-gemm", type=int, default=0, metavar="M",
+                   help="measure the fused decode + GEMM with M rows of X (default set moe-w2-bf16)")
     p.add_argument("--copy-ref", action="store_true",
                    help="after timing, launch one plain device copy of 256 MiB (read 256 MiB, write 256 MiB): "
                         "the reference for scaling hardware byte counters taken over this run")
@@ -197,6 +205,178 @@ def coded_plane_entropy(xs, tables, seek, layout, tensor_table, max_chunks=4096)
             "chunks_sampled": -(-C // stride), "chunk_stride": stride}
 
 
+def fused_gemm_main(args):
+    """Decode fused with its consumer against BF16 GEMM and decode-then-GEMM."""
+    import torch
+    import lossless_weight_compression_bf16_amd as wc
+    from lossless_weight_compression_bf16_amd import _binding as B, codec, gemm as G, synthetic as S
+
+    wc.lib()
+    dev = torch.device("cuda:0")
+    name = "moe-w2-bf16" if args.workload == DEFAULT_WORKLOAD else args.workload
+    w = S.workload(name)
+    if w.dtype != "bf16":
+        raise SystemExit("the fused decode + GEMM takes BF16 sets")
+    m = int(args.fused_gemm)
+    shapes = [(int(r), int(c)) for r, c in w.shapes]
+    T = len(shapes)
+    log(f"[fused] generating {w.name}: {T} matrices, {w.n} elements; m = {m}")
+    bits = S.set_bits(w)
+    # W stacked per shape (bmm operands), each matrix a contiguous view
+    groups = {}
+    for i, sh in enumerate(shapes):
+        groups.setdefault(sh, []).append(i)
+    wstack, ws = {}, [None] * T
+    for sh, idx in groups.items():
+        st = torch.empty((len(idx),) + sh, dtype=torch.int16, device=dev)
+        for j, i in enumerate(idx):
+            st[j].copy_(torch.from_numpy(bits[i].view(np.int16)).view(sh))
+            ws[i] = st[j].view(torch.bfloat16)
+        wstack[sh] = st.view(torch.bfloat16)
+    g = np.random.default_rng(12345)
+    xb = [S.f32_to_bf16_bits(g.standard_normal(m * c).astype(np.float32)).reshape(m, c) for _, c in shapes]
+    xs = [torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) for x in xb]
+    xt = {sh: torch.stack([xs[i].t() for i in idx]).contiguous() for sh, idx in groups.items()}  # G x K x m
+    yflat = torch.zeros(sum(m * r for r, _ in shapes), dtype=torch.float32, device=dev)
+    ys, off = [], 0
+    for r, _ in shapes:
+        ys.append(yflat[off:off + m * r].view(m, r))
+        off += m * r
+    log("[fused] encoding (tile order, and row-major for decode-then-GEMM)")
+    et = G.encode_weights(ws)
+    er = codec.encode_batch([x.view(-1) for x in ws])
+    dstack = {sh: torch.empty_like(wstack[sh]) for sh in groups}
+    douts = [None] * T
+    for sh, idx in groups.items():
+        for j, i in enumerate(idx):
+            douts[i] = dstack[sh][j].view(-1)
+    ns = [r * c for r, c in shapes]
+    fmt = B.format_word("bf16")
+    h_segs, tot = B.wc_plan_batch(fmt, ns)
+    d_segs = codec.segments_to_device(h_segs, T, dev)
+    h_g = G.gemm_descriptors(xs, ys, shapes)
+    d_g = G.descriptors_to_device(h_g, dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    bufs = et.batch.buffers()
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        yflat.zero_()
+        B.wc_decode_gemm_batch(fmt, h_segs, d_segs, T, h_g, d_g, m, bufs, err, stream)
+
+    def bf16_gemm():
+        return [torch.bmm(wstack[sh], xt[sh]) for sh in groups]
+
+    def decode_then_gemm():
+        codec.decode_batch(er, outs=douts, check=False)
+        return [torch.bmm(dstack[sh], xt[sh]) for sh in groups]
+
+    # before timing: both encodings round-trip bit for bit, and the fused Y
+    # agrees with torch's BF16 GEMM of the uncompressed weights (whose output
+    # is rounded to BF16: relative differences of a few 2^-9 are expected;
+    # the element-wise parity against the oracle is in the test suite)
+    fused()
+    torch.cuda.synchronize()
+    if int(err.item()):
+        raise RuntimeError(f"device error bits {int(err.item()):#x}")
+    for a, b in zip(G.decode_weights(et), ws):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    yt = decode_then_gemm()
+    torch.cuda.synchronize()
+    for sh in groups:
+        assert torch.equal(dstack[sh].view(torch.int16), wstack[sh].view(torch.int16))
+    worst = 0.0
+    for (sh, idx), y_b in zip(groups.items(), yt):
+        for j, i in enumerate(idx):
+            ref = y_b[j].t().float()
+            worst = max(worst, float((ys[i] - ref).abs().max() / ref.abs().max().clamp_min(1e-30)))
+    if worst > 2.0 ** -6:
+        raise RuntimeError(f"fused Y differs from the BF16 GEMM by {worst:.3g} of its largest value")
+    log(f"[fused] checked: both encodings round-trip; fused Y within {worst:.2e} of the BF16 GEMM")
+
+    def timed(fn, K, W):
+        for _ in range(W):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = [a.elapsed_time(b) for a, b in ev]
+        return float(np.mean(t)), float(np.median(t)), float(min(t))
+
+    K, W = args.steps, args.warmup
+    f_ms = timed(fused, K, W)
+    b_ms = timed(bf16_gemm, K, W)
+    d_ms = timed(decode_then_gemm, K, W)
+    dec_only = timed(lambda: codec.decode_batch(er, outs=douts, check=False), K, W)
+    C = int(tot.num_chunks)
+    payload_bytes = int(et.batch.payload.numel())
+    raw_w = 2 * int(tot.n)
+    alg = (payload_bytes + int(tot.raw_bytes) + int(tot.table_bytes) + 8 * (C + 1)
+           + sum(2 * m * c for _, c in shapes) + sum(4 * m * r for r, _ in shapes))
+    achieved = alg / (f_ms[0] / 1e3) / 1e9
+    flops = sum(2.0 * m * r * c for r, c in shapes)
+    result = {
+        "metric": "fused decode+GEMM: BF16 weight GB/s consumed (Y = X W^T from compressed W)",
+        "value": round(raw_w / (f_ms[0] / 1e3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(f_ms[0], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "m": m, "matrices": T, "elements": int(tot.n), "chunks": C},
+        "ratio": round(et.ratio, 5),
+        "fused_ms": {"mean": round(f_ms[0], 5), "median": round(f_ms[1], 5), "min": round(f_ms[2], 5)},
+        "bf16_gemm_ms": {"mean": round(b_ms[0], 5), "median": round(b_ms[1], 5), "min": round(b_ms[2], 5),
+                         "kind": f"torch.bmm per shape ({len(groups)} launches), uncompressed BF16 weights"},
+        "decode_then_gemm_ms": {"mean": round(d_ms[0], 5), "median": round(d_ms[1], 5),
+                                "min": round(d_ms[2], 5)},
+        "decode_only_ms": round(dec_only[0], 5),
+        "fused_vs_bf16": round(b_ms[0] / f_ms[0], 4),
+        "fused_vs_decode_then_gemm": round(d_ms[0] / f_ms[0], 4),
+        "bf16_gemm_weight_GBps": round(raw_w / (b_ms[0] / 1e3) / 1e9, 2),
+        "tflops": round(flops / (f_ms[0] / 1e3) / 1e12, 3),
+        "roofline": {"kernel": "decode_gemm", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "alg_bytes": alg},
+        "max_rel_diff_vs_bf16_gemm": round(worst, 6),
+    }
+    if not args.no_cpu_baseline:
+        log("[fused] timing the oracle on host cores")
+        result["cpu_baseline"] = fused_cpu_baseline(w, bits, xb, shapes)
+    print(json.dumps(result), flush=True)
+
+
+def fused_cpu_baseline(w, bits, xb, shapes):
+    """The oracle as it stands on the first matrix: decode of its tile-ordered
+    stream (all host cores, at most 16), the inverse tile order, and the
+    double-precision X W^T (one thread)."""
+    import oracle
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    threads = max(1, min(16, avail))
+    r, c = shapes[0]
+    tiles = oracle.tile_order(bits[0].reshape(r, c))
+    e = oracle.encode(tiles, "bf16", threads=threads)
+    t = time.perf_counter()
+    y, _ = oracle.decode(e, threads=threads)
+    wmat = oracle.tile_order(y, True, (r, c))
+    oracle.gemm_bf16(xb[0], wmat)
+    dt = time.perf_counter() - t
+    assert np.array_equal(wmat.reshape(-1), bits[0])
+    return {"value": 2 * r * c / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"matrix 0 of {w.name} ({r} x {c}), m = {xb[0].shape[0]}: decode ({threads} threads), "
+                      f"inverse tile order and double-precision X W^T (1 thread)",
+            "seconds": dt}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -204,6 +384,11 @@ def main():
               "whole tensors with no exchange on decode, and no multi-GPU path is built here.",
               file=sys.stderr)
         sys.exit(2)
+    if args.fused_gemm:
+        if not 1 <= args.fused_gemm <= 64:
+            raise SystemExit("--fused-gemm takes 1 to 64 rows")
+        fused_gemm_main(args)
+        return
 
     import torch
     import lossless_weight_compression_bf16_amd as wc

@@ -13,7 +13,7 @@
 // into BF16 (as the plain decoder joins them), which are, with this order,
 // the B-operand values of v_mfma_f32_16x16x16_bf16 for wave lanes l
 // (i < 4) and l + 32 (i >= 4).  So at the end of a group the two halves of a
-// wave swap half their values (one cross-lane exchange of two dwords), each
+// wave swap half their values (two v_permlane32_swap), each
 // lane then holds its B operand for both chunks of the wave, and the group
 // ends with two MFMAs per 16 rows of X instead of a 16-byte store.
 //
@@ -77,9 +77,22 @@ struct GemmSide {
     uint32_t t0;                  // the chunk's first tile
     uint32_t p0;                  // its panel
     uint32_t npan;                // panels the chunk touches
-    float rtpp;                   // 1 / tpp
+    uint32_t magic, shift;        // t / tpp = mulhi(t << 8, magic) >> shift for t < 2^24
     uint32_t put;                 // its half owns the chunk and decodes it validly
 };
+
+// Division of a tile index t < 2^24 by d (1 <= d < 2^28) as a multiply:
+// with 2^l >= d and M = ceil(2^(24+l) / d), t M / 2^(24+l) exceeds t / d by
+// less than t / 2^(24+l) < 2^-l <= 1/d, too little to reach the next
+// integer, so floor(t / d) = (t M) >> (24 + l) = mulhi(t << 8, M) >> l; M
+// is below 2^25 + 1.
+__device__ __forceinline__ void tile_divisor(uint32_t d, uint32_t &magic, uint32_t &shift)
+{
+    uint32_t l = 0;
+    while ((1u << l) < d) l++;
+    magic = (uint32_t)((((uint64_t)1 << (24 + l)) + d - 1) / d);
+    shift = l;
+}
 
 __device__ __forceinline__ uint32_t xchg32(uint32_t v) { return (uint32_t)__shfl_xor((int)v, 32, 64); }
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -101,7 +114,8 @@ __device__ __forceinline__ GemmSide uniform(const GemmSide &a)
     u.t0 = uni(a.t0);
     u.p0 = uni(a.p0);
     u.npan = uni(a.npan);
-    u.rtpp = __uint_as_float(uni(__float_as_uint(a.rtpp)));
+    u.magic = uni(a.magic);
+    u.shift = uni(a.shift);
     u.put = uni(a.put);
     return u;
 }
@@ -117,7 +131,8 @@ struct GemmView {
     };
     const WC_GLOBAL uint8_t *lo;
     GemmSide side[2];
-    uint32_t my_len, M, L, half;
+    uint32_t my_len, M, L;
+    uint32_t xoff[2][MT];
     f32x4_t acc[2][P][MT];
 
     __device__ void reset()
@@ -134,7 +149,6 @@ struct GemmView {
                          bool put, const wc_gemm *gm, uint32_t m)
     {
         L = threadIdx.x & 63;
-        half = L >> 5;
         M = m;
         my_len = len;
         lo = gptr(raw) + sg.raw_base + start;
@@ -143,8 +157,10 @@ struct GemmView {
         const uint32_t full = (uint32_t)min((uint64_t)kChunk, sg.n - start);  // the chunk's length
         const uint32_t t0 = (uint32_t)(start / 256);
         const uint32_t t1 = t0 + (full ? (full - 1) / 256 : 0u);
+        uint32_t magic, shift;
+        tile_divisor(tpp, magic, shift);
         GemmSide me{reinterpret_cast<const WC_GLOBAL uint16_t *>(g.x), reinterpret_cast<WC_GLOBAL float *>(g.y),
-                    g.rows, g.cols, tpp, t0, t0 / tpp, t1 / tpp - t0 / tpp + 1, 1.0f / (float)tpp, put ? 1u : 0u};
+                    g.rows, g.cols, tpp, t0, t0 / tpp, t1 / tpp - t0 / tpp + 1, magic, shift, put ? 1u : 0u};
         GemmSide ot;
         ot.x = reinterpret_cast<const WC_GLOBAL uint16_t *>(
             ((uint64_t)xchg32((uint32_t)((uint64_t)me.x >> 32)) << 32) | xchg32((uint32_t)(uint64_t)me.x));
@@ -156,49 +172,43 @@ struct GemmView {
         ot.t0 = xchg32(me.t0);
         ot.p0 = xchg32(me.p0);
         ot.npan = xchg32(me.npan);
-        ot.rtpp = __uint_as_float(xchg32(__float_as_uint(me.rtpp)));
+        ot.magic = xchg32(me.magic);
+        ot.shift = xchg32(me.shift);
         ot.put = xchg32(me.put);
         // lane 0 is in half 0: its own side is chunk 0, the exchanged one chunk 1
         side[0] = uniform(me);
         side[1] = uniform(ot);
+        // the lane's byte offset into X per side and row block: row 16 mt + i
+        // (clamped to the last row: rows past m only feed rows of D that are
+        // never added to Y), columns 4j .. 4j+3 of the tile
+        const uint32_t i = L & 15, j = L >> 4;
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+                const uint32_t r = 16 * mt + i < M ? 16 * mt + i : M - 1;
+                xoff[h][mt] = 2 * (r * side[h].cols + 4 * j);
+            }
         reset();
     }
 
-    // panel (relative to the chunk's first) and column block of group g's tile
-    __device__ static void tile_of(const GemmSide &s, uint32_t g, uint32_t &pi, uint32_t &kb)
-    {
-        const uint32_t t = s.t0 + g;  // < 2^24: the float quotient is off by at most one
-        uint32_t q = (uint32_t)((float)t * s.rtpp);
-        int32_t r = (int32_t)(t - q * s.tpp);
-        if (r < 0) {
-            q--;
-            r += (int32_t)s.tpp;
-        } else if (r >= (int32_t)s.tpp) {
-            q++;
-            r -= (int32_t)s.tpp;
-        }
-        pi = q - s.p0;
-        kb = (uint32_t)r;
-    }
-
+    // X operands of group g (uniform): the tile's panel (relative to the
+    // chunk's first) and column block by scalar arithmetic, then one 8-byte
+    // load per side and row block
     __device__ void fetch_x(Pre &p, uint32_t e) const
     {
-        const uint32_t g = __builtin_amdgcn_readfirstlane(e >> 8);
-        const uint32_t i = L & 15, j = L >> 4;
+        const uint32_t g = uni(e >> 8);
 #pragma unroll
         for (int h = 0; h < 2; h++) {
-            uint32_t kb, pi;
-            tile_of(side[h], g, pi, kb);
-            p.pi[h] = uni(pi);
-            kb = uni(kb);
+            const GemmSide &s = side[h];
+            const uint32_t t = s.t0 + g;
+            const uint32_t q = __umulhi(t << 8, s.magic) >> s.shift;
+            const uint32_t kb = t - q * s.tpp;
+            p.pi[h] = q - s.p0;
+            const WC_GLOBAL uint8_t *base = reinterpret_cast<const WC_GLOBAL uint8_t *>(s.x) + 32 * kb;
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++) {
-                const uint32_t m = 16 * mt + i;
-                const uint32_t mc = m < M ? m : M - 1;  // in bounds; the value is dropped below
-                const u32x2 v = *reinterpret_cast<const WC_GLOBAL u32x2 *>(
-                    side[h].x + (uint64_t)mc * side[h].cols + 16 * kb + 4 * j);
-                p.a[h][mt] = m < M ? v : u32x2{0u, 0u};
-            }
+            for (int mt = 0; mt < MT; mt++)
+                p.a[h][mt] = *reinterpret_cast<const WC_GLOBAL u32x2 *>(base + xoff[h][mt]);
         }
     }
 
@@ -246,13 +256,15 @@ struct GemmView {
         uint32_t d2 = B16::from_coded(__builtin_amdgcn_perm(sym.y, p.lo.y, 0x05010400u));
         uint32_t d3 = B16::from_coded(__builtin_amdgcn_perm(sym.y, p.lo.y, 0x07030602u));
         if (!have) d0 = d1 = d2 = d3 = 0u;
-        // lanes 0-31 keep elements 0-3 (wave lane l) and send 4-7 (lane l+32);
-        // lanes 32-63 keep 4-7 and send 0-3
-        const uint32_t s0 = half ? d0 : d2, s1 = half ? d1 : d3;
-        const uint32_t k0 = half ? d2 : d0, k1 = half ? d3 : d1;
-        const uint32_t r0 = xchg32(s0), r1 = xchg32(s1);
-        const u32x2 b0 = half ? u32x2{r0, r1} : u32x2{k0, k1};  // chunk of half 0
-        const u32x2 b1 = half ? u32x2{k0, k1} : u32x2{r0, r1};  // chunk of half 1
+        // v_permlane32_swap trades lanes 32-63 of its first operand with
+        // lanes 0-31 of its second: swapping (d0, d2) and (d1, d3) leaves in
+        // the first operand elements 0-3 of half 0's lane l in lane l and its
+        // elements 4-7 in lane l + 32 (the B operand of half 0's chunk), and
+        // in the second the same for half 1's chunk
+        const auto p0 = __builtin_amdgcn_permlane32_swap(d0, d2, false, false);
+        const auto p1 = __builtin_amdgcn_permlane32_swap(d1, d3, false, false);
+        const u32x2 b0 = u32x2{p0[0], p1[0]};  // chunk of half 0
+        const u32x2 b1 = u32x2{p0[1], p1[1]};  // chunk of half 1
         mma(p.pi[0], 0, p.a[0], b0);
         mma(p.pi[1], 1, p.a[1], b1);
     }

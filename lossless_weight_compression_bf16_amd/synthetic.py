@@ -119,6 +119,11 @@ WORKLOADS = {
         Workload("moe-experts-bf16", "bf16", _moe_experts(),
                  Dist("student_t", nu=3.0, scale=0.015 / math.sqrt(3.0)),
                  note="256 experts x (w1, w3, w2), Student-t nu=3 scaled to std 0.015"),
+        # the experts' down projections as weights of Y = X W^T (rows = 7168
+        # output features, cols = 2048 inputs): the fused decode + GEMM set
+        Workload("moe-w2-bf16", "bf16", tuple([(7168, 2048)] * 256),
+                 Dist("student_t", nu=3.0, scale=0.015 / math.sqrt(3.0)), seed=5,
+                 note="256 expert down projections, 7168 x 2048 (out x in), Student-t nu=3, std 0.015"),
     ]
 }
 

@@ -108,3 +108,31 @@ def test_llama3_8b_set(dev, oracle_lib):
 def test_moe_experts_set(dev, oracle_lib):
     e = _check_set("moe-experts-bf16", oracle_lib, dev)
     assert 0.66 < e.ratio < 0.70
+
+
+def test_moe_w2_fused_gemm_set(dev, oracle_lib):
+    """The fused decode + GEMM over all 256 expert down projections in one
+    launch (m = 16, as the benchmark times it): sampled matrices against the
+    oracle's double-precision X W^T within the fp32 rounding bound, all of
+    them against torch's GEMM of the uncompressed weights in fp32."""
+    from lossless_weight_compression_bf16_amd import gemm as G
+    w = S.workload("moe-w2-bf16")
+    ws = [t.view(r, c) for t, (r, c) in zip(_upload_set(w, dev), w.shapes)]
+    m = 16
+    g = np.random.default_rng(12345)
+    xb = [S.f32_to_bf16_bits(g.standard_normal(m * c).astype(np.float32)).reshape(m, c) for _, c in w.shapes]
+    xs = [torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) for x in xb]
+    e = G.encode_weights(ws)
+    _say(f"[full] moe-w2-bf16: encoded in tile order, ratio {e.ratio:.4f}")
+    ys = G.decode_gemm(e, xs)
+    torch.cuda.synchronize()
+    for i in sorted({0, 1, 127, 254, 255}):
+        wi = ws[i].view(torch.int16).cpu().numpy().view(np.uint16)
+        ref, mag = oracle_lib.gemm_bf16(xb[i], wi, magnitude=True)
+        bound = (w.shapes[i][1] + 16) * 2.0 ** -24 * mag + 1e-30
+        assert np.all(np.abs(ys[i].cpu().numpy().astype(np.float64) - ref) <= bound), i
+    for i in range(len(ws)):
+        ref = xs[i].float() @ ws[i].float().t()
+        tol = (w.shapes[i][1] + 16) * 2.0 ** -23 * (xs[i].float().abs() @ ws[i].float().abs().t()) + 1e-30
+        assert bool(((ys[i] - ref).abs() <= tol).all()), i
+    _say("[full] moe-w2-bf16: fused Y checked")
