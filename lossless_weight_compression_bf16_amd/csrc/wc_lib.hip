@@ -269,17 +269,24 @@ void launch_gemm(const SegTable &st, uint64_t chunks, const wc_buffers *in, uint
                        in->raw, in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts, d_gemm, m);
 }
 
+// Accumulator sets per chunk for mt row blocks when a chunk touches at most
+// p panels (P * mt <= 8 registers' worth), or 0 if none fits.
+uint32_t gemm_panels(uint32_t mt, uint32_t p)
+{
+    if (mt == 1) return p <= 2 ? 2 : p <= 8 ? 8 : 0;
+    if (mt == 2) return p <= 2 ? 2 : p <= 4 ? 4 : 0;
+    return p <= 2 ? 2 : 0;
+}
+
 template <int DT>
-bool launch_gemm_any(uint32_t mt, uint32_t p, const SegTable &st, uint64_t chunks, const wc_buffers *in,
+void launch_gemm_any(uint32_t mt, uint32_t pp, const SegTable &st, uint64_t chunks, const wc_buffers *in,
                      uint32_t *d_err, hipStream_t stream, Opts opts, const wc_gemm *d_gemm, uint32_t m)
 {
-    if (mt == 1 && p <= 2) launch_gemm<DT, 1, 2>(st, chunks, in, d_err, stream, opts, d_gemm, m);
-    else if (mt == 1 && p <= 8) launch_gemm<DT, 1, 8>(st, chunks, in, d_err, stream, opts, d_gemm, m);
-    else if (mt == 2 && p <= 2) launch_gemm<DT, 2, 2>(st, chunks, in, d_err, stream, opts, d_gemm, m);
-    else if (mt == 2 && p <= 4) launch_gemm<DT, 2, 4>(st, chunks, in, d_err, stream, opts, d_gemm, m);
-    else if (mt == 4 && p <= 2) launch_gemm<DT, 4, 2>(st, chunks, in, d_err, stream, opts, d_gemm, m);
-    else return false;
-    return true;
+    if (mt == 1 && pp == 2) launch_gemm<DT, 1, 2>(st, chunks, in, d_err, stream, opts, d_gemm, m);
+    else if (mt == 1) launch_gemm<DT, 1, 8>(st, chunks, in, d_err, stream, opts, d_gemm, m);
+    else if (mt == 2 && pp == 2) launch_gemm<DT, 2, 2>(st, chunks, in, d_err, stream, opts, d_gemm, m);
+    else if (mt == 2) launch_gemm<DT, 2, 4>(st, chunks, in, d_err, stream, opts, d_gemm, m);
+    else launch_gemm<DT, 4, 2>(st, chunks, in, d_err, stream, opts, d_gemm, m);
 }
 
 }  // namespace
@@ -426,6 +433,8 @@ wc_status wc_decode_gemm_batch(wc_format format, const wc_segment *h_segs, const
             most = p > most ? p : most;
         }
     }
+    const uint32_t pp = gemm_panels(mt, most);
+    if (pp == 0) return WC_ERR_ARG;  // before anything is launched
     if (tot.num_chunks == 0) return WC_OK;
     SegTable st{d_segs, nseg, {0, 0, 0, 0}};
     const Opts o = opts_of(format);
@@ -433,11 +442,10 @@ wc_status wc_decode_gemm_batch(wc_format format, const wc_segment *h_segs, const
         hipLaunchKernelGGL(k_crc32<true>, dim3((uint32_t)tot.num_chunks), dim3(256), 0, stream, in->seek,
                            in->payload, in->payload_bytes, in->crc, d_err);
     }
-    const bool ok = lay == WC_BF16 ? launch_gemm_any<WC_BF16>(mt, most, st, tot.num_chunks, in, d_err, stream, o,
-                                                              d_gemm, m)
-                                   : launch_gemm_any<WC_BF16_REORDER>(mt, most, st, tot.num_chunks, in, d_err,
-                                                                      stream, o, d_gemm, m);
-    if (!ok) return WC_ERR_ARG;
+    if (lay == WC_BF16)
+        launch_gemm_any<WC_BF16>(mt, pp, st, tot.num_chunks, in, d_err, stream, o, d_gemm, m);
+    else
+        launch_gemm_any<WC_BF16_REORDER>(mt, pp, st, tot.num_chunks, in, d_err, stream, o, d_gemm, m);
     return hipGetLastError() == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 

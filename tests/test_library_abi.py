@@ -119,3 +119,42 @@ def test_argument_errors_without_launch(L):
     segs[1].chunk_base = 5  # not what the plan says
     assert L.wc_decode_batch(0, ctypes.cast(segs, ctypes.c_void_p), 0x3000, 2, ctypes.byref(good),
                              None, None) == B.WC_ERR_ARG
+
+
+def test_tile_order_and_gemm_argument_errors_without_launch(L):
+    # ragged shapes, null or misaligned or overlapping buffers: rejected on the host
+    assert L.wc_tile_order(0x1000, 0x100000, 24, 16, 0, None) == B.WC_ERR_ARG
+    assert L.wc_tile_order(0x1000, 0x100000, 16, 8, 0, None) == B.WC_ERR_ARG
+    assert L.wc_tile_order(None, 0x100000, 16, 16, 0, None) == B.WC_ERR_ARG
+    assert L.wc_tile_order(0x1008, 0x100000, 16, 16, 0, None) == B.WC_ERR_ARG
+    assert L.wc_tile_order(0x1000, 0x1100, 16, 16, 1, None) == B.WC_ERR_ARG  # 512-byte buffers overlap
+    assert L.wc_tile_order(0x1000, 0x100000, 1 << 16, 1 << 16, 0, None) == B.WC_ERR_ARG  # 2^32 elements
+    assert L.wc_tile_order(0x1000, 0x100000, 0, 16, 0, None) == B.WC_OK  # nothing to do
+    segs, tot = wc.wc_plan_batch("bf16", [64 * 2048])
+    good = B.wc_buffers(256, 256, 256, 256, 1 << 20)
+    g = (B.wc_gemm * 1)()
+    g[0].x, g[0].y, g[0].rows, g[0].cols = 0x10000, 0x20000, 64, 2048
+
+    def call(fmt=0, m=16, gemm=g, d_gemm=0x3000):
+        return L.wc_decode_gemm_batch(fmt, ctypes.cast(segs, ctypes.c_void_p), 0x4000, 1,
+                                      ctypes.cast(gemm, ctypes.c_void_p), d_gemm, m, ctypes.byref(good), None,
+                                      None)
+    assert call(fmt=B.format_word("fp16")) == B.WC_ERR_ARG      # BF16 layouts only
+    assert call(fmt=B.format_word("fp32")) == B.WC_ERR_ARG
+    assert call(fmt=B.format_word("bf16", raw_fallback=True)) == B.WC_ERR_ARG
+    assert call(m=0) == B.WC_ERR_ARG
+    assert call(m=65) == B.WC_ERR_ARG
+    assert call(d_gemm=0) == B.WC_ERR_ARG
+    assert call(d_gemm=0x3004) == B.WC_ERR_ARG                  # misaligned descriptors
+    g[0].rows = 48                                               # rows * cols != segment size
+    assert call() == B.WC_ERR_ARG
+    g[0].rows, g[0].x = 64, 0x10004                              # X not 8-byte aligned
+    assert call() == B.WC_ERR_ARG
+    g[0].x, g[0].y = 0x10000, 0x20002                            # Y not 4-byte aligned
+    assert call() == B.WC_ERR_ARG
+    # 768 columns: a full chunk spans 6 panels of 16 rows, more than m = 64 leaves accumulators for
+    segs2, _ = wc.wc_plan_batch("bf16", [256 * 768])
+    g2 = (B.wc_gemm * 1)()
+    g2[0].x, g2[0].y, g2[0].rows, g2[0].cols = 0x10000, 0x20000, 256, 768
+    assert L.wc_decode_gemm_batch(0, ctypes.cast(segs2, ctypes.c_void_p), 0x4000, 1, ctypes.cast(g2, ctypes.c_void_p),
+                                  0x3000, 64, ctypes.byref(good), None, None) == B.WC_ERR_ARG
