@@ -12,8 +12,6 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libwc.so")
 SOURCES = [os.path.join(CSRC, "wc_lib.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("wc_common.hpp", "wc_encode.hpp", "wc_decode.hpp")] + [
-    os.path.join(INCLUDE, "wc.h")]
 
 ARCH = "gfx950"
 
