@@ -112,7 +112,7 @@ WORKLOADS = {
                  Dist("normal", sigma_range=(0.01, 0.05)),
                  note="GPT-2-small-shaped BF16 set, 49 tensors, sigma_t ~ U[0.01, 0.05]"),
         Workload("fp32-768x2304", "fp32", ((768, 2304),), Dist("normal", sigma=0.02),
-                 note="config-1 draws kept in FP32 (BF16 of it is bf16-768x2304)"),
+                 note="the float32 draws of bf16-768x2304 kept in FP32 (their BF16 rounding is that set)"),
         Workload("llama3-8b-bf16", "bf16", _llama3_8b(),
                  Dist("normal", sigma=0.02, p_outlier=1e-3, outlier_k=20.0),
                  note="Llama-3-8B-shaped BF16 set, 226 tensors, 0.1% outliers at 20 sigma"),

@@ -180,12 +180,12 @@ def test_golden_streams_on_gpu(dev):
         assert h["payload"].size == case["payload_bytes"], case["name"]
 
 
-def test_config1_full(dev, oracle_lib):
+def test_bf16_768x2304_full(dev, oracle_lib):
     w = S.workload("bf16-768x2304")
     _round_trip(S.tensor_bits(w, 0), "bf16", dev, oracle_lib, w.name)
 
 
-def test_config3_full(dev, oracle_lib):
+def test_fp32_768x2304_full(dev, oracle_lib):
     w = S.workload("fp32-768x2304")
     _round_trip(S.tensor_bits(w, 0), "fp32", dev, oracle_lib, w.name)
 
@@ -212,7 +212,7 @@ def test_batch_edges(dev, oracle_lib):
     _batch_parity(xs, "bf16", dev, oracle_lib, "edges")
 
 
-def test_config2_full(dev, oracle_lib):
+def test_gpt2_small_set_full(dev, oracle_lib):
     w = S.workload("gpt2-small-bf16")
     xs = S.set_bits(w)
     e, o = _batch_parity(xs, "bf16", dev, oracle_lib, w.name)
