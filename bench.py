@@ -499,11 +499,14 @@ def main():
     # algorithmic bytes (the minimum the method moves), per launch
     side = payload_bytes + table_bytes + 8 * (C + 1)
     raw_plane = int(tot.raw_bytes)
+    # the raw plane is written by the encoder for the 16-bit layouts, by the
+    # split pass for FP32 and FP8
+    raw_by_encoder = layout not in ("fp32", "fp8e4m3", "fp8e5m2")
     alg = {
         "rans_decode": side + raw_plane + raw_in_bytes,           # read compressed + raw plane, write BF16
         "encode_total": raw_in_bytes + raw_plane + side,          # read BF16, write raw plane + compressed
-        "split_hist": raw_in_bytes + raw_plane + table_bytes,
-        "rans_encode": raw_in_bytes + table_bytes + payload_bytes,
+        "split_hist": raw_in_bytes + table_bytes + (0 if raw_by_encoder else raw_plane),
+        "rans_encode": raw_in_bytes + table_bytes + payload_bytes + (raw_plane if raw_by_encoder else 0),
         "compact": 2 * payload_bytes,
     }
     times = {"split_hist": stage_ms["split_hist"], "rans_encode": stage_ms["rans_encode"],

@@ -1,13 +1,15 @@
 // wc_encode.hpp -- encoder kernels for gfx950.
 //
 //   k_split_hist  one 256-thread block per chunk: coalesced 16-byte loads of
-//                 the tensor (four in flight per thread), raw planes written
-//                 back with vector stores, the coded plane counted into
-//                 per-lane LDS sub-histograms, then the chunk's 12-bit table
-//                 built with integer arithmetic only.
+//                 the tensor (four in flight per thread), the coded plane
+//                 counted into per-lane LDS sub-histograms, then the chunk's
+//                 12-bit table built with integer arithmetic only; FP32 and
+//                 FP8 raw planes written back with vector stores.
 //   k_encode      one wavefront per two chunks (one chunk per 32-lane half):
 //                 32 interleaved rANS states, reverse order, words written
-//                 downwards into the chunk's scratch slot.
+//                 downwards into the chunk's scratch slot; the 16-bit
+//                 layouts' raw plane (low bytes) written from the same loads,
+//                 so the split pass only reads.
 //   k_scan_*      exclusive scan of the chunk sizes into the seek table
 //                 (tile sums, then per-tile scans).
 //   k_compact     moves every chunk's payload from its slot to its offset.
@@ -114,6 +116,11 @@ __device__ inline uint32_t normalize256(C c, C T, uint32_t *red, C *keys)
 // chunk, so counters never carry into their neighbour).  At most two lanes
 // of one LDS atomic hit the same word; the odd stride spreads the copies
 // over the banks.  32 copies (16.5 KiB) leave room for six blocks per CU.
+// 16-bit layouts: the encoder, which loads every element anyway, writes the
+// raw plane; the split pass only counts.
+template <int DT>
+constexpr bool raw_in_encoder() { return DT != WC_FP32 && !is_fp8(DT); }
+
 constexpr uint32_t kHistCopies = 32;
 constexpr uint32_t kHistStride = 129;
 
@@ -213,9 +220,6 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
 #pragma unroll
             for (uint32_t u = 0; u < U; u++) {
                 v[u] = u32x4{B::to_coded(v[u].x), B::to_coded(v[u].y), B::to_coded(v[u].z), B::to_coded(v[u].w)};
-                const u32x2 l = u32x2{__builtin_amdgcn_perm(v[u].y, v[u].x, 0x06040200u),
-                                      __builtin_amdgcn_perm(v[u].w, v[u].z, 0x06040200u)};
-                reinterpret_cast<WC_GLOBAL u32x2 *>(lo)[g + 256 * u] = l;
                 const uint32_t h0 = __builtin_amdgcn_perm(v[u].y, v[u].x, 0x07050301u);
                 const uint32_t h1 = __builtin_amdgcn_perm(v[u].w, v[u].z, 0x07050301u);
 #pragma unroll
@@ -227,19 +231,13 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
         for (; g < ng; g += 256) {
             u32x4 v = reinterpret_cast<const WC_GLOBAL u32x4 *>(in)[g];
             v = u32x4{B::to_coded(v.x), B::to_coded(v.y), B::to_coded(v.z), B::to_coded(v.w)};
-            const u32x2 l = u32x2{__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
-                                  __builtin_amdgcn_perm(v.w, v.z, 0x06040200u)};
-            reinterpret_cast<WC_GLOBAL u32x2 *>(lo)[g] = l;
             const uint32_t h0 = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
             const uint32_t h1 = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
             for (uint32_t i = 0; i < 4; i++) hist_add(my, (h0 >> (8 * i)) & 0xFF);
             for (uint32_t i = 0; i < 4; i++) hist_add(my, (h1 >> (8 * i)) & 0xFF);
         }
-        for (uint32_t i = ng * 8 + tid; i < len; i += 256) {
-            const uint32_t e = B::to_coded(in[i]);
-            lo[i] = (uint8_t)(e & 0xFF);
-            hist_add(my, e >> 8);
-        }
+        for (uint32_t i = ng * 8 + tid; i < len; i += 256) hist_add(my, B::to_coded(in[i]) >> 8);
+        (void)lo;
     } else {
         // FP32: exponent counted; raw = sign bits | m0 | m1 | m2 (plane bases
         // follow the segment's element count, so the mantissa planes have no
@@ -439,7 +437,7 @@ constexpr uint32_t kRawMark = 0xFFFFFFFFu;
 template <int DT>
 __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__restrict__ tables,
                                                uint8_t *__restrict__ slots, uint2 *__restrict__ meta,
-                                               uint64_t total_chunks, Opts opts)
+                                               uint64_t total_chunks, Opts opts, uint8_t *__restrict__ raw)
 {
     __shared__ EncSym enc[2][256];
     __shared__ uint32_t estage[2][kEncBlk / 4];  // one full group's coded bytes per half
@@ -494,6 +492,9 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     asm volatile("" : "+v"(woff), "+v"(hs));
     SymView<DT> sv;
     sv.in = gptr<const typename SymView<DT>::Elem>(sg.ptr) + start;
+    // 16-bit layouts: this chunk's part of the raw plane (low bytes of the
+    // rearranged values); a shadow half writes its sibling's bytes again
+    WC_GLOBAL uint8_t *const lo = gptr(raw) + sg.raw_base + start;
     uint32_t x = kL;
     uint32_t p_w = kMaxWords;  // words are written downwards from here
 
@@ -508,6 +509,13 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     auto group = [&](auto check_tag, uint32_t g, uint32_t g_next, const Pre &cur, Pre &ahead) {
         constexpr bool CHECK = decltype(check_tag)::value;
         ahead = sv.template fetch<CHECK>(g_next, lane, len);
+        if constexpr (raw_in_encoder<DT>()) {
+#pragma unroll
+            for (uint32_t i = 0; i < kEncGroup; i++) {
+                const uint32_t j = kEncBlk * g + kLanes * i + lane;
+                if (j < len) lo[j] = (uint8_t)(Bits16<DT>::to_coded(cur.e[i]) & 0xFF);
+            }
+        }
         EncSym es[kEncGroup];
 #pragma unroll
         for (uint32_t i = 0; i < kEncGroup; i++) es[i] = enc[h][SymView<DT>::symbol(cur.e[i])];
@@ -536,7 +544,16 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
         WideView<DT> wv;
         wv.in = reinterpret_cast<decltype(wv.in)>(sv.in);
         const uint8_t *stg = reinterpret_cast<const uint8_t *>(&estage[h][0]);
-        auto transpose = [&](const WPre &d, uint32_t (&sy)[kEncGroup]) {
+        // stages group gs's coded bytes for its steps (and, 16-bit layouts,
+        // writes its raw bytes: 8 per lane, contiguous)
+        auto transpose = [&](const WPre &d, uint32_t (&sy)[kEncGroup], uint32_t gs) {
+            if constexpr (raw_in_encoder<DT>()) {
+                using B = Bits16<DT>;
+                const uint32_t a0 = B::to_coded(d.v.x), a1 = B::to_coded(d.v.y);
+                const uint32_t a2 = B::to_coded(d.v.z), a3 = B::to_coded(d.v.w);
+                reinterpret_cast<WC_GLOBAL u32x2 *>(lo + kEncBlk * gs)[lane] =
+                    u32x2{__builtin_amdgcn_perm(a1, a0, 0x06040200u), __builtin_amdgcn_perm(a3, a2, 0x06040200u)};
+            }
             const uint2 b = WideView<DT>::bytes(d);
             wave_lds_order();
             reinterpret_cast<uint2 *>(&estage[h][0])[lane] = b;
@@ -547,13 +564,13 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
         uint32_t sy[kEncGroup];
         // g: the group encoded; gl: the group whose load is issued; nx: the
         // next group's data, staged now
-        auto fgroup = [&](uint32_t gl, WPre &load_into, const WPre &nx) {
+        auto fgroup = [&](uint32_t gl, WPre &load_into, const WPre &nx, uint32_t gs) {
             load_into = wv.fetch(gl, lane);
             EncSym es[kEncGroup];
 #pragma unroll
             for (uint32_t i = 0; i < kEncGroup; i++) es[i] = enc[h][sy[i]];
             uint32_t sn[kEncGroup];
-            transpose(nx, sn);
+            transpose(nx, sn, gs);
 #pragma unroll
             for (int i = kEncGroup - 1; i >= 0; i--) enc_step<false>(x, p_w, true, es[i], wbase, woff, h, hs);
 #pragma unroll
@@ -561,15 +578,16 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
         };
         // n3 - 1 = 2 (mod 3): the sets hold groups 2, 1, 0 (mod 3)
         WPre s2 = wv.fetch(n3 - 1, lane);
-        transpose(s2, sy);
+        transpose(s2, sy, n3 - 1);
         WPre s1 = wv.fetch(n3 - 2, lane);
         WPre s0 = wv.fetch(n3 - 3, lane);
 #pragma unroll 1
         for (uint32_t g = n3; g > 0; g -= 3) {
-            // groups g-1, g-2, g-3; loads below group 0 re-load group 0
-            fgroup(g >= 4 ? g - 4 : 0, s2, s1);
-            fgroup(g >= 5 ? g - 5 : 0, s1, s0);
-            fgroup(g >= 6 ? g - 6 : 0, s0, s2);
+            // groups g-1, g-2, g-3; loads below group 0 re-load group 0 (and
+            // stage it again: its raw bytes are then written twice, equal)
+            fgroup(g >= 4 ? g - 4 : 0, s2, s1, g - 2);
+            fgroup(g >= 5 ? g - 5 : 0, s1, s0, g - 3);
+            fgroup(g >= 6 ? g - 6 : 0, s0, s2, g >= 4 ? g - 4 : 0);
         }
     }
 

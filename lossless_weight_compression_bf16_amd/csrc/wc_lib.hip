@@ -2,6 +2,7 @@
 //
 // Host side: argument validation, buffer layout, and the launch sequence
 //   encode: k_split_hist -> k_encode -> k_scan_tiles, k_scan_apply -> k_compact
+//           (16-bit layouts: the raw plane is written by k_encode)
 //           (tensor-wide tables: k_zero_u64 before the split, k_tensor_table after;
 //           CRC-32 option: k_crc32 after the compaction)
 //   decode: k_decode (then k_decode_raw for chunks stored raw; CRC-32 option:
@@ -136,7 +137,7 @@ wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, c
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return WC_ERR_HIP;
     if (chunks) {
         hipLaunchKernelGGL(k_encode<DT>, dim3((uint32_t)((chunks + 1) / 2)), dim3(64), 0, stream, st,
-                           out->tables, slots, meta, chunks, opts);
+                           out->tables, slots, meta, chunks, opts, out->raw);
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return WC_ERR_HIP;
     {
