@@ -686,15 +686,12 @@ __global__ __launch_bounds__(1024) void k_scan_apply(const uint2 *__restrict__ m
 
 // ------------------------------------------------------------------ compact
 
-__global__ __launch_bounds__(256) void k_compact(const uint8_t *__restrict__ slots,
-                                                 const uint2 *__restrict__ meta,
-                                                 const uint64_t *__restrict__ seek,
-                                                 uint8_t *__restrict__ payload, uint64_t capacity)
+// Moves chunk k's payload (meta mk) from its slot to dst_off (a chunk that
+// would not fit the capacity is skipped: the scan reports it).
+__device__ inline void compact_chunk(const uint8_t *__restrict__ slots, uint64_t k, uint2 mk, uint64_t dst_off,
+                                     uint8_t *__restrict__ payload, uint64_t capacity)
 {
-    const uint64_t k = blockIdx.x;
-    const uint2 mk = meta[k];
-    const uint64_t dst_off = seek[k];
-    if (dst_off + mk.x > capacity) return;  // reported by the scan
+    if (dst_off + mk.x > capacity) return;
     const WC_GLOBAL uint32_t *src = reinterpret_cast<const WC_GLOBAL uint32_t *>(gptr(slots) + k * kSlotBytes);
     WC_GLOBAL uint32_t *dst = reinterpret_cast<WC_GLOBAL uint32_t *>(gptr(payload) + dst_off);
     const uint32_t tid = threadIdx.x;
@@ -732,6 +729,47 @@ __global__ __launch_bounds__(256) void k_compact(const uint8_t *__restrict__ slo
             wd[i] = d;
         }
     }
+}
+
+__global__ __launch_bounds__(256) void k_compact(const uint8_t *__restrict__ slots,
+                                                 const uint2 *__restrict__ meta,
+                                                 const uint64_t *__restrict__ seek,
+                                                 uint8_t *__restrict__ payload, uint64_t capacity)
+{
+    const uint64_t k = blockIdx.x;
+    compact_chunk(slots, k, meta[k], seek[k], payload, capacity);
+}
+
+// Scan and compaction in one launch for at most one scan tile of chunks:
+// block k sums the sizes of the chunks before it (at most 4095 8-byte meta
+// records, read from L2), writes seek[k] (the last block also the total, and
+// the capacity error), then moves its payload.
+__global__ __launch_bounds__(256) void k_scan_compact(const uint8_t *__restrict__ slots,
+                                                      const uint2 *__restrict__ meta, uint64_t total_chunks,
+                                                      uint64_t *__restrict__ seek, uint8_t *__restrict__ payload,
+                                                      uint64_t capacity, uint32_t *err)
+{
+    __shared__ uint64_t wsum[4];
+    __shared__ uint64_t off;
+    const uint64_t k = blockIdx.x;
+    const uint32_t tid = threadIdx.x;
+    uint64_t v = 0;
+    for (uint64_t i = tid; i < k; i += 256) v += meta[i].x;
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if ((tid & 63) == 0) wsum[tid >> 6] = v;
+    __syncthreads();
+    const uint2 mk = meta[k];
+    if (tid == 0) {
+        const uint64_t before = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        off = before;
+        seek[k] = before;
+        if (k + 1 == total_chunks) {
+            seek[total_chunks] = before + mk.x;
+            if (before + mk.x > capacity && err) atomicOr(err, WC_EF_CAPACITY);
+        }
+    }
+    __syncthreads();
+    compact_chunk(slots, k, mk, off, payload, capacity);
 }
 
 }  // namespace wc

@@ -2,6 +2,7 @@
 //
 // Host side: argument validation, buffer layout, and the launch sequence
 //   encode: k_split_hist -> k_encode -> k_scan_tiles, k_scan_apply -> k_compact
+//           (at most 4096 chunks: k_scan_compact does scan and compaction)
 //           (16-bit layouts: the raw plane is written by k_encode)
 //           (tensor-wide tables: k_zero_u64 before the split, k_tensor_table after;
 //           CRC-32 option: k_crc32 after the compaction)
@@ -140,7 +141,8 @@ wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, c
                            out->tables, slots, meta, chunks, opts, out->raw);
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return WC_ERR_HIP;
-    {
+    const bool one_tile = chunks > 0 && chunks <= kScanTile;  // scan + compaction in one launch
+    if (!one_tile) {
         // tile sums go to the spare slot after the last chunk's
         const uint32_t tiles = (uint32_t)((chunks + kScanTile - 1) / kScanTile);
         uint64_t *tile_sum = reinterpret_cast<uint64_t *>(slots + chunks * kSlotBytes);
@@ -150,7 +152,10 @@ wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, c
                            out->seek, out->payload_bytes, d_err);
     }
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return WC_ERR_HIP;
-    if (chunks) {
+    if (one_tile) {
+        hipLaunchKernelGGL(k_scan_compact, dim3((uint32_t)chunks), dim3(256), 0, stream, slots, meta, chunks,
+                           out->seek, out->payload, out->payload_bytes, d_err);
+    } else if (chunks) {
         hipLaunchKernelGGL(k_compact, dim3((uint32_t)chunks), dim3(256), 0, stream, slots, meta, out->seek,
                            out->payload, out->payload_bytes);
     }
