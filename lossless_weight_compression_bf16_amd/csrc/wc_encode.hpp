@@ -526,17 +526,20 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
         }
     };
     // Groups run from the last to the first.  The groups above the largest
-    // multiple of three below the shorter chunk's full-group count run checked
-    // first; then whole triples of full groups run unchecked, their input
-    // loaded two groups ahead into three register sets in fixed registers.
-    const uint32_t n3 = nfull / 3 * 3;
+    // multiple of D below the shorter chunk's full-group count run checked
+    // first; then rounds of D full groups run unchecked, each group's input
+    // loaded D groups ahead into one of D register sets in fixed registers
+    // (D = 8 hides a miss to HBM where a set fits the Infinity Cache only
+    // partly; 3 and 4 did not, 16 costs occupancy on large sets).
+    constexpr uint32_t D = 8;  // groups per loop round = register sets = prefetch distance
+    const uint32_t n3 = nfull / D * D;
     for (uint32_t g = ng; g-- > n3;) {
         const Pre cur = sv.template fetch<true>(g, lane, len);
         Pre dummy;
         group(std::true_type{}, g, g, cur, dummy);
     }
     if (n3) {
-        // Full groups, descending: group g's wide load is issued three groups
+        // Full groups, descending: group g's wide load is issued D groups
         // before g is encoded, its bytes go through the stage one group
         // before, and each group reads its per-symbol constants from the
         // symbols so staged.  Loads and stage traffic overlap the steps.
@@ -576,18 +579,19 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
 #pragma unroll
             for (uint32_t i = 0; i < kEncGroup; i++) sy[i] = sn[i];
         };
-        // n3 - 1 = 2 (mod 3): the sets hold groups 2, 1, 0 (mod 3)
-        WPre s2 = wv.fetch(n3 - 1, lane);
-        transpose(s2, sy, n3 - 1);
-        WPre s1 = wv.fetch(n3 - 2, lane);
-        WPre s0 = wv.fetch(n3 - 3, lane);
+        // set i holds group k = i (mod D); n3 = 0 (mod D)
+        WPre s[D];
+#pragma unroll
+        for (uint32_t i = 0; i < D; i++) s[i] = wv.fetch(n3 - D + i, lane);
+        transpose(s[D - 1], sy, n3 - 1);
 #pragma unroll 1
-        for (uint32_t g = n3; g > 0; g -= 3) {
-            // groups g-1, g-2, g-3; loads below group 0 re-load group 0 (and
-            // stage it again: its raw bytes are then written twice, equal)
-            fgroup(g >= 4 ? g - 4 : 0, s2, s1, g - 2);
-            fgroup(g >= 5 ? g - 5 : 0, s1, s0, g - 3);
-            fgroup(g >= 6 ? g - 6 : 0, s0, s2, g >= 4 ? g - 4 : 0);
+        for (uint32_t g = n3; g > 0; g -= D) {
+#pragma unroll
+            for (uint32_t j = 1; j <= D; j++) {
+                // encode group g - j (its set is free: load group g - j - D into
+                // it, group 0 when below) and stage group g - j - 1
+                fgroup(g >= j + D ? g - j - D : 0, s[(D - j) % D], s[(2 * D - j - 1) % D], g >= j + 1 ? g - j - 1 : 0);
+            }
         }
     }
 
