@@ -1,31 +1,34 @@
 // wc_decode.hpp -- fused decoder for gfx950.
 //
-// One wavefront decodes two chunks, one per 32-lane half, so every VALU
-// instruction of the serial rANS loop carries 64 useful lanes.  Per half the
-// LDS holds
-//   - the chunk's slot lookup table, in one of two forms:
-//       wide  (kL1 = true):  one u32 per slot = symbol | (f-1) << 8 |
-//                            (slot-b) << 20; one LDS read per step.  16 KiB
-//                            per chunk, so 4 wavefronts per CU: used when
-//                            there are few chunks and the run is bound by
-//                            the serial latency of each chunk;
-//       narrow (kL1 = false): slot -> symbol bytes (4 KiB) plus per-symbol
-//                            b | (f-4096) << 16 (1 KiB); two LDS reads per
-//                            step but 3x the wavefronts per CU, used when
-//                            there are enough chunks to fill the machine;
-//   - a 320-word ring of the compressed stream (plus its first 64 words
-//     repeated after the end, so a step's 32 reads never wrap), refilled
-//     64 words at a time: a refill is loaded at the start of a group of 8
-//     steps and written to the ring at the start of the group after next,
-//     so the load has two groups to land and the word fetch of a step is
-//     an LDS read.  The ring is sized for one group's worst case (256
-//     words) plus a block, not for the refill latency: a group runs
-//     speculatively on the words landed so far; a chunk in which a group
-//     consumed a word that had not landed is decoded again from the start
-//     with a synchronous fill before every group (rare: it needs more than
-//     64 words per group for many groups in a row, about 2 bits/symbol
-//     above what weights carry).
-//     A small ring keeps 13 wavefronts per CU;
+// Two forms, chosen by how many chunks there are:
+//   - narrow table (kL1 = false, kH = 2): one wavefront decodes two chunks,
+//     one per 32-lane half, so every VALU instruction of the serial rANS
+//     loop carries 64 useful lanes.  Per half the LDS holds slot -> symbol
+//     bytes (4 KiB) plus per-symbol b | (f-4096) << 16 (1 KiB); a step makes
+//     two dependent table reads and then its ring read.  10 wavefronts per
+//     CU: used when there are enough chunks to fill the machine;
+//   - wide table (kL1 = true, kH = 1): one chunk per wavefront, one u32 per
+//     slot = symbol | (f-1) << 8 | (slot-b) << 20 (16 KiB), and a ring that
+//     keeps each stream word next to the entry of the slot it brings in.  A
+//     step starts from the entry of its own slot (known from the step
+//     before) and issues in one batch the read of the entry for the state it
+//     keeps and the ring read of its next word with that word's entry, so it
+//     waits for one LDS latency.  Used while every chunk fits on the machine
+//     at once (8 wavefronts per CU), when the run is bound by the serial
+//     latency of each chunk.
+// Per chunk the LDS also holds
+//   - a ring of the compressed stream (320 words, 512 with two-dword
+//     refills; its first 64 or 128 words repeated after the end, so a step's
+//     32 reads never wrap), refilled 64 or 128 words at a time: a refill is
+//     loaded at the start of a group of 8 steps and written to the ring at
+//     the start of the group after next, so the load has two groups to land
+//     and the word fetch of a step is an LDS read.  The ring is sized for one
+//     group's worst case (256 words) plus a block, not for the refill
+//     latency: a group runs speculatively on the words landed so far; a
+//     chunk in which a group consumed a word that had not landed is decoded
+//     again from the start with a synchronous fill before every group (rare:
+//     it needs more than 64 words per group for many groups in a row, about
+//     2 bits/symbol above what weights carry);
 //   - the 256 decoded bytes of the current group.
 // At the end of a group each lane joins 8 consecutive decoded bytes with 8
 // raw bytes (loaded with one 8-byte load issued two groups earlier) and
@@ -43,7 +46,6 @@ namespace wc {
 
 constexpr uint32_t kGroup = 8;                       // steps per group
 constexpr uint32_t kGroupWords = kLanes * kGroup;    // most words one group consumes
-constexpr uint32_t kApron = 2 * kLanes;              // ring words 0..63 repeated after the end
 constexpr uint32_t kStageBytes = kLanes * kGroup;    // decoded bytes per group per half
 
 // Ring geometry for refills of kB dwords per lane.  A refill moves a block
@@ -56,34 +58,49 @@ constexpr uint32_t kStageBytes = kLanes * kGroup;    // decoded bytes per group 
 // which would otherwise outrun the refills and take the second pass.
 // A block never covers an unconsumed word: at issue fewer than kAhead words
 // are unconsumed, so with the block fewer than kWords.
-template <int kB>
+// The ring's first kApron words are repeated after its end, and the cursor
+// is reduced modulo the ring size every kWrap = kApron / 32 steps, so the 32
+// reads of a step never wrap (the wide table's ring reduces it every fourth
+// step, the narrow one every second).
+template <int B, bool kWide = false>
 struct Ring {
+    static constexpr int kB = B;
     static constexpr uint32_t kBlk = 2 * kLanes * kB;
     static constexpr uint32_t kWords = kB == 1 ? kGroupWords + kBlk : 512;
+    static constexpr uint32_t kApron = (kWide ? 4 : 2) * kLanes;
+    static constexpr uint32_t kWrap = kApron / kLanes;
     static constexpr uint32_t kAlloc = kWords + kApron;
     static constexpr uint32_t kAhead = kWords - kBlk;
+    // groups between a refill's load and its write to the ring (and between
+    // a raw-byte load and its use)
+    static constexpr uint32_t kDepth = 3;
     static_assert(kWords % kBlk == 0, "blocks must not wrap the ring");
     static_assert(kAhead >= kGroupWords, "a synchronous fill must land a whole group's worst case");
 };
 
-// H = chunks per wavefront (one per 32-lane half)
+// H = chunks per wavefront (one per 32-lane half).  The wide table's ring
+// holds each stream word next to the table entry of the slot the word
+// brings into a renormalising state (its low 12 bits), both written when
+// the word lands; the (b, f) scratch of the table build shares its space.
 template <int H, int kB>
 struct DecSharedL1 {
-    static constexpr int kRefill = kB;
-    static constexpr uint32_t kRingWords = Ring<kB>::kWords;
+    using R = Ring<kB, true>;
+    static constexpr uint32_t kRingWords = R::kWords;
     uint32_t tab[H][kM];                    // per slot: sym | (f-1) << 8 | (slot-b) << 20
-    uint32_t fbtmp[H][256];                 // (b, f) while the table is built
-    uint32_t ring[H][Ring<kB>::kAlloc / 2];
+    union alignas(16) {
+        uint32_t fbtmp[H][256];             // (b, f) while the table is built
+        u32x2 ring2[H][R::kAlloc];          // per ring word: (tab[word & 4095], word)
+    };
     uint32_t stage[H][kStageBytes / 4];
 };
 
 template <int H, int kB>
 struct DecSharedL2 {
-    static constexpr int kRefill = kB;
-    static constexpr uint32_t kRingWords = Ring<kB>::kWords;
+    using R = Ring<kB>;
+    static constexpr uint32_t kRingWords = R::kWords;
     uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
     uint32_t fb[H][256];                    // b | (f - 4096) << 16
-    uint32_t ring[H][Ring<kB>::kAlloc / 2];
+    uint32_t ring[H][R::kAlloc / 2];
     uint32_t stage[H][kStageBytes / 4];
 };
 
@@ -118,10 +135,10 @@ __device__ __forceinline__ Refill refill_none()
     return Refill{0u, 0u, 0u, false, true};
 }
 
-template <int kB>
+template <typename R>
 __device__ __forceinline__ Refill refill_issue(Stream &st, uint32_t lane, bool on)
 {
-    using R = Ring<kB>;
+    constexpr int kB = R::kB;
     Refill r;
     r.go = on && st.fill - st.ptr < R::kAhead && st.fill < st.nw;
     if constexpr (kB == 1) {
@@ -150,21 +167,44 @@ __device__ __forceinline__ Refill refill_issue(Stream &st, uint32_t lane, bool o
     return r;
 }
 
-template <int kB>
+template <typename R>
 __device__ __forceinline__ void refill_commit(Stream &st, Refill &r, uint32_t *ring)
 {
-    using R = Ring<kB>;
+    constexpr int kB = R::kB;
     if (r.go) {
-        // the cursor wraps every second step, so the reads of a step start
-        // below R::kWords + 32 and never wrap
         if constexpr (kB == 1) {
             ring[r.pos] = r.v;
-            if (r.pos < kApron / 2) ring[R::kWords / 2 + r.pos] = r.v;
+            if (r.pos < R::kApron / 2) ring[R::kWords / 2 + r.pos] = r.v;
         } else {
             // d0 < d: dword d is the pair's second (or past the end), d + 1 is past the end
             const uint2 w = make_uint2(r.first ? r.v : r.v1, r.v1);
             *reinterpret_cast<uint2 *>(&ring[r.pos]) = w;
-            if (r.pos < kApron / 2) *reinterpret_cast<uint2 *>(&ring[R::kWords / 2 + r.pos]) = w;
+            if (r.pos < R::kApron / 2) *reinterpret_cast<uint2 *>(&ring[R::kWords / 2 + r.pos]) = w;
+        }
+        st.land += R::kBlk;
+        r.go = false;
+    }
+}
+
+// The wide table's ring: each landed word is written with its slot's entry.
+// The lane's words start at ring word 2 r.pos (even), so each pair of words
+// is one aligned 16-byte store.
+template <typename R>
+__device__ __forceinline__ void refill_commit(Stream &st, Refill &r, u32x2 *ring2, const uint32_t *tab)
+{
+    constexpr int kB = R::kB;
+    if (r.go) {
+        auto put = [&](uint32_t at, uint32_t v) {
+            const uint32_t w0 = v & 0xFFFF, w1 = v >> 16;
+            const u32x4 e = {tab[w0 & (kM - 1)], w0, tab[w1 & (kM - 1)], w1};
+            *reinterpret_cast<u32x4 *>(&ring2[at]) = e;
+            if (at < R::kApron) *reinterpret_cast<u32x4 *>(&ring2[R::kWords + at]) = e;
+        };
+        if constexpr (kB == 1) {
+            put(2 * r.pos, r.v);
+        } else {
+            put(2 * r.pos, r.first ? r.v : r.v1);
+            put(2 * r.pos + 2, r.v1);
         }
         st.land += R::kBlk;
         r.go = false;
@@ -174,15 +214,15 @@ __device__ __forceinline__ void refill_commit(Stream &st, Refill &r, uint32_t *r
 // Lands what the next group may need (256 words, or the rest of the
 // stream): up to 256 / block blocks, loaded together and then written.
 // Only called with nothing in flight, so issued equals landed.
-template <int kB>
-__device__ __forceinline__ void refill_sync(Stream &st, uint32_t lane, bool ok, uint32_t *ring)
+template <typename R, typename... Sink>
+__device__ __forceinline__ void refill_sync(Stream &st, uint32_t lane, bool ok, Sink... sink)
 {
-    constexpr uint32_t n = kGroupWords / Ring<kB>::kBlk;
+    constexpr uint32_t n = kGroupWords / R::kBlk;
     Refill r[n];
 #pragma unroll
-    for (uint32_t j = 0; j < n; j++) r[j] = refill_issue<kB>(st, lane, ok && st.fill - st.ptr < kGroupWords);
+    for (uint32_t j = 0; j < n; j++) r[j] = refill_issue<R>(st, lane, ok && st.fill - st.ptr < kGroupWords);
 #pragma unroll
-    for (uint32_t j = 0; j < n; j++) refill_commit<kB>(st, r[j], ring);
+    for (uint32_t j = 0; j < n; j++) refill_commit<R>(st, r[j], sink...);
 }
 
 // ----------------------------------------------------------- raw plane views
@@ -330,26 +370,9 @@ using RawView = typename std::conditional<
 
 // -------------------------------------------------------------- table lookup
 
-template <bool kL1>
-struct Lookup;
-
-// One LDS read: xd = f (x >> 12) + slot - b = (f-1) q + q + (slot-b).
-template <>
-struct Lookup<true> {
-    template <typename Sh>
-    __device__ static inline uint32_t step(const Sh &sh, uint32_t h, uint32_t, uint32_t x, uint32_t &s)
-    {
-        const uint32_t e = sh.tab[h][x & (kM - 1)];
-        const uint32_t q = x >> kScaleBits;
-        s = e & 0xFF;
-        return __umul24((e >> 8) & 0xFFF, q) + (q + (e >> 20));
-    }
-};
-
-// Two LDS reads: with x = 4096 q + slot,
+// The narrow table's lookup, two LDS reads: with x = 4096 q + slot,
 // f q + slot - b == x - b + (f - 4096) q  (mod 2^32), one signed 24-bit mad.
-template <>
-struct Lookup<false> {
+struct LookupNarrow {
     // sb = 4096 h and fbb = 1024 h: byte offsets of the half's tables
     template <typename Sh>
     __device__ static inline uint32_t step(const Sh &sh, uint32_t sb, uint32_t fbb, uint32_t x, uint32_t &s)
@@ -362,17 +385,17 @@ struct Lookup<false> {
     }
 };
 
-// One decode step of one lane: table lookup, renormalisation from the ring
-// (rank among the half's renormalising lanes via ballot + mbcnt, added to
-// the stream position of the half's next word), decoded byte into the
-// group's stage.  b0, b1 are the half's table bases and hs = 32 h, all held
-// opaque so every address is one instruction.
-template <bool kL1, bool CHECK, int kH, typename Sh>
+// One narrow-table decode step of one lane: table lookup, renormalisation
+// from the ring (rank among the half's renormalising lanes via ballot +
+// mbcnt, added to the stream position of the half's next word), decoded
+// byte into the group's stage.  b0, b1 are the half's table bases and hs =
+// 32 h, all held opaque so every address is one instruction.
+template <bool CHECK, int kH, typename Sh>
 __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, uint32_t b0, uint32_t b1, uint32_t hs,
                                 uint32_t h, uint32_t lane, bool active, uint32_t i)
 {
     uint32_t s;
-    const uint32_t xd = Lookup<kL1>::step(sh, b0, b1, x, s);
+    const uint32_t xd = LookupNarrow::step(sh, b0, b1, x, s);
     // the decoded byte goes to the stage now: its store can fill the wait
     // the ballot's consumers need after the compare.  The store must not
     // see the table byte itself: then the symbol load would be an
@@ -405,6 +428,38 @@ __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, ui
     if (i & 1) rpos = rpos < Sh::kRingWords ? rpos : rpos - Sh::kRingWords;
     asm volatile("" : "+v"(rpos));
     if (!CHECK || active) x = xn;
+}
+
+// One decode step with the wide table (one chunk per wavefront).  The entry
+// e of the slot x holds is known when the step starts: xd = f (x >> 12) +
+// slot - b = (f-1) q + q + (slot-b) needs no read, and the step waits for
+// one LDS latency only: it issues together the read of xd's slot entry
+// (used if the lane keeps xd) and the ring read of its next word with that
+// word's slot entry (used if it renormalises).  The decoded byte is e's low
+// byte, stored to the stage at once.
+template <bool CHECK, typename Sh>
+__device__ __forceinline__ void dec_step_wide(uint32_t &x, uint32_t &e, uint32_t &rpos, Sh &sh, uint32_t b0,
+                                              uint32_t lane, bool active, uint32_t i)
+{
+    const uint32_t q = x >> kScaleBits;
+    const uint32_t xd = __umul24((e >> 8) & 0xFFF, q) + (q + (e >> 20));
+    reinterpret_cast<uint8_t *>(&sh.stage[0][0])[kLanes * i + lane] = (uint8_t)e;
+    const uint32_t et = sh.tab[b0][xd & (kM - 1)];
+    const bool need = (!CHECK || active) && xd < kL;
+    const uint32_t ml = (uint32_t)__ballot(need);
+    const uint32_t widx = __builtin_amdgcn_mbcnt_lo(ml, rpos);  // < Sh::kRingWords + kApron
+    const u32x2 rw = sh.ring2[0][widx];                          // (entry, word)
+    // x = need ? xd << 16 | w : xd, as one byte permute of (xd, w)
+    const uint32_t sel = need ? 0x05040100u : 0x07060504u;
+    const uint32_t xn = __builtin_amdgcn_perm(xd, rw.y, sel);
+    const uint32_t en = need ? rw.x : et;
+    rpos += __popc(ml);
+    if (i % Sh::R::kWrap == Sh::R::kWrap - 1) rpos = rpos < Sh::kRingWords ? rpos : rpos - Sh::kRingWords;
+    asm volatile("" : "+v"(rpos));
+    if (!CHECK || active) {
+        x = xn;
+        e = en;
+    }
 }
 
 // Builds the slot table of half h from the lane's 8 frequencies f[] (symbols
@@ -476,8 +531,11 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
                                             uint64_t total_chunks, uint32_t *err, Opts opts, MakeView make_view)
 {
     constexpr bool kWave = is_wave_view<View>::value;
+    static_assert(!kL1 || kH == 1, "the wide table decodes one chunk per wavefront");
     using Sh = typename std::conditional<kL1, DecSharedL1<kH, kB>, DecSharedL2<kH, kB>>::type;
+    using R = typename Sh::R;
     constexpr uint32_t kRingWords = Sh::kRingWords;
+    constexpr uint32_t D = R::kDepth;
     __shared__ Sh sh;
     const uint32_t lane = threadIdx.x & 31, h = kH == 1 ? 0u : threadIdx.x >> 5;
     const uint64_t k_own = (uint64_t)kH * blockIdx.x + h;
@@ -538,9 +596,22 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         else fbtmp = &sh.fb[h][0];
         build_table<kL1>(sh, h, lane, f, incl - local, fbtmp);
     }
+    // the wide table's refills also write the slot entries of the words they land
+    auto commit = [&](Refill &r) {
+        if constexpr (kL1) refill_commit<R>(cs, r, sh.ring2[0], sh.tab[0]);
+        else refill_commit<R>(cs, r, sh.ring[h]);
+    };
+    auto sync_fill = [&]() {
+        if constexpr (kL1) refill_sync<R>(cs, lane, ok, sh.ring2[0], (const uint32_t *)sh.tab[0]);
+        else refill_sync<R>(cs, lane, ok, sh.ring[h]);
+    };
     __syncthreads();
-    refill_sync<kB>(cs, lane, ok, sh.ring[h]);
+    sync_fill();
     __syncthreads();
+    // wide table: the entry of the slot x holds (a half without a valid
+    // table reads an entry it never uses)
+    uint32_t e = 0;
+    if constexpr (kL1) e = sh.tab[0][x & (kM - 1)];
 
     const uint2 *stage = reinterpret_cast<const uint2 *>(&sh.stage[h][0]);
     const bool put = ok && real;  // this half writes output
@@ -564,6 +635,11 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     }
     asm volatile("" : "+v"(b0), "+v"(b1), "+v"(hs));
     uint32_t rpos = 0;  // cs.ptr modulo the ring size, advanced every step
+    auto step = [&](auto check_tag, bool active, uint32_t i) {
+        constexpr bool CHECK = decltype(check_tag)::value;
+        if constexpr (kL1) dec_step_wide<CHECK>(x, e, rpos, sh, b0, lane, active, i);
+        else dec_step<CHECK, kH>(x, rpos, sh, b0, b1, hs, h, lane, active, i);
+    };
     // Speculation: set when a group consumed a word that had not landed.
     bool overrun = false;
     // One group: due is the refill to write into the ring now, next where
@@ -572,8 +648,8 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     auto group = [&](auto check_tag, uint32_t gg, uint32_t g_last, const Pre &cur, Pre &ahead, Refill &due,
                      Refill &next, bool refills = true) {
         constexpr bool CHECK = decltype(check_tag)::value;
-        refill_commit<kB>(cs, due, sh.ring[h]);
-        next = refill_issue<kB>(cs, lane, ok && refills);
+        commit(due);
+        next = refill_issue<R>(cs, lane, ok && refills);
         // the value loaded for a group past the last is never used
         const uint32_t gn = gg + 2 <= g_last ? gg + 2 : g_last;
         if constexpr (CHECK) ahead = put || kWave ? rv.fetch_checked(kGroupWords * gn + 8 * lane, len) : Pre{};
@@ -583,7 +659,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
 #pragma unroll
         for (uint32_t i = 0; i < kGroup; i++) {
             const bool active = !CHECK || (ok && kLanes * (kGroup * gg + i) + lane < len);
-            dec_step<kL1, CHECK, kH>(x, rpos, sh, b0, b1, hs, h, lane, active, i);
+            step(check_tag, active, i);
         }
         wave_lds_order();
         // unconditional in full groups, so the compiler counts memory
@@ -615,14 +691,14 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     };
     auto fast = [&](auto prev_tag, uint32_t gg, uint32_t g_last, Pre &pv, Refill &due, Refill &next, Pend &pd) {
         constexpr bool PREV = decltype(prev_tag)::value;
-        refill_commit<kB>(cs, due, sh.ring[h]);
+        commit(due);
         const Pend mine{cs.land, rpos};
         uint2 sprev = make_uint2(0u, 0u);
         wave_lds_order();
         if constexpr (PREV) sprev = stage[lane];
 #pragma unroll
         for (uint32_t i = 0; i < kGroup; i++) {
-            dec_step<kL1, false, kH>(x, rpos, sh, b0, b1, hs, h, lane, true, i);
+            step(std::false_type{}, true, i);
             if (i == 0) {
                 // unconditional, so the compiler counts memory operations
                 // exactly: a shadow half writes what its sibling does
@@ -630,67 +706,71 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
                     rv.flush(kGroupWords * (gg - 1) + 8 * lane, sprev, pv);
                     settle(pd, mine.r0);
                 }
-                next = refill_issue<kB>(cs, lane, ok);
+                next = refill_issue<R>(cs, lane, ok);
                 // the value loaded for a group past the last is never used
-                pv = rv.fetch(kGroupWords * (gg + 2 <= g_last ? gg + 2 : g_last) + 8 * lane);
+                pv = rv.fetch(kGroupWords * (gg + D - 1 <= g_last ? gg + D - 1 : g_last) + 8 * lane);
             }
         }
         wave_lds_order();
         pd = mine;
     };
-    // Raw bytes of group g are loaded three groups before its store into
-    // one of three register sets, and the refill issued in group g is
-    // committed in group g + 2, also from one of three sets: the hot loop
-    // runs whole triples of full groups so every set stays in fixed
-    // registers.
-    Refill q0 = refill_none(), q1 = q0, q2 = q0;
-    const uint32_t n3 = nfull / 3 * 3;
-    if (n3) {
+    // Raw bytes of group g are loaded D groups before its store into one of
+    // D register sets, and the refill issued in group g is written to the
+    // ring in group g + D - 1, also from one of D sets: the hot loop runs
+    // whole rounds of D full groups so every set stays in fixed registers.
+    // Group g + j of a round flushes with set j - 1 (mod D) and reloads it
+    // for group g + j + D - 1, writes refill set j + 1 (mod D) and issues
+    // into set j.
+    Refill q[D];
+#pragma unroll
+    for (uint32_t j = 0; j < D; j++) q[j] = refill_none();
+    const uint32_t nD = nfull / D * D;
+    if (nD) {
         const std::false_type no{};
         const std::true_type yes{};
-        Pre pa = rv.fetch(8 * lane);
-        Pre pb = rv.fetch(kGroupWords + 8 * lane);
-        Pre pc;
+        Pre p[D];
+#pragma unroll
+        for (uint32_t j = 0; j + 1 < D; j++) p[j] = rv.fetch(kGroupWords * j + 8 * lane);
         Pend pd{0u, 0u};
-        const uint32_t last = n3 - 1;
-        // the first triple is peeled, so the loop is entered with the
+        const uint32_t last = nD - 1;
+        // the first round is peeled, so the loop is entered with the
         // memory operations in flight that every iteration leaves behind
-        fast(no, 0, last, pc, q1, q0, pd);
-        fast(yes, 1, last, pa, q2, q1, pd);
-        fast(yes, 2, last, pb, q0, q2, pd);
+        fast(no, 0, last, p[D - 1], q[1], q[0], pd);
+#pragma unroll
+        for (uint32_t j = 1; j < D; j++) fast(yes, j, last, p[j - 1], q[(j + 1) % D], q[j], pd);
 #pragma unroll 1
-        for (uint32_t g = 3; g < n3; g += 3) {
-            fast(yes, g, last, pc, q1, q0, pd);
-            fast(yes, g + 1, last, pa, q2, q1, pd);
-            fast(yes, g + 2, last, pb, q0, q2, pd);
+        for (uint32_t g = D; g < nD; g += D) {
+#pragma unroll
+            for (uint32_t j = 0; j < D; j++) fast(yes, g + j, last, p[(j + D - 1) % D], q[(j + 1) % D], q[j], pd);
         }
         // the last full group's epilogue
         wave_lds_order();
-        rv.flush(kGroupWords * last + 8 * lane, stage[lane], pc);
+        rv.flush(kGroupWords * last + 8 * lane, stage[lane], p[D - 1]);
         wave_lds_order();
         settle(pd, rpos);
     }
-    // What is left (at most two full groups and a partial one) runs checked,
+    // What is left (fewer than D full groups and a partial one) runs checked,
     // with refills committed one group after they are issued: first the ones
     // still in flight land, oldest first.
-    refill_commit<kB>(cs, q1, sh.ring[h]);
-    refill_commit<kB>(cs, q2, sh.ring[h]);
-    for (uint32_t g = n3; g < ng; g++) {
+#pragma unroll
+    for (uint32_t j = 1; j < D; j++) commit(q[j]);
+    for (uint32_t g = nD; g < ng; g++) {
         Pre cur = put || kWave ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
         Pre dummy;
-        group(std::true_type{}, g, g, cur, dummy, q0, q0);
+        group(std::true_type{}, g, g, cur, dummy, q[0], q[0]);
     }
     // A chunk whose speculation failed is decoded again from its start,
     // every group checked and preceded by a synchronous fill, and its
     // output written again.
     if (__ballot(overrun)) {
         if constexpr (kWave) rv.reset();
-        refill_commit<kB>(cs, q0, sh.ring[h]);
+        commit(q[0]);
         cs.ptr = cs.fill = cs.land = cs.fpos = 0;
         rpos = 0;
         if (ok) x = reinterpret_cast<const WC_GLOBAL uint32_t *>(cs.base)[lane];
+        if constexpr (kL1) e = sh.tab[0][x & (kM - 1)];
         for (uint32_t g = 0; g < ng; g++) {
-            refill_sync<kB>(cs, lane, ok, sh.ring[h]);
+            sync_fill();
             Pre cur = put || kWave ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
             Pre dummy;
             Refill none = refill_none();

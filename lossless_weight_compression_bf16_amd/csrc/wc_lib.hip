@@ -168,16 +168,23 @@ wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, c
 }
 
 // Decoder variant.  While every chunk fits on the machine at once with one
-// chunk per wavefront and the wide table (8 wavefronts per CU), the run is
-// bound by the serial latency of one chunk, and the wide table's single LDS
-// read per step with no per-half selects is fastest.  With more chunks the
-// narrow table's two chunks per wavefront and 10 wavefronts per CU win.
+// chunk per wavefront and the wide table (8 wavefronts per CU with one-dword
+// refills, 7 with two-dword ones: the LDS decides), the run is bound by the
+// serial latency of one chunk, and the wide table's single LDS wait per step
+// with no per-half selects is fastest.  With more chunks the narrow table's
+// two chunks per wavefront and 10 wavefronts per CU win.
+template <int DT, int kB>
 bool use_wide_table(uint64_t chunks)
 {
+    static const int per_cu = [] {
+        int n = 0;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<DT, true, 1, kB>, 32, 0) == hipSuccess ? n
+                                                                                                             : 0;
+    }();
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-    return chunks <= 8ull * (uint64_t)cus;
+    return chunks <= (uint64_t)per_cu * (uint64_t)cus;
 }
 
 // Refill block (dwords per lane): the stream's words per 8-step group are
@@ -193,7 +200,7 @@ template <int DT, int kB>
 void launch_decode(const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err,
                    hipStream_t stream, Opts opts)
 {
-    if (use_wide_table(chunks)) {
+    if (use_wide_table<DT, kB>(chunks)) {
         hipLaunchKernelGGL((k_decode<DT, true, 1, kB>), dim3((uint32_t)chunks), dim3(32), 0, stream, st, in->raw,
                            in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts);
     } else {
