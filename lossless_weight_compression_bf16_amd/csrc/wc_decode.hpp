@@ -455,7 +455,9 @@ __device__ __forceinline__ void dec_step_wide(uint32_t &x, uint32_t &e, uint32_t
     const uint32_t en = need ? rw.x : et;
     rpos += __popc(ml);
     if (i % Sh::R::kWrap == Sh::R::kWrap - 1) rpos = rpos < Sh::kRingWords ? rpos : rpos - Sh::kRingWords;
-    asm volatile("" : "+v"(rpos));
+    // keeps the cursor in a VGPR; not volatile, so the scheduler may move
+    // the group epilogue into the steps' LDS waits
+    asm("" : "+v"(rpos));
     if (!CHECK || active) {
         x = xn;
         e = en;

@@ -168,23 +168,26 @@ wc_status encode_impl(const SegTable &st, uint64_t chunks, uint64_t raw_total, c
 }
 
 // Decoder variant.  While every chunk fits on the machine at once with one
-// chunk per wavefront and the wide table (8 wavefronts per CU with one-dword
-// refills, 7 with two-dword ones: the LDS decides), the run is bound by the
+// chunk per wavefront and the wide table (LDS-bound: 8 wavefronts per CU
+// with one-dword refills, 7 with two-dword ones), the run is bound by the
 // serial latency of one chunk, and the wide table's single LDS wait per step
 // with no per-half selects is fastest.  With more chunks the narrow table's
 // two chunks per wavefront and 10 wavefronts per CU win.
-template <int DT, int kB>
+constexpr uint32_t kLdsPerCu = 160 * 1024;  // gfx950
+template <int kB>
+constexpr uint32_t wide_waves_per_cu()
+{
+    return kLdsPerCu / (uint32_t)sizeof(DecSharedL1<1, kB>);
+}
+static_assert(wide_waves_per_cu<1>() == 8 && wide_waves_per_cu<2>() == 7, "wide decoder LDS footprint");
+
+template <int kB>
 bool use_wide_table(uint64_t chunks)
 {
-    static const int per_cu = [] {
-        int n = 0;
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<DT, true, 1, kB>, 32, 0) == hipSuccess ? n
-                                                                                                             : 0;
-    }();
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-    return chunks <= (uint64_t)per_cu * (uint64_t)cus;
+    return chunks <= (uint64_t)wide_waves_per_cu<kB>() * (uint64_t)cus;
 }
 
 // Refill block (dwords per lane): the stream's words per 8-step group are
@@ -200,7 +203,7 @@ template <int DT, int kB>
 void launch_decode(const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err,
                    hipStream_t stream, Opts opts)
 {
-    if (use_wide_table<DT, kB>(chunks)) {
+    if (use_wide_table<kB>(chunks)) {
         hipLaunchKernelGGL((k_decode<DT, true, 1, kB>), dim3((uint32_t)chunks), dim3(32), 0, stream, st, in->raw,
                            in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts);
     } else {
