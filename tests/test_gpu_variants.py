@@ -4,8 +4,9 @@ Layouts BF16_REORDER, FP16, FP16_REORDER (the PTWM README's bit reorder and
 2-plane split) and the options TENSOR_TABLE and RAW_FALLBACK: tables, seek
 table, payload and raw planes must equal the oracle's, and the decoded bit
 patterns the input, through both decoder variants (one chunk per wavefront
-below 2,049 chunks, two chunks per wavefront above).  All calls go through
-the C ABI.
+while every chunk fits on a 256-CU device at once: up to 2,048 chunks with
+one-dword refills, 1,792 with two-dword ones; two chunks per wavefront
+above).  All calls go through the C ABI.
 """
 import sys
 
