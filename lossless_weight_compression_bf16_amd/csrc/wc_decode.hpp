@@ -71,8 +71,9 @@ struct Ring {
     static constexpr uint32_t kWrap = kApron / kLanes;
     static constexpr uint32_t kAlloc = kWords + kApron;
     static constexpr uint32_t kAhead = kWords - kBlk;
-    // groups between a refill's load and its write to the ring (and between
-    // a raw-byte load and its use)
+    // register sets of the pipelined group loop: a refill loaded in group g
+    // is written to the ring in group g + kDepth - 1, and a group's raw bytes
+    // are loaded kDepth groups before its store
     static constexpr uint32_t kDepth = 3;
     static_assert(kWords % kBlk == 0, "blocks must not wrap the ring");
     static_assert(kAhead >= kGroupWords, "a synchronous fill must land a whole group's worst case");
