@@ -219,6 +219,42 @@ def test_gpt2_small_set_full(dev, oracle_lib):
     _say(f"[parity] {w.name}: ratio {e.ratio:.4f}")
 
 
+def _mixed_chunks(g, nchunks, tail):
+    """Chunks of varied entropy, one kind each: weights of random scale,
+    heavy-tailed values, uniform 16-bit patterns, a constant, two values, and
+    values confined to a few exponents; then a ragged tail of weights."""
+    parts = []
+    for _ in range(nchunks):
+        kind = int(g.integers(0, 6))
+        if kind == 0:
+            c = _weights(65536, int(g.integers(1 << 30)), float(g.uniform(0.001, 0.2)))
+        elif kind == 1:
+            c = S.f32_to_bf16_bits((g.standard_t(3, 65536) * 0.015).astype(np.float32))
+        elif kind == 2:
+            c = g.integers(0, 65536, 65536, dtype=np.uint64).astype(np.uint16)
+        elif kind == 3:
+            c = np.full(65536, int(g.integers(0, 65536)), np.uint16)
+        elif kind == 4:
+            c = np.where(g.random(65536) < 0.3, 0x3C00, 0xBC80).astype(np.uint16)
+        else:
+            c = ((g.integers(0x78, 0x7C, 65536) << 8) | g.integers(0, 256, 65536)).astype(np.uint16)
+        parts.append(c)
+    parts.append(_weights(tail, int(g.integers(1 << 30))))
+    return np.concatenate(parts)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mixed_entropy_chunks(dev, oracle_lib, seed):
+    """Random mixes of chunk kinds and counts (1 to 12 chunks plus a ragged
+    tail): the one-chunk-per-wavefront decoder with either refill width
+    (chosen by the mix's average bits per symbol), redo passes on the
+    near-uniform chunks, partial last groups and ring wrap-around, all
+    against the oracle's bytes."""
+    g = np.random.default_rng(500 + seed)
+    x = _mixed_chunks(g, int(g.integers(1, 13)), int(g.integers(0, 65536)))
+    _round_trip(x, "bf16", dev, oracle_lib, f"mixed chunks, seed {seed}")
+
+
 def test_deterministic(dev):
     x = _to_dev(_weights(5 * 65536 + 3, 9), dev, "bf16").view(torch.bfloat16)
     a = codec.encode(x).to_host()
