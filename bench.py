@@ -457,11 +457,12 @@ def main():
         if sev is not None:
             sev.record(6, stream)
 
-    payload_bytes = tot.payload_capacity
-    step()
+    # one encode first, so every decode (warm-up included) is given the
+    # payload's real size, which selects the decoder variant
+    B.wc_encode_batch(fmt, h_in, d_in, len(ins), enc_bufs, scratch, scratch.numel(), err, stream, None)
     torch.cuda.synchronize()
     payload_bytes = int(seek[-1].item())
-    for _ in range(max(W - 1, 0)):
+    for _ in range(max(W, 1)):
         step()
     torch.cuda.synchronize()
     if int(err.item()):
