@@ -29,7 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
-DEFAULT_WORKLOAD = "gpt2-small-bf16"
+DEFAULT_WORKLOAD = "moe-experts-bf16"  # the largest single-GPU set (22.5 GB)
+FUSED_DEFAULT_WORKLOAD = "moe-w2-bf16"
 STAGES = ["split_hist", "rans_encode", "scan", "compact"]
 
 
@@ -42,7 +43,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--workload", default=None,
+                   help=f"weight set (default {DEFAULT_WORKLOAD}; with --fused-gemm {FUSED_DEFAULT_WORKLOAD})")
     p.add_argument("--layout", default=None, choices=["bf16", "bf16r", "fp16", "fp16r", "fp32", "fp8e4m3", "fp8e5m2"],
                    help="plane layout (default: the set's own type; fp16* store the set as IEEE half, "
                         "fp8* as FP8 scaled per tensor)")
@@ -218,7 +220,7 @@ def fused_gemm_main(args):
 
     wc.lib()
     dev = torch.device("cuda:0")
-    name = "moe-w2-bf16" if args.workload == DEFAULT_WORKLOAD else args.workload
+    name = args.workload or FUSED_DEFAULT_WORKLOAD
     w = S.workload(name)
     if w.dtype != "bf16":
         raise SystemExit("the fused decode + GEMM takes BF16 sets")
@@ -401,7 +403,7 @@ def main():
 
     wc.lib()
     dev = torch.device("cuda:0")
-    w = S.workload(args.workload)
+    w = S.workload(args.workload or DEFAULT_WORKLOAD)
     layout = args.layout or w.dtype
     if layout.startswith("fp16"):
         w = S.with_dtype(w, "fp16")

@@ -5,10 +5,10 @@
  * ----------------
  * Lossless compression of BF16 / FP32 weight tensors by byte-plane split and
  * rANS coding of the skewed plane:
- *   - BF16 (weight-compression / Split12 README: "byte-split BF16, high byte
- *     reconstructed from a codebook, low byte kept raw"): the high byte
- *     (sign + exponent bits 7..1) is rANS coded; the low byte (exponent bit 0
- *     + 7 mantissa bits) is stored raw.
+ *   - BF16 (weight-compression / Split12 README, the idea paragraph: split
+ *     each value into two bytes, code the upper one, keep the lower one as
+ *     it is): the high byte (sign + exponent bits 7..1) is rANS coded; the
+ *     low byte (exponent bit 0 + 7 mantissa bits) is stored raw.
  *   - FP32 (SMEF README, pass 3: sign / exponent / mantissa byte streams):
  *     the exponent byte is rANS coded; raw = sign bits packed LSB-first
  *     (ceil(n/8) bytes), then mantissa bytes m0 = bits 0-7, m1 = bits 8-15,
@@ -31,9 +31,10 @@
  *     bits) is coded, its low byte raw.  WC_FP16_REORDER applies the bit
  *     reorder first: the coded byte is the 5 exponent bits, the sign and 2
  *     mantissa bits; the raw byte the other 8 mantissa bits.
- *   - WC_FP8_E4M3, WC_FP8_E5M2 ("PTWM" README: for 8-bit floats the bit
- *     reorder moves the exponent into the high nibble, then a 2-plane nibble
- *     split): byte s e4 m3 -> e4 s m3, byte s e5 m2 -> e5 s m2; the high
+ *   - WC_FP8_E4M3, WC_FP8_E5M2 ("PTWM" README, "How it works" steps 1-2:
+ *     for the 8-bit floats the reorder brings the exponent bits to the top
+ *     four bits of the byte, and the planes are split by nibble):
+ *     byte s e4 m3 -> e4 s m3, byte s e5 m2 -> e5 s m2; the high
  *     nibble is coded (16 symbols, same tables and coder), the low nibbles
  *     are raw, two per byte (element 2j in the low nibble of byte j), so the
  *     raw plane is ceil(n/2) bytes.
@@ -176,15 +177,31 @@ int wc_version(void);
 /* Human-readable name of a status code. */
 const char *wc_status_string(wc_status s);
 
-/* Layout of one tensor of n elements.  Pure host function. */
+/* Layout of one tensor of n elements: the size of every buffer the codec
+ * reads or writes for it (PTWM README, "Configuration": the stream is cut
+ * into independently decodable chunks; SMEF README, file table: the
+ * container keeps a seek table).  Pure host function; returns WC_ERR_ARG for
+ * a null out, a bad format word or n > 2^40.  The caller allocates every
+ * buffer from these sizes and owns it. */
 wc_status wc_query_layout(wc_format format, uint64_t n, wc_layout *out);
 
 /* Fills chunk_base and raw_base of segs[0..nseg) (host array; ptr and n are
- * read) and the batch's total layout.  Pure host function. */
+ * read) and the batch's total layout (SMEF README, "Try it yourself": a
+ * whole state dict of named tensors is encoded into one file; here the
+ * tensors of a batch are laid end to end, each chunked on its own).  Pure
+ * host function; WC_ERR_ARG for a bad format word, segs == NULL with
+ * nseg > 0, or an n above 2^40. */
 wc_status wc_plan_batch(wc_format format, wc_segment *segs, uint32_t nseg, wc_layout *total);
 
 /* Encode one tensor of n elements at d_in (FP32 as u32 patterns, the 16-bit
- * layouts as u16 patterns, FP8 as bytes).  Writes out->raw (layout.raw_bytes), out->tables,
+ * layouts as u16 patterns, FP8 as bytes): plane split, per-chunk histogram
+ * and 12-bit table, chunked rANS, seek-table scan and compaction
+ * (weight-compression / Split12 README, the idea paragraph; SMEF README,
+ * passes 3 and 4 of the file table).  All pointers are device pointers owned
+ * by the caller; the call only enqueues on `stream`.  Argument errors
+ * (null or misaligned pointers, a bad format word) return WC_ERR_ARG, a
+ * scratch_bytes below the layout WC_ERR_CAPACITY; a payload that does not
+ * fit payload_bytes sets WC_EF_CAPACITY in *d_err.  Writes out->raw (layout.raw_bytes), out->tables,
  * out->seek and out->payload (at most out->payload_bytes; layout's
  * payload_capacity always suffices).  d_scratch must hold
  * layout.scratch_bytes.  stage_events may be NULL or point to 5 events that
@@ -194,16 +211,26 @@ wc_status wc_encode(wc_format format, const void *d_in, uint64_t n, const wc_buf
                     void *d_scratch, uint64_t scratch_bytes, uint32_t *d_err,
                     hipStream_t stream, hipEvent_t *stage_events);
 
-/* Decode one tensor of n elements into d_out (u32 / u16 / u8 bit patterns).
+/* Decode one tensor of n elements into d_out (u32 / u16 / u8 bit patterns):
+ * every chunk's rANS stream decoded and joined with the raw planes in one
+ * pass (SMEF README, file table: the decoder's full decode;
+ * weight-compression / Split12 README: the round trip is bit for bit;
+ * SeedPack README: the GPU decodes one tensor at a time).  Device pointers
+ * owned by the caller; enqueues on `stream`.  Argument errors return
+ * WC_ERR_ARG; stream errors set WC_EF_* bits in *d_err (see above).
  * With WC_OPT_RAW_FALLBACK a chunk stored raw is copied; its padding must be
  * zero (else WC_EF_BAD_TAIL). */
 wc_status wc_decode(wc_format format, const wc_buffers *in, uint64_t n, void *d_out,
                     uint32_t *d_err, hipStream_t stream);
 
-/* Batched forms: one launch sequence over all chunks of all tensors.
- * h_segs is the host copy of the planned segment array (for validation);
- * d_segs holds the same bytes in device memory (read by the kernels).
- * The scratch size is the batch layout's scratch_bytes. */
+/* Batched forms of wc_encode and wc_decode: one launch sequence over all
+ * chunks of all tensors (SMEF README, "Try it yourself": a state dict is
+ * encoded and decoded as a whole; SeedPack README: a repository is packed
+ * file by file into one archive).  h_segs is the host copy of the planned
+ * segment array (for validation: a plan that does not match wc_plan_batch's
+ * rule is WC_ERR_ARG); d_segs holds the same bytes in device memory (read by
+ * the kernels).  The scratch size is the batch layout's scratch_bytes.
+ * Errors as for wc_encode / wc_decode. */
 wc_status wc_encode_batch(wc_format format, const wc_segment *h_segs, const wc_segment *d_segs,
                           uint32_t nseg, const wc_buffers *out, void *d_scratch,
                           uint64_t scratch_bytes, uint32_t *d_err, hipStream_t stream,
@@ -250,6 +277,17 @@ wc_status wc_decode_gemm_batch(wc_format format, const wc_segment *h_segs, const
  * 1..4096 against boundary and sampled dividends below 2^32.  Returns the
  * number of wrong quotients (0 expected). */
 uint64_t wc_check_division(uint32_t samples_per_divisor);
+
+/* Which decoder wc_decode / wc_decode_batch would launch for num_chunks
+ * chunks of n elements in total with payload_bytes of payload, on the
+ * device that `stream` belongs to (the current device for the null
+ * stream): *one_chunk_per_wave = 1 for the wide-table decoder (one chunk per
+ * wavefront, taken while every chunk fits on that device's compute units at
+ * once), 0 for two chunks per wavefront; *refill_dwords = 1 or 2 (the ring
+ * refill block per lane, 2 above 3.25 bits per coded symbol).  Host
+ * function; WC_ERR_HIP if the stream's device cannot be queried. */
+wc_status wc_decode_variant(wc_format format, uint64_t num_chunks, uint64_t n, uint64_t payload_bytes,
+                            hipStream_t stream, int *one_chunk_per_wave, int *refill_dwords);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,7 @@ CHUNK = 65536
 
 EXPORTS = ["wc_version", "wc_status_string", "wc_query_layout", "wc_plan_batch", "wc_encode",
            "wc_decode", "wc_encode_batch", "wc_decode_batch", "wc_check_division", "wc_tile_order",
-           "wc_decode_gemm_batch"]
+           "wc_decode_gemm_batch", "wc_decode_variant"]
 
 
 class WcError(RuntimeError):
@@ -95,8 +95,9 @@ def lib() -> ctypes.CDLL:
     L.wc_check_division.restype = U64
     L.wc_tile_order.argtypes = [P, P, U32, U32, I, P]
     L.wc_decode_gemm_batch.argtypes = [I, P, P, U32, P, P, U32, ctypes.POINTER(wc_buffers), P, P]
+    L.wc_decode_variant.argtypes = [I, U64, U64, U64, P, ctypes.POINTER(I), ctypes.POINTER(I)]
     for name in ("wc_query_layout", "wc_plan_batch", "wc_encode", "wc_decode", "wc_encode_batch",
-                 "wc_decode_batch", "wc_tile_order", "wc_decode_gemm_batch"):
+                 "wc_decode_batch", "wc_tile_order", "wc_decode_gemm_batch", "wc_decode_variant"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -212,6 +213,16 @@ def wc_decode_gemm_batch(dtype, h_segs, d_segs, nseg: int, h_gemm, d_gemm, m: in
                                     ctypes.cast(h_gemm, ctypes.c_void_p), _ptr(d_gemm), int(m), ctypes.byref(bufs),
                                     _ptr(d_err), _stream(stream))
     _check(rc, "wc_decode_gemm_batch")
+
+
+def wc_decode_variant(dtype, num_chunks: int, n: int, payload_bytes: int, stream=None):
+    """(one_chunk_per_wave, refill_dwords) of the decoder the library would
+    launch on the device of `stream`."""
+    a, b = ctypes.c_int(0), ctypes.c_int(0)
+    rc = lib().wc_decode_variant(_code(dtype), int(num_chunks), int(n), int(payload_bytes), _stream(stream),
+                                 ctypes.byref(a), ctypes.byref(b))
+    _check(rc, "wc_decode_variant")
+    return bool(a.value), int(b.value)
 
 
 def wc_check_division(samples_per_divisor: int = 256) -> int:

@@ -181,11 +181,24 @@ constexpr uint32_t wide_waves_per_cu()
 }
 static_assert(wide_waves_per_cu<1>() == 8 && wide_waves_per_cu<2>() == 7, "wide decoder LDS footprint");
 
-template <int kB>
-bool use_wide_table(uint64_t chunks)
+// The device whose queue `stream` feeds (the current device for the null
+// stream): the decoder variant depends on that device's CU count, not on
+// whichever device happens to be current on the calling thread.
+bool stream_device(hipStream_t stream, int *dev)
 {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (stream) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) return false;
+        *dev = d;
+        return true;
+    }
+    return hipGetDevice(dev) == hipSuccess;
+}
+
+template <int kB>
+bool use_wide_table(uint64_t chunks, int dev)
+{
+    int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
     return chunks <= (uint64_t)wide_waves_per_cu<kB>() * (uint64_t)cus;
 }
@@ -201,9 +214,9 @@ bool use_wide_refills(uint64_t payload_bytes, uint64_t n)
 
 template <int DT, int kB>
 void launch_decode(const SegTable &st, uint64_t chunks, const wc_buffers *in, uint32_t *d_err,
-                   hipStream_t stream, Opts opts)
+                   hipStream_t stream, Opts opts, int dev)
 {
-    if (use_wide_table<kB>(chunks)) {
+    if (use_wide_table<kB>(chunks, dev)) {
         hipLaunchKernelGGL((k_decode<DT, true, 1, kB>), dim3((uint32_t)chunks), dim3(32), 0, stream, st, in->raw,
                            in->tables, in->seek, in->payload, in->payload_bytes, chunks, d_err, opts);
     } else {
@@ -217,14 +230,16 @@ wc_status decode_impl(const SegTable &st, uint64_t chunks, uint64_t n, const wc_
                       hipStream_t stream, Opts opts)
 {
     if (chunks == 0) return WC_OK;
+    int dev = 0;
+    if (!stream_device(stream, &dev)) return WC_ERR_HIP;
     if (opts.crc()) {
         hipLaunchKernelGGL(k_crc32<true>, dim3((uint32_t)chunks), dim3(256), 0, stream, in->seek, in->payload,
                            in->payload_bytes, in->crc, d_err);
     }
     if (use_wide_refills(in->payload_bytes, n))
-        launch_decode<DT, 2>(st, chunks, in, d_err, stream, opts);
+        launch_decode<DT, 2>(st, chunks, in, d_err, stream, opts, dev);
     else
-        launch_decode<DT, 1>(st, chunks, in, d_err, stream, opts);
+        launch_decode<DT, 1>(st, chunks, in, d_err, stream, opts, dev);
     if (opts.raw_fallback()) {
         hipLaunchKernelGGL(k_decode_raw<DT>, dim3((uint32_t)chunks), dim3(256), 0, stream, st, in->raw, in->seek,
                            in->payload, in->payload_bytes, d_err);
@@ -360,6 +375,18 @@ wc_status wc_encode(wc_format format, const void *d_in, uint64_t n, const wc_buf
     if (d_err && !aligned(d_err, 4)) return WC_ERR_ARG;
     SegTable st{nullptr, 0, {reinterpret_cast<uint64_t>(d_in), n, 0, 0}};
     return encode_any(format, st, lay.num_chunks, lay.raw_bytes, out, d_scratch, d_err, stream, stage_events);
+}
+
+wc_status wc_decode_variant(wc_format format, uint64_t num_chunks, uint64_t n, uint64_t payload_bytes,
+                            hipStream_t stream, int *one_chunk_per_wave, int *refill_dwords)
+{
+    if (!valid_format(format) || !one_chunk_per_wave || !refill_dwords) return WC_ERR_ARG;
+    int dev = 0;
+    if (!stream_device(stream, &dev)) return WC_ERR_HIP;
+    const bool wide_refill = use_wide_refills(payload_bytes, n);
+    *refill_dwords = wide_refill ? 2 : 1;
+    *one_chunk_per_wave = wide_refill ? use_wide_table<2>(num_chunks, dev) : use_wide_table<1>(num_chunks, dev);
+    return WC_OK;
 }
 
 wc_status wc_decode(wc_format format, const wc_buffers *in, uint64_t n, void *d_out, uint32_t *d_err,

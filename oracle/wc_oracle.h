@@ -11,9 +11,9 @@
  *   - "SMEF -- blog companion code" README, file table: pass 3 splits each
  *     tensor into sign / exponent / mantissa byte streams; pass 4 codes a
  *     stream with a vectorised rANS coder.
- *   - "weight-compression" README (Split12): BF16 is byte-split, the high byte
- *     is reconstructed from a codebook, the low byte is kept raw, and the
- *     bar is a bit-for-bit round trip.
+ *   - "weight-compression" README (Split12), the idea paragraph: each BF16
+ *     value is cut into its two bytes, the upper one coded against a table
+ *     and the lower one stored unchanged; its bar is an exact round trip.
  *   - "PTWM" README, "How it works": exponent-plane separation by byte split;
  *     "Configuration": large tensors coded as independently decodable chunks.
  * The pages name rANS but fix none of its parameters.  This format fixes them

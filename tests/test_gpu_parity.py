@@ -353,3 +353,20 @@ def test_corrupt_streams_two_chunk_wavefronts(dev, oracle_lib):
             # an undetected change decodes to the same bytes on both sides
             assert np.array_equal(y.cpu().numpy().view(np.uint16), oy), trial
 
+
+
+def test_decoder_variant_follows_the_streams_device(dev):
+    """The decoder is picked from the CU count of the device the stream
+    belongs to: one chunk per wavefront while every chunk fits at once (8
+    wavefronts per CU with one-dword refills, 7 with two-dword ones), two per
+    wavefront above; the same answer on the null stream and on a stream of
+    that device."""
+    from lossless_weight_compression_bf16_amd import _binding as B
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    side = torch.cuda.Stream(device=dev)
+    for stream in (None, side):
+        for per_cu, bytes_per_chunk, dwords in ((8, 22000, 1), (7, 60000, 2)):
+            c = per_cu * cus
+            for chunks, one in ((c, True), (c + 1, False)):
+                got = B.wc_decode_variant("bf16", chunks, chunks * 65536, chunks * bytes_per_chunk, stream)
+                assert got == (one, dwords), (stream, per_cu, chunks, got)

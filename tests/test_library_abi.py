@@ -158,3 +158,41 @@ def test_tile_order_and_gemm_argument_errors_without_launch(L):
     g2[0].x, g2[0].y, g2[0].rows, g2[0].cols = 0x10000, 0x20000, 256, 768
     assert L.wc_decode_gemm_batch(0, ctypes.cast(segs2, ctypes.c_void_p), 0x4000, 1, ctypes.cast(g2, ctypes.c_void_p),
                                   0x3000, 64, ctypes.byref(good), None, None) == B.WC_ERR_ARG
+
+
+# The entry points that carry the codec's work: each declaration's comment
+# names the passage of the pages that defines what it computes.
+CITED = ["wc_query_layout", "wc_plan_batch", "wc_encode", "wc_decode", "wc_encode_batch", "wc_decode_batch",
+         "wc_tile_order", "wc_decode_gemm_batch"]
+
+
+def _comment_before(text, name):
+    """The block comment that ends right before the declaration of name (for
+    wc_decode_batch, declared right after wc_encode_batch, the shared one)."""
+    m = re.search(r"^\s*wc_status\s+" + name + r"\s*\(", text, re.M)
+    assert m, name
+    head = text[: m.start()]
+    if name == "wc_decode_batch":
+        head = head[: head.rindex("wc_status wc_encode_batch")]
+    end = head.rindex("*/")
+    return head[head.rindex("/*", 0, end): end]
+
+
+@pytest.mark.parametrize("name", CITED)
+def test_every_entry_point_cites_its_passage(name):
+    text = open(os.path.join(ROOT, "include", "wc.h")).read()
+    c = _comment_before(text, name)
+    assert re.search(r"(README|docs)", c), f"{name}: no passage cited"
+
+
+def test_decoder_variant_needs_a_device(L):
+    """The decoder variant follows the CU count of the stream's device; with
+    no device there is none to query, and the call says so instead of
+    guessing."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present: covered by the GPU tests")
+    a, b = ctypes.c_int(7), ctypes.c_int(7)
+    assert L.wc_decode_variant(0, 100, 100 * 65536, 1 << 20, None, ctypes.byref(a), ctypes.byref(b)) == B.WC_ERR_HIP
+    assert L.wc_decode_variant(0, 100, 100 * 65536, 1 << 20, None, None, ctypes.byref(b)) == B.WC_ERR_ARG
+    assert L.wc_decode_variant(0x800, 100, 100 * 65536, 1 << 20, None, ctypes.byref(a), ctypes.byref(b)) == B.WC_ERR_ARG
