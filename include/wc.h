@@ -289,6 +289,29 @@ uint64_t wc_check_division(uint32_t samples_per_divisor);
 wc_status wc_decode_variant(wc_format format, uint64_t num_chunks, uint64_t n, uint64_t payload_bytes,
                             hipStream_t stream, int *one_chunk_per_wave, int *refill_dwords);
 
+/* Size of the fixed device array wc_encode_noalloc takes its scratch from
+ * (one per device the library runs on, held until the process ends). */
+#define WC_NOALLOC_SCRATCH_BYTES (128ull << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc: wc_encode
+ * with the encoder's scratch taken from the library's fixed array of
+ * WC_NOALLOC_SCRATCH_BYTES on the stream's device instead of a caller
+ * buffer.  Inputs, outputs, results and errors are those of wc_encode; a
+ * tensor whose layout needs more scratch (more chunks than
+ * wc_noalloc_max_chunks(format): 1,021 for BF16, about 66.9 million
+ * elements) returns WC_ERR_CAPACITY before anything is enqueued.  Calls no
+ * allocator.  Every call on a device shares that device's array and leaves
+ * its contents behind (nothing in it needs clearing): calls that overlap on
+ * one device, from other streams or threads, race and must be serialised by
+ * the caller. */
+wc_status wc_encode_noalloc(wc_format format, const void *d_in, uint64_t n, const wc_buffers *out, uint32_t *d_err,
+                            hipStream_t stream);
+
+/* The most chunks wc_encode_noalloc takes under `format` (0 for a bad
+ * format word).  Pure host function. */
+uint64_t wc_noalloc_max_chunks(wc_format format);
+
 #ifdef __cplusplus
 }
 #endif

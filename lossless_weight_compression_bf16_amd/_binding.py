@@ -34,10 +34,11 @@ EF_NAMES = {EF_BAD_TABLE: "bad table", EF_WORD_OVERRUN: "word overrun",
             EF_BAD_SEEK: "bad seek", EF_CAPACITY: "payload capacity", EF_BAD_CRC: "CRC mismatch"}
 
 CHUNK = 65536
+WC_NOALLOC_SCRATCH_BYTES = 128 << 20  # the fixed device array of wc_encode_noalloc
 
 EXPORTS = ["wc_version", "wc_status_string", "wc_query_layout", "wc_plan_batch", "wc_encode",
            "wc_decode", "wc_encode_batch", "wc_decode_batch", "wc_check_division", "wc_tile_order",
-           "wc_decode_gemm_batch", "wc_decode_variant"]
+           "wc_decode_gemm_batch", "wc_decode_variant", "wc_encode_noalloc", "wc_noalloc_max_chunks"]
 
 
 class WcError(RuntimeError):
@@ -96,8 +97,12 @@ def lib() -> ctypes.CDLL:
     L.wc_tile_order.argtypes = [P, P, U32, U32, I, P]
     L.wc_decode_gemm_batch.argtypes = [I, P, P, U32, P, P, U32, ctypes.POINTER(wc_buffers), P, P]
     L.wc_decode_variant.argtypes = [I, U64, U64, U64, P, ctypes.POINTER(I), ctypes.POINTER(I)]
+    L.wc_encode_noalloc.argtypes = [I, P, U64, ctypes.POINTER(wc_buffers), P, P]
+    L.wc_noalloc_max_chunks.argtypes = [I]
+    L.wc_noalloc_max_chunks.restype = U64
     for name in ("wc_query_layout", "wc_plan_batch", "wc_encode", "wc_decode", "wc_encode_batch",
-                 "wc_decode_batch", "wc_tile_order", "wc_decode_gemm_batch", "wc_decode_variant"):
+                 "wc_decode_batch", "wc_tile_order", "wc_decode_gemm_batch", "wc_decode_variant",
+                 "wc_encode_noalloc"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -194,6 +199,17 @@ def wc_encode_batch(dtype, h_segs, d_segs, nseg: int, bufs: wc_buffers, d_scratc
                                int(nseg), ctypes.byref(bufs), _ptr(d_scratch), int(scratch_bytes),
                                _ptr(d_err), _stream(stream), ev)
     _check(rc, "wc_encode_batch")
+
+
+def wc_encode_noalloc(dtype, d_in, n: int, bufs: wc_buffers, d_err=None, stream=None):
+    """wc_encode with the library's fixed device scratch (no allocation)."""
+    rc = lib().wc_encode_noalloc(_code(dtype), _ptr(d_in), int(n), ctypes.byref(bufs), _ptr(d_err),
+                                 _stream(stream))
+    _check(rc, "wc_encode_noalloc")
+
+
+def wc_noalloc_max_chunks(dtype) -> int:
+    return int(lib().wc_noalloc_max_chunks(_code(dtype)))
 
 
 def wc_decode_batch(dtype, h_segs, d_segs, nseg: int, bufs: wc_buffers, d_err=None, stream=None):

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libwc.so")
-SOURCES = [os.path.join(CSRC, "wc_lib.hip")]
+SOURCES = [os.path.join(CSRC, "wc_lib.hip"), os.path.join(CSRC, "wc_noalloc.hip")]
 
 ARCH = "gfx950"
 
