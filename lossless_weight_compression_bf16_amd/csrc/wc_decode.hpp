@@ -58,16 +58,15 @@ constexpr uint32_t kStageBytes = kLanes * kGroup;    // decoded bytes per group 
 // which would otherwise outrun the refills and take the second pass.
 // A block never covers an unconsumed word: at issue fewer than kAhead words
 // are unconsumed, so with the block fewer than kWords.
-// The ring's first kApron words are repeated after its end, and the cursor
-// is reduced modulo the ring size every kWrap = kApron / 32 steps, so the 32
-// reads of a step never wrap (the wide table's ring reduces it every fourth
-// step, the narrow one every second).
+// The ring's first kApron = 128 words are repeated after its end, and the
+// cursor is reduced modulo the ring size every kWrap = kApron / 32 = 4 steps,
+// so the 32 reads of a step never wrap.
 template <int B, bool kWide = false>
 struct Ring {
     static constexpr int kB = B;
     static constexpr uint32_t kBlk = 2 * kLanes * kB;
     static constexpr uint32_t kWords = kB == 1 ? kGroupWords + kBlk : 512;
-    static constexpr uint32_t kApron = (kWide ? 4 : 2) * kLanes;
+    static constexpr uint32_t kApron = 4 * kLanes;
     static constexpr uint32_t kWrap = kApron / kLanes;
     static constexpr uint32_t kAlloc = kWords + kApron;
     static constexpr uint32_t kAhead = kWords - kBlk;
@@ -423,10 +422,11 @@ __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, ui
     // x = need ? xd << 16 | w : xd, as one byte permute of (xd, w)
     const uint32_t sel = need ? 0x05040100u : 0x07060504u;
     const uint32_t xn = __builtin_amdgcn_perm(xd, w, sel);
-    // the cursor is reduced modulo the ring size every second step (after
-    // one unreduced step it is below kRingWords + 32)
+    // the cursor is reduced modulo the ring size every fourth step (after
+    // three unreduced steps it is below kRingWords + 96, so a step's reads
+    // stay inside the 128-word apron)
     rpos += __popc(half);
-    if (i & 1) rpos = rpos < Sh::kRingWords ? rpos : rpos - Sh::kRingWords;
+    if (i % Sh::R::kWrap == Sh::R::kWrap - 1) rpos = rpos < Sh::kRingWords ? rpos : rpos - Sh::kRingWords;
     asm volatile("" : "+v"(rpos));
     if (!CHECK || active) x = xn;
 }

@@ -561,8 +561,14 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
             wave_lds_order();
             reinterpret_cast<uint2 *>(&estage[h][0])[lane] = b;
             wave_lds_order();
+            // each byte is pinned as a 32-bit value at once, so the load
+            // zero-extends and no mask is needed where it indexes the table
 #pragma unroll
-            for (uint32_t i = 0; i < kEncGroup; i++) sy[i] = stg[kLanes * i + lane];
+            for (uint32_t i = 0; i < kEncGroup; i++) {
+                uint32_t v = stg[kLanes * i + lane];
+                asm("" : "+v"(v));
+                sy[i] = v;
+            }
         };
         uint32_t sy[kEncGroup];
         // g: the group encoded; gl: the group whose load is issued; nx: the
@@ -691,7 +697,14 @@ __global__ __launch_bounds__(1024) void k_scan_apply(const uint2 *__restrict__ m
 // ------------------------------------------------------------------ compact
 
 // Moves chunk k's payload (meta mk) from its slot to dst_off (a chunk that
-// would not fit the capacity is skipped: the scan reports it).
+// would not fit the capacity is skipped: the scan reports it).  Each thread
+// moves runs of 4 consecutive output dwords with one 16-byte load and one
+// 16-byte store (both only 4-byte aligned: the payload offsets are multiples
+// of 4 and the stream starts at any word of the slot), 24 dwords per thread
+// per round, so a weight chunk's payload (about 22 KB) moves in one round
+// with all its loads in flight.
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 __device__ inline void compact_chunk(const uint8_t *__restrict__ slots, uint64_t k, uint2 mk, uint64_t dst_off,
                                      uint8_t *__restrict__ payload, uint64_t capacity)
 {
@@ -706,31 +719,44 @@ __device__ inline void compact_chunk(const uint8_t *__restrict__ slots, uint64_t
     const uint32_t p = mk.y, nw = kMaxWords - p, ndw = (nw + 1) / 2;
     if (tid < 32) dst[tid] = src[tid];
     // word area as dwords: word j is half (j & 1) of dword j / 2; output
-    // dword i holds words p + 2 i and p + 2 i + 1.  Up to 16 dwords per
-    // thread per round, interleaved so every load is coalesced and up to 16
-    // are in flight.
+    // dword i holds words p + 2 i and p + 2 i + 1.  With an odd p each output
+    // dword joins two input dwords, and the run's last one needs the dword
+    // after it.  Reads reach at most 4 dwords past the slot's end, into the
+    // next slot (or the spare slot after the last chunk's); what they bring
+    // in only feeds the zero pad word or is not stored.
     const WC_GLOBAL uint32_t *ws = src + 32 + (p >> 1);
     WC_GLOBAL uint32_t *wd = dst + 32;
     const bool odd = p & 1;
-    constexpr uint32_t U = 16;
-    for (uint32_t i0 = 0; i0 < ndw; i0 += 256 * U) {
-        uint32_t v[U], w[U];
+    constexpr uint32_t U = 6;  // runs of 4 dwords per thread per round
+    for (uint32_t r0 = 0; r0 < ndw; r0 += 256 * 4 * U) {
+        u32x4a4 v[U];
+        uint32_t nx[U];
 #pragma unroll
         for (uint32_t u = 0; u < U; u++) {
-            const uint32_t i = i0 + tid + 256 * u;
-            // with an odd start the last dword's upper word lies one dword
-            // past the slot (the next slot's, or the spare slot after the
-            // last chunk's); the pad mask below drops it
-            v[u] = i < ndw ? ws[i] : 0u;
-            w[u] = odd && i < ndw ? ws[i + 1] : 0u;
+            const uint32_t i = r0 + 4 * (tid + 256 * u);
+            const bool in = i < ndw;
+            v[u] = in ? *reinterpret_cast<const WC_GLOBAL u32x4a4 *>(ws + i) : u32x4a4{0u, 0u, 0u, 0u};
+            nx[u] = odd && in ? ws[i + 4] : 0u;
         }
 #pragma unroll
         for (uint32_t u = 0; u < U; u++) {
-            const uint32_t i = i0 + tid + 256 * u;
+            const uint32_t i = r0 + 4 * (tid + 256 * u);
             if (i >= ndw) continue;
-            uint32_t d = odd ? (v[u] >> 16) | (w[u] << 16) : v[u];
-            if (2 * i + 1 >= nw) d &= 0xFFFFu;  // odd count: zero pad word
-            wd[i] = d;
+            u32x4a4 o = v[u];
+            if (odd) {
+                o.x = __builtin_amdgcn_alignbit(v[u].y, v[u].x, 16);
+                o.y = __builtin_amdgcn_alignbit(v[u].z, v[u].y, 16);
+                o.z = __builtin_amdgcn_alignbit(v[u].w, v[u].z, 16);
+                o.w = __builtin_amdgcn_alignbit(nx[u], v[u].w, 16);
+            }
+            if (i + 4 <= ndw) {
+                if (2 * (i + 3) + 1 >= nw) o.w &= 0xFFFFu;  // odd word count: zero pad word
+                *reinterpret_cast<WC_GLOBAL u32x4a4 *>(wd + i) = o;
+            } else {
+                const uint32_t t[4] = {o.x, o.y, o.z, o.w};
+                for (uint32_t q = 0; q < 4 && i + q < ndw; q++)
+                    wd[i + q] = 2 * (i + q) + 1 >= nw ? t[q] & 0xFFFFu : t[q];
+            }
         }
     }
 }
