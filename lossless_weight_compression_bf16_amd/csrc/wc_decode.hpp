@@ -104,14 +104,38 @@ struct DecSharedL2 {
     uint32_t stage[H][kStageBytes / 4];
 };
 
-// Per-half stream cursor (values uniform within a half).
+// Ring block positions: a refill fills block j of the ring (j < kWords /
+// kBlk <= 7), and the next one block (j + 1) mod n.  j is kept as the
+// selector 0x07070700 | j of a byte permute whose operands hold the
+// successor table (bytes 0-6: next(0) .. next(6), byte 7: 7), so one
+// v_perm_b32 steps it and the upper selector bytes reproduce themselves.
+template <uint32_t n>
+struct BlockCycle {
+    static_assert(n >= 2 && n <= 7, "ring blocks");
+    static constexpr uint32_t next(uint32_t j) { return j + 1 < n ? j + 1 : 0u; }
+    static constexpr uint32_t lo = next(0) | next(1) << 8 | next(2) << 16 | next(3) << 24;
+    static constexpr uint32_t hi = (n > 4 ? next(4) : 0u) | (n > 5 ? next(5) : 0u) << 8 |
+                                   (n > 6 ? next(6) : 0u) << 16 | 7u << 24;
+    static constexpr uint32_t start = 0x07070700u;
+    __device__ static uint32_t step(uint32_t enc) { return __builtin_amdgcn_perm(hi, lo, enc); }
+    __device__ static uint32_t index(uint32_t enc) { return enc & 7u; }
+};
+
+// Per-half stream cursor (values uniform within a half).  A lane's refill
+// dwords for the words from fill on start at byte lane_off + 2 fill of the
+// chunk's payload, clamped to lim, the start of the half's last dword (pair),
+// so a refill past the stream end (or one that is not due) still reads in
+// bounds; a valid stream never consumes a word past its end.  A half without
+// a valid chunk has lane_off = lim = 0 and base at its chunk's table.
 struct Stream {
     const WC_GLOBAL uint8_t *base;    // the chunk's payload: 128 bytes of states, then words
+    uint32_t lane_off;                // offset of the lane's first refill dword(s)
+    uint32_t lim;                     // largest offset a refill load starts at
     uint32_t nw;                      // words in the chunk (pad included, even)
     uint32_t ptr;                     // next word to consume (advanced once per group)
     uint32_t fill;                    // words issued to the ring (landed or in flight)
     uint32_t land;                    // words landed in the ring
-    uint32_t fpos;                    // fill modulo the ring size
+    uint32_t fenc;                    // ring block of the next refill (BlockCycle selector)
     __device__ uint32_t word_pair(uint32_t d) const  // stream dword d
     {
         return *reinterpret_cast<const WC_GLOBAL uint32_t *>(base + 128 + 4 * d);
@@ -120,9 +144,8 @@ struct Stream {
 
 // A refill moves the next block into the ring, kB dwords per lane.  Its
 // loads are issued unconditionally, so the compiler can count outstanding
-// memory operations exactly: when no refill is due they read the chunk's
-// first states, and dwords past the stream end are replaced by ones in
-// bounds (a valid stream never consumes a word past its end).
+// memory operations exactly: when no refill is due they read in bounds
+// data that is never used.
 struct Refill {
     uint32_t v, v1;  // the lane's dwords (v1 with kB = 2)
     uint32_t pos;    // first ring dword the lane writes
@@ -139,30 +162,27 @@ template <typename R>
 __device__ __forceinline__ Refill refill_issue(Stream &st, uint32_t lane, bool on)
 {
     constexpr int kB = R::kB;
+    using C = BlockCycle<R::kWords / R::kBlk>;
     Refill r;
     r.go = on && st.fill - st.ptr < R::kAhead && st.fill < st.nw;
+    const uint32_t uoff = st.lane_off + 2 * st.fill;
+    const uint32_t off = min(uoff, st.lim);
+    const WC_GLOBAL uint32_t *p = reinterpret_cast<const WC_GLOBAL uint32_t *>(st.base + off);
     if constexpr (kB == 1) {
-        // with go, nw >= 2: the clamp stays inside the stream
-        const uint32_t d = min(st.fill / 2 + lane, st.nw / 2 - 1);
-        const uint32_t off = r.go ? 128 + 4 * d : 0u;
-        r.v = *reinterpret_cast<const WC_GLOBAL uint32_t *>(st.base + off);
+        r.v = p[0];
         r.v1 = 0;
         r.first = true;
     } else {
-        // dwords d, d + 1 from d0 = min(d, nw/2 - 2): with go, nw >= 2, so
-        // d0 >= -1 and the pair starts at most one dword into the states
-        const int32_t d = (int32_t)(st.fill / 2 + 2 * lane);
-        const int32_t d0 = min(d, (int32_t)(st.nw / 2) - 2);
-        const uint32_t off = r.go ? (uint32_t)(128 + 4 * d0) : 0u;
-        const WC_GLOBAL uint32_t *p = reinterpret_cast<const WC_GLOBAL uint32_t *>(st.base + off);
+        // clamped: the pair starts before the lane's first dword, which is
+        // then the pair's second (or past the end, like the dword after it)
         r.v = p[0];
         r.v1 = p[1];
-        r.first = d0 == d;
+        r.first = off == uoff;
     }
-    r.pos = st.fpos / 2 + kB * lane;
+    r.pos = (R::kBlk / 2) * C::index(st.fenc) + kB * lane;
     if (r.go) {
         st.fill += R::kBlk;
-        st.fpos = st.fpos + R::kBlk < R::kWords ? st.fpos + R::kBlk : 0u;
+        st.fenc = C::step(st.fenc);
     }
     return r;
 }
@@ -237,15 +257,23 @@ struct RawView16 {  // the 16-bit layouts
     struct Pre {
         uint2 v;
     };
+    const WC_GLOBAL uint8_t *lol;  // lo + the lane's 8 elements of a group
     __device__ void init(const uint8_t *raw, const wc_segment &sg, uint64_t start)
     {
         lo = gptr(raw) + sg.raw_base + start;
+        lol = lo + 8 * (threadIdx.x & 31);
         out = gptr<uint16_t>(sg.ptr) + start;
     }
     // elements [e, e + 8), all inside the chunk, e a multiple of 8
     __device__ Pre fetch(uint32_t e) const
     {
         const WC_GLOBAL uint32_t *p = reinterpret_cast<const WC_GLOBAL uint32_t *>(lo + e);
+        return Pre{make_uint2(p[0], p[1])};
+    }
+    // the lane's elements of full group g (g uniform: one 64-bit add)
+    __device__ Pre fetch_group(uint32_t g) const
+    {
+        const WC_GLOBAL uint32_t *p = reinterpret_cast<const WC_GLOBAL uint32_t *>(lol + (uint64_t)(kGroupWords * g));
         return Pre{make_uint2(p[0], p[1])};
     }
     __device__ void flush(uint32_t e, uint2 sym, const Pre &p) const
@@ -295,13 +323,20 @@ struct RawView8 {
     struct Pre {
         uint32_t v;
     };
+    const WC_GLOBAL uint8_t *lol;  // lo + the raw bytes of the lane's 8 elements of a group
     __device__ void init(const uint8_t *raw, const wc_segment &sg, uint64_t start)
     {
         lo = gptr(raw) + sg.raw_base + start / 2;
+        lol = lo + 4 * (threadIdx.x & 31);
         out = gptr<uint8_t>(sg.ptr) + start;
     }
     // elements [e, e + 8), all inside the chunk, e a multiple of 8
     __device__ Pre fetch(uint32_t e) const { return Pre{*reinterpret_cast<const WC_GLOBAL uint32_t *>(lo + e / 2)}; }
+    // the lane's elements of full group g (g uniform)
+    __device__ Pre fetch_group(uint32_t g) const
+    {
+        return Pre{*reinterpret_cast<const WC_GLOBAL uint32_t *>(lol + (uint64_t)(kGroupWords / 2 * g))};
+    }
     __device__ static u32x2 join(uint2 sym, uint32_t r)
     {
         const uint32_t a = r & 0x0F0F0F0Fu, b = (r >> 4) & 0x0F0F0F0Fu;  // elements 0,2,4,6 / 1,3,5,7
@@ -349,6 +384,7 @@ struct RawView32 {
     // the mantissa planes have no alignment guarantee: they are read with
     // byte loads when the group is written out
     __device__ Pre fetch(uint32_t) const { return Pre{0}; }
+    __device__ Pre fetch_group(uint32_t) const { return Pre{0}; }
     __device__ Pre fetch_checked(uint32_t, uint32_t) const { return Pre{0}; }
     __device__ void flush_checked(uint32_t e, uint2 sym, const Pre &, uint32_t len) const
     {
@@ -553,8 +589,9 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     const uint32_t len = (uint32_t)min((uint64_t)kChunk, sg.n - start);
     const uint64_t tix = opts.tensor_table() ? sidx : k;
     // A half with a bad seek entry still issues its refill loads (never
-    // used): they read the first dword at base, here the chunk's own table.
-    Stream cs{gptr(reinterpret_cast<const uint8_t *>(tables + tix * 256)), 0, 0, 0, 0, 0};
+    // used): they read the first dword(s) at base, here the chunk's own table.
+    Stream cs{gptr(reinterpret_cast<const uint8_t *>(tables + tix * 256)), 0, 0, 0, 0, 0, 0,
+              BlockCycle<R::kWords / R::kBlk>::start};
     uint32_t x = kL;
     // a chunk stored raw (WC_OPT_RAW_FALLBACK) takes no part in the rANS
     // loop (like a bad one, but reports nothing): k_decode_raw copies it
@@ -571,6 +608,11 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         } else {
             cs.base = gptr(payload + a);
             cs.nw = (uint32_t)min<uint64_t>((b - a - 128) / 2, 2ull * kMaxWords + 2);
+            // dword d of the stream is at 128 + 4 d; the lane's first refill
+            // starts at dword kB lane, the last load at dword nw/2 - kB (for
+            // nw < 2 kB that is one of the states: still in bounds)
+            cs.lane_off = 128 + 4 * kB * lane;
+            cs.lim = 128 - 4 * kB + 2 * cs.nw;
             x = reinterpret_cast<const WC_GLOBAL uint32_t *>(cs.base)[lane];
         }
     }
@@ -656,7 +698,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         // the value loaded for a group past the last is never used
         const uint32_t gn = gg + 2 <= g_last ? gg + 2 : g_last;
         if constexpr (CHECK) ahead = put || kWave ? rv.fetch_checked(kGroupWords * gn + 8 * lane, len) : Pre{};
-        else ahead = rv.fetch(kGroupWords * gn + 8 * lane);
+        else ahead = rv.fetch_group(gn);
         const uint32_t landed = cs.land, r0 = rpos;
         wave_lds_order();
 #pragma unroll
@@ -673,8 +715,10 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
             rv.flush(kGroupWords * gg + 8 * lane, stage[lane], cur);
         }
         wave_lds_order();
-        // words this group consumed (at most 256, less than the ring)
-        const uint32_t used = rpos >= r0 ? rpos - r0 : rpos + kRingWords - r0;
+        // words this group consumed (at most 256, less than the ring): the
+        // cursor difference, plus the ring size if the cursor wrapped
+        const uint32_t dr = rpos - r0;
+        const uint32_t used = min(dr, dr + kRingWords);
         overrun |= cs.ptr + used > landed;
         cs.ptr += used;
     };
@@ -688,7 +732,8 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         uint32_t landed, r0;  // words landed at the group's start, its starting cursor
     };
     auto settle = [&](const Pend &pd, uint32_t r_end) {
-        const uint32_t used = r_end >= pd.r0 ? r_end - pd.r0 : r_end + kRingWords - pd.r0;
+        const uint32_t dr = r_end - pd.r0;
+        const uint32_t used = min(dr, dr + kRingWords);
         overrun |= cs.ptr + used > pd.landed;
         cs.ptr += used;
     };
@@ -711,7 +756,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
                 }
                 next = refill_issue<R>(cs, lane, ok);
                 // the value loaded for a group past the last is never used
-                pv = rv.fetch(kGroupWords * (gg + D - 1 <= g_last ? gg + D - 1 : g_last) + 8 * lane);
+                pv = rv.fetch_group(gg + D - 1 <= g_last ? gg + D - 1 : g_last);
             }
         }
         wave_lds_order();
@@ -733,7 +778,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         const std::true_type yes{};
         Pre p[D];
 #pragma unroll
-        for (uint32_t j = 0; j + 1 < D; j++) p[j] = rv.fetch(kGroupWords * j + 8 * lane);
+        for (uint32_t j = 0; j + 1 < D; j++) p[j] = rv.fetch_group(j);
         Pend pd{0u, 0u};
         const uint32_t last = nD - 1;
         // the first round is peeled, so the loop is entered with the
@@ -768,7 +813,8 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     if (__ballot(overrun)) {
         if constexpr (kWave) rv.reset();
         commit(q[0]);
-        cs.ptr = cs.fill = cs.land = cs.fpos = 0;
+        cs.ptr = cs.fill = cs.land = 0;
+        cs.fenc = BlockCycle<R::kWords / R::kBlk>::start;
         rpos = 0;
         if (ok) x = reinterpret_cast<const WC_GLOBAL uint32_t *>(cs.base)[lane];
         if constexpr (kL1) e = sh.tab[0][x & (kM - 1)];

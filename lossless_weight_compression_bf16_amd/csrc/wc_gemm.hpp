@@ -220,6 +220,8 @@ struct GemmView {
         fetch_x(p, e);
         return p;
     }
+    // the lane's elements of full group g
+    __device__ Pre fetch_group(uint32_t g) const { return fetch(kGroupWords * g + 8 * (L & 31)); }
     __device__ Pre fetch_checked(uint32_t e, uint32_t) const
     {
         Pre p;
