@@ -422,6 +422,11 @@ uint32_t wco_decode_chunk(const uint8_t *p, uint64_t size, const uint16_t freq[2
 
     uint32_t x[ORC_LANES];
     for (uint32_t l = 0; l < ORC_LANES; l++) x[l] = get_u32(p + 4 * l);
+    /* Every state stays in [L, 2^32) (the interval rANS keeps its state in),
+       so the encoder's final states, stored first, are never below L: a
+       chunk that stores one is no encoding and is rejected before a step. */
+    for (uint32_t l = 0; l < ORC_LANES; l++)
+        if (x[l] < ORC_L) return WCO_EF_BAD_FINAL_STATE;
 
     uint64_t ptr = 128;
     uint32_t steps = (n + ORC_LANES - 1) / ORC_LANES;

@@ -85,6 +85,8 @@ def py_decode(payload, f, n):
         owner += [s] * f[s]
         acc += f[s]
     x = list(struct.unpack_from(f"<{LANES}I", payload, 0))
+    if any(v < L for v in x):  # the stored final states lie in [L, 2^32)
+        return None
     pos = 128
     out = []
     for j in range(n):  # step ascending, lane ascending

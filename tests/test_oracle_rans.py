@@ -232,3 +232,102 @@ def test_corruption_never_crashes(oracle_lib):
         if err or not np.array_equal(y, x):
             detected += 1
     assert detected >= 55
+
+
+# ----------------------------------------------- the state interval [L, 2^32)
+
+@pytest.mark.parametrize("kind", ["weights", "uniform", "rare", "single"])
+def test_stored_states_lie_in_the_state_interval(oracle_lib, kind):
+    """The encoder keeps every state in [L, 2^32), so the 32 final states it
+    stores in front of a chunk are all at least L, whatever the symbols."""
+    g = np.random.default_rng(31)
+    for n in (1, 33, 4097, 65536):
+        if kind == "weights":
+            sym = (_weights_like(g, n) >> 8).astype(np.uint8)
+        elif kind == "uniform":
+            sym = g.integers(0, 256, n).astype(np.uint8)
+        elif kind == "rare":  # one frequent symbol, 255 of frequency 1
+            sym = np.full(n, 7, np.uint8)
+            sym[g.permutation(n)[: min(n, 255)]] = np.arange(min(n, 255)).astype(np.uint8) + 8
+        else:
+            sym = np.full(n, 200, np.uint8)
+        f = oracle_lib.normalize(oracle_lib.histogram(sym))
+        st = oracle_lib.encode_chunk(sym, f)[:128].view("<u4")
+        assert st.min() >= L, (kind, n)
+
+
+def test_a_stored_state_below_L_is_rejected(oracle_lib):
+    """A chunk whose stored states include one below L is no encoding: the
+    decoder reports WCO_EF_BAD_FINAL_STATE, and nothing else, before any
+    step; L itself is still accepted (the state of an all-same chunk)."""
+    g = np.random.default_rng(32)
+    sym = (_weights_like(g, 4096) >> 8).astype(np.uint8)
+    f = oracle_lib.normalize(oracle_lib.histogram(sym))
+    p = oracle_lib.encode_chunk(sym, f)
+    for lane, v in ((0, 0), (5, L - 1), (31, 1)):
+        q = p.copy()
+        q[4 * lane:4 * lane + 4] = np.frombuffer(np.uint32(v).tobytes(), np.uint8)
+        _, err = oracle_lib.decode_chunk(q, f, sym.size)
+        assert err == oracle_lib.EF_BAD_FINAL_STATE, (lane, v, err)
+    same = np.full(100, 9, np.uint8)
+    fs = oracle_lib.normalize(oracle_lib.histogram(same))
+    ps = oracle_lib.encode_chunk(same, fs)
+    out, err = oracle_lib.decode_chunk(ps, fs, 100)
+    assert err == 0 and np.array_equal(out, same)
+
+
+def _renorm_runs(freq, x, words):
+    """Decode steps of one lane from state x, renormalising from `words`;
+    returns the per-step renormalisation flags (plain integer arithmetic)."""
+    b = np.concatenate([[0], np.cumsum(freq)[:-1]]).astype(np.int64)
+    owner = np.repeat(np.arange(256), freq)
+    flags = []
+    wi = 0
+    for _ in range(len(words)):
+        slot = x % 4096
+        s = owner[slot]
+        x = int(freq[s]) * (x >> 12) + slot - int(b[s])
+        r = x < L
+        if r:
+            x = (x << 16) | int(words[wi])
+            wi += 1
+        flags.append(r)
+    return flags
+
+
+def test_at_most_three_renormalisations_in_a_row():
+    """From a state in [L, 2^32) a lane renormalises at most three steps in a
+    row (so at most 6 words in 8 steps): the bound the GPU decoder sizes its
+    stream ring by.  The adversary below is tight: 255 symbols of frequency
+    1, the smallest state L, and words that always land in their slots."""
+    freq = np.ones(256, np.int64)
+    freq[255] = 4096 - 255
+    words = [0] * 64  # slot 0 (symbol 0, frequency 1), smallest high bits
+    flags = _renorm_runs(freq, L, words)
+    runs, run, best8 = [], 0, 0
+    for t, r in enumerate(flags):
+        run = run + 1 if r else 0
+        runs.append(run)
+    for t0 in range(0, len(flags) - 7):
+        best8 = max(best8, sum(flags[t0:t0 + 8]))
+    assert max(runs) == 3 and best8 == 6
+    # random tables, states and words never exceed it
+    g = np.random.default_rng(33)
+    for trial in range(300):
+        k = int(g.integers(1, 257))
+        freq = np.zeros(256, np.int64)
+        idx = g.choice(256, k, replace=False)
+        cut = np.sort(g.choice(np.arange(1, 4096), k - 1, replace=False)) if k > 1 else np.array([], np.int64)
+        freq[idx] = np.diff(np.concatenate([[0], cut, [4096]]))
+        if trial % 3 == 0:  # many rare symbols
+            freq[:] = 1
+            freq[int(g.integers(0, 256))] = 4096 - 255
+        x = int(g.integers(L, 1 << 32))
+        words = g.integers(0, 65536, 96).tolist()
+        flags = _renorm_runs(freq, x, words)
+        run = 0
+        for t, r in enumerate(flags):
+            run = run + 1 if r else 0
+            assert run <= 3, trial
+        for t0 in range(0, len(flags) - 7):
+            assert sum(flags[t0:t0 + 8]) <= 6, trial
