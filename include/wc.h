@@ -116,7 +116,7 @@ typedef enum {
 /* Device error bits (OR-ed into *d_err). */
 #define WC_EF_BAD_TABLE 1u       /* a chunk's table does not sum to 4096 */
 #define WC_EF_WORD_OVERRUN 2u    /* decoding wanted more words than the chunk holds */
-#define WC_EF_BAD_FINAL_STATE 4u /* a lane did not return to the initial state */
+#define WC_EF_BAD_FINAL_STATE 4u /* a lane did not return to the initial state, or a stored state is below 2^16 */
 #define WC_EF_BAD_TAIL 8u        /* words left over, or a non-zero pad word */
 #define WC_EF_BAD_SEEK 16u       /* seek entries out of order, misaligned or past payload_bytes */
 #define WC_EF_CAPACITY 32u       /* encode: the payload did not fit payload_bytes */

@@ -45,8 +45,17 @@
 namespace wc {
 
 constexpr uint32_t kGroup = 8;                       // steps per group
-constexpr uint32_t kGroupWords = kLanes * kGroup;    // most words one group consumes
+constexpr uint32_t kGroupWords = kLanes * kGroup;    // lane-steps of a group per half
 constexpr uint32_t kStageBytes = kLanes * kGroup;    // decoded bytes per group per half
+// Most words one group of one half consumes.  The decoder checks that every
+// stored state is at least L = 2^16; then every state stays in [L, 2^32):
+// a step gives x' = f q + slot - b >= f q >= 16 f (q = x >> 12 >= 16), and a
+// renormalised state x' 2^16 + w is at least 16 f 2^16.  So a lane that
+// renormalises at steps t, t+1, ... has x'_t >= 16 f_t, q_(t+1) >= 256 f_t,
+// x'_(t+1) >= 256 f_t f_(t+1), ..., x'_(t+3) >= 2^16 f_t f_(t+1) f_(t+2)
+// f_(t+3) >= 2^16: four renormalisations in a row are impossible, and a
+// lane takes at most 6 words in 8 steps.
+constexpr uint32_t kGroupMaxWords = 6 * kLanes;
 
 // Ring geometry for refills of kB dwords per lane.  A refill moves a block
 // of 64 kB words, at most one per group, issued while fewer than kAhead
@@ -55,27 +64,31 @@ constexpr uint32_t kStageBytes = kLanes * kGroup;    // decoded bytes per group 
 // group, and that must exceed r.  kB = 1 (320-word ring, kAhead 256) covers
 // weights (r about 45); kB = 2 (512-word ring, kAhead 384, 128-word blocks)
 // covers coded bytes of up to 8 bits, e.g. the FP16 high byte (r about 88),
-// which would otherwise outrun the refills and take the second pass.
+// which would otherwise outrun the refills and take the second pass.  The
+// symbol-carrying ring of the narrow one-dword decoder (kSym) has 256 words
+// (kAhead 192: r up to about 56).
 // A block never covers an unconsumed word: at issue fewer than kAhead words
 // are unconsumed, so with the block fewer than kWords.
-// The ring's first kApron = 128 words are repeated after its end, and the
-// cursor is reduced modulo the ring size every kWrap = kApron / 32 = 4 steps,
-// so the 32 reads of a step never wrap.
-template <int B, bool kWide = false>
+// The ring's first kApron words (128; 64 with kSym) are repeated after its
+// end, and the cursor is reduced modulo the ring size every kWrap = kApron /
+// 32 steps, so the 32 reads of a step never wrap.
+template <int B, bool kWide = false, bool kSym = false>
 struct Ring {
     static constexpr int kB = B;
     static constexpr uint32_t kBlk = 2 * kLanes * kB;
-    static constexpr uint32_t kWords = kB == 1 ? kGroupWords + kBlk : 512;
-    static constexpr uint32_t kApron = 4 * kLanes;
+    static constexpr uint32_t kWords = kSym ? 256u : kB == 1 ? kGroupWords + kBlk : 512u;
+    static constexpr uint32_t kApron = (kSym ? 2 : 4) * kLanes;
     static constexpr uint32_t kWrap = kApron / kLanes;
     static constexpr uint32_t kAlloc = kWords + kApron;
     static constexpr uint32_t kAhead = kWords - kBlk;
+    static constexpr bool kPow2 = (kWords & (kWords - 1)) == 0;
     // register sets of the pipelined group loop: a refill loaded in group g
     // is written to the ring in group g + kDepth - 1, and a group's raw bytes
     // are loaded kDepth groups before its store
     static constexpr uint32_t kDepth = 3;
     static_assert(kWords % kBlk == 0, "blocks must not wrap the ring");
-    static_assert(kAhead >= kGroupWords, "a synchronous fill must land a whole group's worst case");
+    static_assert(kAhead >= kGroupMaxWords, "a synchronous fill must land a whole group's worst case");
+    static_assert(!kSym || kB == 1, "the symbol-carrying ring takes one-dword refills");
 };
 
 // H = chunks per wavefront (one per 32-lane half).  The wide table's ring
@@ -101,6 +114,25 @@ struct DecSharedL2 {
     uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
     uint32_t fb[H][256];                    // b | (f - 4096) << 16
     uint32_t ring[H][R::kAlloc / 2];
+    uint32_t stage[H][kStageBytes / 4];
+};
+
+// The narrow table with a symbol-carrying ring (one-dword refills): next to
+// each stream word the symbol of the slot the word brings into a
+// renormalising state, looked up when the word lands.  A renormalising lane
+// takes its next symbol from the ring read that brings its word, a lane that
+// keeps x' reads the symbol of x' meanwhile, so a step waits for two
+// dependent LDS reads ((b, f) of the current symbol, then word and symbol)
+// instead of three.  12,672 B per wavefront: ten 1,280-byte LDS granules,
+// 12 wavefronts per CU like DecSharedL2<2, 1>.
+template <int H>
+struct DecSharedS {
+    using R = Ring<1, false, true>;
+    static constexpr uint32_t kRingWords = R::kWords;
+    uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
+    uint32_t fb[H][256];                    // b | (f - 4096) << 16
+    uint32_t ring[H][R::kAlloc / 2];        // stream words, two per dword
+    uint32_t rsym[H][R::kAlloc / 4];        // per ring word: sym[word & 4095]
     uint32_t stage[H][kStageBytes / 4];
 };
 
@@ -206,6 +238,27 @@ __device__ __forceinline__ void refill_commit(Stream &st, Refill &r, uint32_t *r
     }
 }
 
+// The symbol-carrying ring: each landed word is written with the symbol of
+// its slot (sym is the half's slot -> symbol bytes).
+template <typename R>
+__device__ __forceinline__ void refill_commit(Stream &st, Refill &r, uint32_t *ring, uint32_t *rsym,
+                                              const uint8_t *sym)
+{
+    static_assert(R::kB == 1, "one dword (two words) per lane");
+    if (r.go) {
+        const uint32_t s0 = sym[r.v & (kM - 1)], s1 = sym[(r.v >> 16) & (kM - 1)];
+        const uint16_t ss = (uint16_t)(s0 | s1 << 8);
+        ring[r.pos] = r.v;
+        reinterpret_cast<uint16_t *>(rsym)[r.pos] = ss;
+        if (r.pos < R::kApron / 2) {
+            ring[R::kWords / 2 + r.pos] = r.v;
+            reinterpret_cast<uint16_t *>(rsym)[R::kWords / 2 + r.pos] = ss;
+        }
+        st.land += R::kBlk;
+        r.go = false;
+    }
+}
+
 // The wide table's ring: each landed word is written with its slot's entry.
 // The lane's words start at ring word 2 r.pos (even), so each pair of words
 // is one aligned 16-byte store.
@@ -231,16 +284,16 @@ __device__ __forceinline__ void refill_commit(Stream &st, Refill &r, u32x2 *ring
     }
 }
 
-// Lands what the next group may need (256 words, or the rest of the
-// stream): up to 256 / block blocks, loaded together and then written.
-// Only called with nothing in flight, so issued equals landed.
+// Lands what the next group may need (kGroupMaxWords words, or the rest of
+// the stream) in blocks loaded together and then written.  Only called with
+// nothing in flight, so issued equals landed.
 template <typename R, typename... Sink>
 __device__ __forceinline__ void refill_sync(Stream &st, uint32_t lane, bool ok, Sink... sink)
 {
-    constexpr uint32_t n = kGroupWords / R::kBlk;
+    constexpr uint32_t n = (kGroupMaxWords + R::kBlk - 1) / R::kBlk;
     Refill r[n];
 #pragma unroll
-    for (uint32_t j = 0; j < n; j++) r[j] = refill_issue<R>(st, lane, ok && st.fill - st.ptr < kGroupWords);
+    for (uint32_t j = 0; j < n; j++) r[j] = refill_issue<R>(st, lane, ok && st.fill - st.ptr < kGroupMaxWords);
 #pragma unroll
     for (uint32_t j = 0; j < n; j++) refill_commit<R>(st, r[j], sink...);
 }
@@ -467,6 +520,52 @@ __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, ui
     if (!CHECK || active) x = xn;
 }
 
+// One narrow-table step with the symbol-carrying ring.  s, the symbol of
+// the slot x holds, is known when the step starts: it is stored to the
+// stage and gives (b, f - 4096), hence x' (one signed 24-bit mad).  Then
+// the lane reads, in one batch, its ring word at its renormalisation rank
+// and one symbol byte: the ring's symbol of that word if it renormalises,
+// else the slot table's symbol of x' (an address select, so the byte is a
+// single zero-extending load).  The cursor is reduced modulo the ring
+// every second step (a step's reads end below kRingWords + 64).  sb = 4096
+// h and fbb = 1024 h are the half's table offsets, hs = 32 h, all opaque.
+template <bool CHECK, typename Sh>
+__device__ __forceinline__ void dec_step_sym(uint32_t &x, uint32_t &s, uint32_t &rpos, Sh &sh, uint32_t sb,
+                                             uint32_t fbb, uint32_t hs, uint32_t h, uint32_t lane, bool active,
+                                             uint32_t i)
+{
+    reinterpret_cast<uint8_t *>(&sh.stage[h][0])[kLanes * i + lane] = (uint8_t)s;
+    const uint8_t *fbt = reinterpret_cast<const uint8_t *>(&sh.fb[0][0]);
+    const uint32_t fb = *reinterpret_cast<const uint32_t *>(fbt + ((s << 2) | fbb));
+    const uint32_t xd = (uint32_t)__mul24((int32_t)fb >> 16, (int32_t)(x >> kScaleBits)) + (x - (fb & 0xFFFF));
+    const bool need = (!CHECK || active) && xd < kL;
+    const uint64_t m = __ballot(need);
+    const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
+    // rank within the own half (see dec_step)
+    const uint32_t lo = __builtin_amdgcn_mbcnt_lo(ml, rpos);
+    const uint32_t hi = __builtin_amdgcn_mbcnt_hi(mh, rpos);
+    const uint32_t widx = h ? hi : lo;  // < Sh::kRingWords + 64
+    const uint32_t half = (uint32_t)(m >> hs);
+    const uint32_t w = reinterpret_cast<const uint16_t *>(&sh.ring[h][0])[widx];
+    // byte offsets from the start of the slot tables (sym[0])
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(&sh.sym[0][0]);
+    const uint32_t at_ring = (uint32_t)(reinterpret_cast<const uint8_t *>(&sh.rsym[h][0]) - base) + widx;
+    const uint32_t at_slot = (xd & (kM - 1)) | sb;
+    uint32_t sn = base[need ? at_ring : at_slot];
+    // the next step's stage store must not see the byte itself: the load
+    // would then be any-extending and the (b, f) address would need a mask
+    asm("" : "+v"(sn));
+    const uint32_t sel = need ? 0x05040100u : 0x07060504u;
+    const uint32_t xn = __builtin_amdgcn_perm(xd, w, sel);
+    rpos += __popc(half);
+    if (i % Sh::R::kWrap == Sh::R::kWrap - 1) rpos &= Sh::kRingWords - 1;
+    asm volatile("" : "+v"(rpos));
+    if (!CHECK || active) {
+        x = xn;
+        s = sn;
+    }
+}
+
 // One decode step with the wide table (one chunk per wavefront).  The entry
 // e of the slot x holds is known when the step starts: xd = f (x >> 12) +
 // slot - b = (f-1) q + q + (slot-b) needs no read, and the step waits for
@@ -571,7 +670,11 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
 {
     constexpr bool kWave = is_wave_view<View>::value;
     static_assert(!kL1 || kH == 1, "the wide table decodes one chunk per wavefront");
-    using Sh = typename std::conditional<kL1, DecSharedL1<kH, kB>, DecSharedL2<kH, kB>>::type;
+    // the narrow table with one-dword refills carries symbols in its ring
+    constexpr bool kSym = !kL1 && kB == 1;
+    using Sh = typename std::conditional<
+        kL1, DecSharedL1<kH, kB>,
+        typename std::conditional<kSym, DecSharedS<kH>, DecSharedL2<kH, kB>>::type>::type;
     using R = typename Sh::R;
     constexpr uint32_t kRingWords = Sh::kRingWords;
     constexpr uint32_t D = R::kDepth;
@@ -635,6 +738,15 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         bits |= WC_EF_BAD_TABLE;
         ok = false;
     }
+    // every stored state is at least L (no encoder run ends below it); this
+    // keeps every state in [L, 2^32) and a group within kGroupMaxWords words
+    {
+        const uint64_t low = __ballot(ok && x < kL);
+        if (ok && (uint32_t)(low >> (32 * h)) != 0) {
+            bits |= WC_EF_BAD_FINAL_STATE;
+            ok = false;
+        }
+    }
     if (ok) {
         uint32_t *fbtmp;
         if constexpr (kL1) fbtmp = &sh.fbtmp[h][0];
@@ -642,21 +754,31 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         build_table<kL1>(sh, h, lane, f, incl - local, fbtmp);
     }
     // the wide table's refills also write the slot entries of the words they land
+    // (and the symbol-carrying ring the symbols of theirs)
     auto commit = [&](Refill &r) {
         if constexpr (kL1) refill_commit<R>(cs, r, sh.ring2[0], sh.tab[0]);
+        else if constexpr (kSym)
+            refill_commit<R>(cs, r, sh.ring[h], sh.rsym[h], reinterpret_cast<const uint8_t *>(&sh.sym[h][0]));
         else refill_commit<R>(cs, r, sh.ring[h]);
     };
     auto sync_fill = [&]() {
         if constexpr (kL1) refill_sync<R>(cs, lane, ok, sh.ring2[0], (const uint32_t *)sh.tab[0]);
+        else if constexpr (kSym)
+            refill_sync<R>(cs, lane, ok, sh.ring[h], sh.rsym[h], reinterpret_cast<const uint8_t *>(&sh.sym[h][0]));
         else refill_sync<R>(cs, lane, ok, sh.ring[h]);
     };
     __syncthreads();
     sync_fill();
     __syncthreads();
-    // wide table: the entry of the slot x holds (a half without a valid
-    // table reads an entry it never uses)
+    // wide table: the entry of the slot x holds; symbol-carrying ring: its
+    // symbol (a half without a valid table reads a value it never uses)
     uint32_t e = 0;
     if constexpr (kL1) e = sh.tab[0][x & (kM - 1)];
+    // symbol-carrying ring: the symbol of the slot x holds
+    auto sym_of = [&](auto &shr, uint32_t v) -> uint32_t {
+        return reinterpret_cast<const uint8_t *>(&shr.sym[h][0])[v & (kM - 1)];
+    };
+    if constexpr (kSym) e = sym_of(sh, x);
 
     const uint2 *stage = reinterpret_cast<const uint2 *>(&sh.stage[h][0]);
     const bool put = ok && real;  // this half writes output
@@ -683,6 +805,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     auto step = [&](auto check_tag, bool active, uint32_t i) {
         constexpr bool CHECK = decltype(check_tag)::value;
         if constexpr (kL1) dec_step_wide<CHECK>(x, e, rpos, sh, b0, lane, active, i);
+        else if constexpr (kSym) dec_step_sym<CHECK>(x, e, rpos, sh, b0, b1, hs, h, lane, active, i);
         else dec_step<CHECK, kH>(x, rpos, sh, b0, b1, hs, h, lane, active, i);
     };
     // Speculation: set when a group consumed a word that had not landed.
@@ -715,10 +838,10 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
             rv.flush(kGroupWords * gg + 8 * lane, stage[lane], cur);
         }
         wave_lds_order();
-        // words this group consumed (at most 256, less than the ring): the
-        // cursor difference, plus the ring size if the cursor wrapped
+        // words this group consumed (at most kGroupMaxWords, less than the
+        // ring): the cursor difference, plus the ring size if it wrapped
         const uint32_t dr = rpos - r0;
-        const uint32_t used = min(dr, dr + kRingWords);
+        const uint32_t used = R::kPow2 ? dr & (kRingWords - 1) : min(dr, dr + kRingWords);
         overrun |= cs.ptr + used > landed;
         cs.ptr += used;
     };
@@ -733,7 +856,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     };
     auto settle = [&](const Pend &pd, uint32_t r_end) {
         const uint32_t dr = r_end - pd.r0;
-        const uint32_t used = min(dr, dr + kRingWords);
+        const uint32_t used = R::kPow2 ? dr & (kRingWords - 1) : min(dr, dr + kRingWords);
         overrun |= cs.ptr + used > pd.landed;
         cs.ptr += used;
     };
@@ -818,6 +941,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         rpos = 0;
         if (ok) x = reinterpret_cast<const WC_GLOBAL uint32_t *>(cs.base)[lane];
         if constexpr (kL1) e = sh.tab[0][x & (kM - 1)];
+        if constexpr (kSym) e = sym_of(sh, x);
         for (uint32_t g = 0; g < ng; g++) {
             sync_fill();
             Pre cur = put || kWave ? rv.fetch_checked(kGroupWords * g + 8 * lane, len) : Pre{};
