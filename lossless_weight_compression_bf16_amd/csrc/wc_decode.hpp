@@ -167,7 +167,8 @@ struct Stream {
     uint32_t ptr;                     // next word to consume (advanced once per group)
     uint32_t fill;                    // words issued to the ring (landed or in flight)
     uint32_t land;                    // words landed in the ring
-    uint32_t fenc;                    // ring block of the next refill (BlockCycle selector)
+    uint32_t fenc;                    // ring block of the next refill (BlockCycle selector), or
+                                      // with a power-of-two ring the lane's ring dword
     __device__ uint32_t word_pair(uint32_t d) const  // stream dword d
     {
         return *reinterpret_cast<const WC_GLOBAL uint32_t *>(base + 128 + 4 * d);
@@ -211,12 +212,29 @@ __device__ __forceinline__ Refill refill_issue(Stream &st, uint32_t lane, bool o
         r.v1 = p[1];
         r.first = off == uoff;
     }
-    r.pos = (R::kBlk / 2) * C::index(st.fenc) + kB * lane;
-    if (r.go) {
-        st.fill += R::kBlk;
-        st.fenc = C::step(st.fenc);
+    if constexpr (R::kPow2) {
+        // fenc is the lane's ring dword itself, stepped a block modulo the ring
+        r.pos = st.fenc;
+        if (r.go) {
+            st.fill += R::kBlk;
+            st.fenc = (st.fenc + R::kBlk / 2) & (R::kWords / 2 - 1);
+        }
+    } else {
+        r.pos = (R::kBlk / 2) * C::index(st.fenc) + kB * lane;
+        if (r.go) {
+            st.fill += R::kBlk;
+            st.fenc = C::step(st.fenc);
+        }
     }
     return r;
+}
+
+// The ring position the first refill of a chunk fills (see Stream::fenc).
+template <typename R>
+__device__ __forceinline__ uint32_t fenc_start(uint32_t lane)
+{
+    if constexpr (R::kPow2) return R::kB * lane;
+    else return BlockCycle<R::kWords / R::kBlk>::start;
 }
 
 template <typename R>
@@ -239,15 +257,17 @@ __device__ __forceinline__ void refill_commit(Stream &st, Refill &r, uint32_t *r
 }
 
 // The symbol-carrying ring: each landed word is written with the symbol of
-// its slot (sym is the half's slot -> symbol bytes).
+// its slot, read from the half's slot -> symbol bytes (sym0: the tables'
+// start, sb = 4096 h opaque, so each lookup address is one and-or).
 template <typename R>
 __device__ __forceinline__ void refill_commit(Stream &st, Refill &r, uint32_t *ring, uint32_t *rsym,
-                                              const uint8_t *sym)
+                                              const uint8_t *sym0, uint32_t sb)
 {
     static_assert(R::kB == 1, "one dword (two words) per lane");
     if (r.go) {
-        const uint32_t s0 = sym[r.v & (kM - 1)], s1 = sym[(r.v >> 16) & (kM - 1)];
-        const uint16_t ss = (uint16_t)(s0 | s1 << 8);
+        const uint32_t s0 = sym0[(r.v & (kM - 1)) | sb];
+        const uint32_t s1 = sym0[((r.v >> 16) & (kM - 1)) | sb];
+        const uint16_t ss = (uint16_t)__builtin_amdgcn_perm(s1, s0, 0x0c0c0400u);  // s0 | s1 << 8
         ring[r.pos] = r.v;
         reinterpret_cast<uint16_t *>(rsym)[r.pos] = ss;
         if (r.pos < R::kApron / 2) {
@@ -694,7 +714,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     // A half with a bad seek entry still issues its refill loads (never
     // used): they read the first dword(s) at base, here the chunk's own table.
     Stream cs{gptr(reinterpret_cast<const uint8_t *>(tables + tix * 256)), 0, 0, 0, 0, 0, 0,
-              BlockCycle<R::kWords / R::kBlk>::start};
+              fenc_start<R>(lane)};
     uint32_t x = kL;
     // a chunk stored raw (WC_OPT_RAW_FALLBACK) takes no part in the rANS
     // loop (like a bad one, but reports nothing): k_decode_raw copies it
@@ -753,18 +773,26 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         else fbtmp = &sh.fb[h][0];
         build_table<kL1>(sh, h, lane, f, incl - local, fbtmp);
     }
+    // the halves' table offsets (4096 h, 1024 h) and 32 h, held opaque
+    uint32_t b0 = h, b1 = 0, hs = 32 * h;
+    if constexpr (!kL1) {
+        b0 = h << 12;
+        b1 = h << 10;
+    }
+    asm volatile("" : "+v"(b0), "+v"(b1), "+v"(hs));
     // the wide table's refills also write the slot entries of the words they land
     // (and the symbol-carrying ring the symbols of theirs)
     auto commit = [&](Refill &r) {
         if constexpr (kL1) refill_commit<R>(cs, r, sh.ring2[0], sh.tab[0]);
         else if constexpr (kSym)
-            refill_commit<R>(cs, r, sh.ring[h], sh.rsym[h], reinterpret_cast<const uint8_t *>(&sh.sym[h][0]));
+            refill_commit<R>(cs, r, sh.ring[h], sh.rsym[h], reinterpret_cast<const uint8_t *>(&sh.sym[0][0]), b0);
         else refill_commit<R>(cs, r, sh.ring[h]);
     };
     auto sync_fill = [&]() {
         if constexpr (kL1) refill_sync<R>(cs, lane, ok, sh.ring2[0], (const uint32_t *)sh.tab[0]);
         else if constexpr (kSym)
-            refill_sync<R>(cs, lane, ok, sh.ring[h], sh.rsym[h], reinterpret_cast<const uint8_t *>(&sh.sym[h][0]));
+            refill_sync<R>(cs, lane, ok, sh.ring[h], sh.rsym[h], reinterpret_cast<const uint8_t *>(&sh.sym[0][0]),
+                           b0);
         else refill_sync<R>(cs, lane, ok, sh.ring[h]);
     };
     __syncthreads();
@@ -795,12 +823,6 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     const uint32_t ng = __builtin_amdgcn_readfirstlane((hi_len + kGroupWords - 1) / kGroupWords);
     const uint32_t nfull = __builtin_amdgcn_readfirstlane(lo_len / kGroupWords);
     using Pre = typename View::Pre;
-    uint32_t b0 = h, b1 = 0, hs = 32 * h;
-    if constexpr (!kL1) {
-        b0 = h << 12;
-        b1 = h << 10;
-    }
-    asm volatile("" : "+v"(b0), "+v"(b1), "+v"(hs));
     uint32_t rpos = 0;  // cs.ptr modulo the ring size, advanced every step
     auto step = [&](auto check_tag, bool active, uint32_t i) {
         constexpr bool CHECK = decltype(check_tag)::value;
@@ -937,7 +959,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         if constexpr (kWave) rv.reset();
         commit(q[0]);
         cs.ptr = cs.fill = cs.land = 0;
-        cs.fenc = BlockCycle<R::kWords / R::kBlk>::start;
+        cs.fenc = fenc_start<R>(lane);
         rpos = 0;
         if (ok) x = reinterpret_cast<const WC_GLOBAL uint32_t *>(cs.base)[lane];
         if constexpr (kL1) e = sh.tab[0][x & (kM - 1)];
