@@ -61,22 +61,22 @@ constexpr uint32_t kGroupMaxWords = 6 * kLanes;
 // of 64 kB words, at most one per group, issued while fewer than kAhead
 // words are issued and unconsumed, and lands two groups later; so about
 // kAhead - 2 r words have landed ahead of a group that consumes r words per
-// group, and that must exceed r.  kB = 1 (320-word ring, kAhead 256) covers
-// weights (r about 45); kB = 2 (512-word ring, kAhead 384, 128-word blocks)
-// covers coded bytes of up to 8 bits, e.g. the FP16 high byte (r about 88),
-// which would otherwise outrun the refills and take the second pass.  The
-// symbol-carrying ring of the narrow one-dword decoder (kSym) has 256 words
-// (kAhead 192: r up to about 56).
+// group, and that must exceed r.  kB = 1 (256-word ring, kAhead 192) covers
+// weights (r about 45, up to about 56); kB = 2 (512-word ring, kAhead 384,
+// 128-word blocks) covers coded bytes of up to 8 bits, e.g. the FP16 high
+// byte (r about 88), which would otherwise outrun the refills and take the
+// second pass.  Both rings take a group's worst case (kGroupMaxWords).
 // A block never covers an unconsumed word: at issue fewer than kAhead words
 // are unconsumed, so with the block fewer than kWords.
-// The ring's first kApron words (128; 64 with kSym) are repeated after its
-// end, and the cursor is reduced modulo the ring size every kWrap = kApron /
-// 32 steps, so the 32 reads of a step never wrap.
+// The ring's first kApron words (128; 64 for the narrow table's symbol-
+// carrying ring) are repeated after its end, and the cursor is reduced
+// modulo the ring size every kWrap = kApron / 32 steps, so the 32 reads of
+// a step never wrap.
 template <int B, bool kWide = false, bool kSym = false>
 struct Ring {
     static constexpr int kB = B;
     static constexpr uint32_t kBlk = 2 * kLanes * kB;
-    static constexpr uint32_t kWords = kSym ? 256u : kB == 1 ? kGroupWords + kBlk : 512u;
+    static constexpr uint32_t kWords = 256u * kB;
     static constexpr uint32_t kApron = (kSym ? 2 : 4) * kLanes;
     static constexpr uint32_t kWrap = kApron / kLanes;
     static constexpr uint32_t kAlloc = kWords + kApron;
@@ -535,7 +535,8 @@ __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, ui
     // three unreduced steps it is below kRingWords + 96, so a step's reads
     // stay inside the 128-word apron)
     rpos += __popc(half);
-    if (i % Sh::R::kWrap == Sh::R::kWrap - 1) rpos = rpos < Sh::kRingWords ? rpos : rpos - Sh::kRingWords;
+    if (i % Sh::R::kWrap == Sh::R::kWrap - 1)
+        rpos = Sh::R::kPow2 ? rpos & (Sh::kRingWords - 1) : rpos < Sh::kRingWords ? rpos : rpos - Sh::kRingWords;
     asm volatile("" : "+v"(rpos));
     if (!CHECK || active) x = xn;
 }
@@ -610,7 +611,8 @@ __device__ __forceinline__ void dec_step_wide(uint32_t &x, uint32_t &e, uint32_t
     const uint32_t xn = __builtin_amdgcn_perm(xd, rw.y, sel);
     const uint32_t en = need ? rw.x : et;
     rpos += __popc(ml);
-    if (i % Sh::R::kWrap == Sh::R::kWrap - 1) rpos = rpos < Sh::kRingWords ? rpos : rpos - Sh::kRingWords;
+    if (i % Sh::R::kWrap == Sh::R::kWrap - 1)
+        rpos = Sh::R::kPow2 ? rpos & (Sh::kRingWords - 1) : rpos < Sh::kRingWords ? rpos : rpos - Sh::kRingWords;
     // keeps the cursor in a VGPR; not volatile, so the scheduler may move
     // the group epilogue into the steps' LDS waits
     asm("" : "+v"(rpos));
