@@ -4,9 +4,13 @@
 //   - narrow table (kL1 = false, kH = 2): one wavefront decodes two chunks,
 //     one per 32-lane half, so every VALU instruction of the serial rANS
 //     loop carries 64 useful lanes.  Per half the LDS holds slot -> symbol
-//     bytes (4 KiB) plus per-symbol b | (f-4096) << 16 (1 KiB); a step makes
-//     two dependent table reads and then its ring read.  10 wavefronts per
-//     CU: used when there are enough chunks to fill the machine;
+//     bytes (4 KiB) plus per-symbol b | (f-4096) << 16 (1 KiB).  With
+//     one-dword refills (kSym) the ring also carries the symbol of each
+//     word's slot, so a step waits for two dependent LDS reads ((b, f) of
+//     its symbol, then its word and next symbol); with two-dword refills it
+//     makes two dependent table reads and then its ring read.  12 (11)
+//     wavefronts per CU: used when there are enough chunks to fill the
+//     machine;
 //   - wide table (kL1 = true, kH = 1): one chunk per wavefront, one u32 per
 //     slot = symbol | (f-1) << 8 | (slot-b) << 20 (16 KiB), and a ring that
 //     keeps each stream word next to the entry of the slot it brings in.  A
@@ -17,18 +21,18 @@
 //     at once (8 wavefronts per CU), when the run is bound by the serial
 //     latency of each chunk.
 // Per chunk the LDS also holds
-//   - a ring of the compressed stream (320 words, 512 with two-dword
+//   - a ring of the compressed stream (256 words, 512 with two-dword
 //     refills; its first 64 or 128 words repeated after the end, so a step's
 //     32 reads never wrap), refilled 64 or 128 words at a time: a refill is
 //     loaded at the start of a group of 8 steps and written to the ring at
 //     the start of the group after next, so the load has two groups to land
 //     and the word fetch of a step is an LDS read.  The ring is sized for one
-//     group's worst case (256 words) plus a block, not for the refill
-//     latency: a group runs speculatively on the words landed so far; a
-//     chunk in which a group consumed a word that had not landed is decoded
-//     again from the start with a synchronous fill before every group (rare:
-//     it needs more than 64 words per group for many groups in a row, about
-//     2 bits/symbol above what weights carry);
+//     group's worst case (kGroupMaxWords = 192 words) plus a block, not for
+//     the refill latency: a group runs speculatively on the words landed so
+//     far; a chunk in which a group consumed a word that had not landed is
+//     decoded again from the start with a synchronous fill before every group
+//     (rare: it needs more than about 56 words per group for several groups
+//     in a row, over 3.5 bits/symbol; weights carry about 2.7);
 //   - the 256 decoded bytes of the current group.
 // At the end of a group each lane joins 8 consecutive decoded bytes with 8
 // raw bytes (loaded with one 8-byte load issued two groups earlier) and
