@@ -355,6 +355,36 @@ def test_corrupt_streams_two_chunk_wavefronts(dev, oracle_lib):
 
 
 
+@pytest.mark.parametrize("n_chunks", [3, 2101])
+def test_stored_state_below_L_is_flagged(dev, oracle_lib, n_chunks):
+    """A chunk whose stored states include one below L = 2^16 is no encoding:
+    both decoder forms (one chunk per wavefront for 3 chunks, two for 2101)
+    report BAD_FINAL_STATE, the same bits as the oracle, and decode the other
+    chunks bit for bit."""
+    import copy
+    from lossless_weight_compression_bf16_amd import _binding as B
+    x = _weights(65536 * (n_chunks - 1) + 999, 21)
+    o = oracle_lib.encode(x, "bf16", threads=8)
+    g = np.random.default_rng(22)
+    for trial, v in enumerate((0, 1, 65535)):
+        d = copy.deepcopy(o)
+        k = int(g.integers(0, n_chunks))
+        lane = int(g.integers(0, 32))
+        at = int(d.seek[k]) + 4 * lane
+        d.payload[at:at + 4] = np.frombuffer(np.uint32(v).tobytes(), np.uint8)
+        _say(f"[parity] stored state {v} in chunk {k} lane {lane} of {n_chunks}")
+        e = _upload(d, dev)
+        y = torch.empty(x.size, dtype=torch.int16, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        B.wc_decode("bf16", e.buffers(), e.n, y, err)
+        bits = int(err.item())
+        oy, obits = oracle_lib.decode(d, threads=8, strict=False)
+        assert bits == obits == oracle_lib.EF_BAD_FINAL_STATE, (trial, bits, obits)
+        keep = np.ones(x.size, bool)
+        keep[65536 * k:65536 * (k + 1)] = False
+        assert np.array_equal(y.cpu().numpy().view(np.uint16)[keep], x[keep]), trial
+
+
 def test_decoder_variant_follows_the_streams_device(dev):
     """The decoder is picked from the CU count of the device the stream
     belongs to: one chunk per wavefront while every chunk fits at once (8
