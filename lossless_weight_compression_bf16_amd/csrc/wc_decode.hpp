@@ -42,6 +42,7 @@
 // (WC_OPT_RAW_FALLBACK) are skipped here and copied by k_decode_raw.
 #pragma once
 
+#include <cstddef>
 #include <type_traits>
 
 #include "wc_common.hpp"
@@ -628,38 +629,59 @@ __device__ __forceinline__ void dec_step_wide(uint32_t &x, uint32_t &e, uint32_t
 
 // Builds the slot table of half h from the lane's 8 frequencies f[] (symbols
 // 8 lane .. 8 lane + 7) and their cumulative start b0.  The owner of a slot
-// is the last symbol whose start b is <= slot; each lane fills 128 slots by a
-// binary search for its first slot and a forward walk.
+// is the last present symbol whose start b is <= slot.  The present symbols
+// are first listed in symbol order (b | s << 16, at list[], 256 scratch
+// dwords of the half), so that the search for a lane's first slot and the
+// forward walk over its 128 slots never step through absent symbols (BF16
+// weights leave about 120 of them between the positive and the negative
+// exponents, which a walk over all symbols crosses one LDS read at a time).
 template <bool kL1, typename Sh>
 __device__ inline void build_table(Sh &sh, uint32_t h, uint32_t lane, const uint32_t f[8], uint32_t b0,
-                                   uint32_t *fbtmp)
+                                   uint32_t *fbtmp, uint32_t *list)
 {
+    uint32_t c = 0;
     {
         uint32_t b = b0;
         for (int i = 0; i < 8; i++) {
             fbtmp[8 * lane + i] = (b & 0xFFFF) | ((f[i] - kM) << 16);
             b += f[i];
+            c += f[i] != 0;
+        }
+    }
+    // the lane's first list position: exclusive prefix of the counts
+    uint32_t incl = c;
+    for (int o = 1; o < 32; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, 32);
+        if (lane >= (uint32_t)o) incl += v;
+    }
+    const uint32_t npres = __shfl(incl, 31, 32);  // >= 1: the table sums to 4096
+    {
+        uint32_t b = b0, pos = incl - c;
+        for (int i = 0; i < 8; i++) {
+            if (f[i]) list[pos++] = b | ((8 * lane + (uint32_t)i) << 16);
+            b += f[i];
         }
     }
     wave_lds_order();
-    auto bstart = [&](uint32_t t) -> uint32_t { return fbtmp[t] & 0xFFFF; };
     const uint32_t s0 = 128 * lane;
-    uint32_t lo = 0, hi = 256;
+    uint32_t lo = 0, hi = npres;
     while (hi - lo > 1) {
         const uint32_t mid = (lo + hi) >> 1;
-        if (bstart(mid) <= s0) lo = mid; else hi = mid;
+        if ((list[mid] & 0xFFFF) <= s0) lo = mid; else hi = mid;
     }
-    uint32_t s = lo;
-    uint32_t bs = bstart(s);
-    uint32_t nb = s < 255 ? bstart(s + 1) : kM;
+    uint32_t idx = lo;
+    uint32_t s = list[idx] >> 16;
+    uint32_t bs = list[idx] & 0xFFFF;
+    uint32_t nb = idx + 1 < npres ? list[idx + 1] & 0xFFFF : kM;
     for (uint32_t q = 0; q < 32; q++) {
         uint32_t word = 0;
         for (uint32_t i = 0; i < 4; i++) {
             const uint32_t slot = s0 + 4 * q + i;
             while (slot >= nb) {
-                s++;
+                idx++;
+                s = list[idx] >> 16;
                 bs = nb;
-                nb = s < 255 ? bstart(s + 1) : kM;
+                nb = idx + 1 < npres ? list[idx + 1] & 0xFFFF : kM;
             }
             if constexpr (kL1) {
                 const uint32_t fm1 = nb - bs - 1;  // f - 1 of the owner
@@ -774,10 +796,19 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         }
     }
     if (ok) {
-        uint32_t *fbtmp;
-        if constexpr (kL1) fbtmp = &sh.fbtmp[h][0];
-        else fbtmp = &sh.fb[h][0];
-        build_table<kL1>(sh, h, lane, f, incl - local, fbtmp);
+        // scratch for the list of present symbols (256 dwords per half): the
+        // ring's space, filled only after the table is built
+        uint32_t *fbtmp, *list;
+        if constexpr (kL1) static_assert(sizeof(sh.ring2) >= 512 * 4, "list scratch");
+        else static_assert(sizeof(Sh) - offsetof(Sh, ring) >= 256 * 4 * kH, "list scratch");
+        if constexpr (kL1) {
+            fbtmp = &sh.fbtmp[h][0];
+            list = reinterpret_cast<uint32_t *>(&sh.ring2[0][0]) + 256;
+        } else {
+            fbtmp = &sh.fb[h][0];
+            list = &sh.ring[0][0] + 256 * h;
+        }
+        build_table<kL1>(sh, h, lane, f, incl - local, fbtmp, list);
     }
     // the halves' table offsets (4096 h, 1024 h) and 32 h, held opaque
     uint32_t b0 = h, b1 = 0, hs = 32 * h;
