@@ -113,7 +113,7 @@ struct DecSharedL1 {
 };
 
 template <int H, int kB>
-struct DecSharedL2 {
+struct alignas(16) DecSharedL2 {
     using R = Ring<kB>;
     static constexpr uint32_t kRingWords = R::kWords;
     uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
@@ -131,7 +131,7 @@ struct DecSharedL2 {
 // instead of three.  12,672 B per wavefront: ten 1,280-byte LDS granules,
 // 12 wavefronts per CU like DecSharedL2<2, 1>.
 template <int H>
-struct DecSharedS {
+struct alignas(16) DecSharedS {
     using R = Ring<1, false, true>;
     static constexpr uint32_t kRingWords = R::kWords;
     uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
@@ -671,6 +671,48 @@ __device__ inline void build_table(Sh &sh, uint32_t h, uint32_t lane, const uint
     }
     uint32_t idx = lo;
     uint32_t s = list[idx] >> 16;
+    if constexpr (!kL1) {
+        // slot -> symbol bytes without a walk: zero the lane's 128 slots, mark
+        // each present symbol at its first slot, then take the running
+        // maximum over the slots from the owner of the lane's first slot
+        // (present symbols start in increasing order, so the largest mark so
+        // far is the owner).  Every lane zeroes its slots before any marks,
+        // and marks before any lane reads its slots back (one wavefront, LDS
+        // served in issue order).
+        u32x4 *row = reinterpret_cast<u32x4 *>(&sh.sym[h][32 * lane]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) row[j] = u32x4{0u, 0u, 0u, 0u};
+        wave_lds_order();
+        {
+            uint8_t *bytes = reinterpret_cast<uint8_t *>(&sh.sym[h][0]);
+            uint32_t b = b0;
+            for (int i = 0; i < 8; i++) {
+                if (f[i]) bytes[b] = (uint8_t)(8 * lane + (uint32_t)i);
+                b += f[i];
+            }
+        }
+        wave_lds_order();
+        u32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = row[j];
+        uint32_t m = s;
+        auto scan = [&](uint32_t w) {
+            const uint32_t m0 = max(m, w & 0xFFu), m1 = max(m0, (w >> 8) & 0xFFu);
+            const uint32_t m2 = max(m1, (w >> 16) & 0xFFu), m3 = max(m2, w >> 24);
+            m = m3;
+            return m0 | (m1 << 8) | (m2 << 16) | (m3 << 24);
+        };
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            u32x4 o;
+            o.x = scan(v[j].x);
+            o.y = scan(v[j].y);
+            o.z = scan(v[j].z);
+            o.w = scan(v[j].w);
+            row[j] = o;
+        }
+        return;
+    }
     uint32_t bs = list[idx] & 0xFFFF;
     uint32_t nb = idx + 1 < npres ? list[idx + 1] & 0xFFFF : kM;
     for (uint32_t q = 0; q < 32; q++) {
