@@ -712,27 +712,51 @@ __device__ inline void build_table(Sh &sh, uint32_t h, uint32_t lane, const uint
             row[j] = o;
         }
         return;
-    }
-    uint32_t bs = list[idx] & 0xFFFF;
-    uint32_t nb = idx + 1 < npres ? list[idx + 1] & 0xFFFF : kM;
-    for (uint32_t q = 0; q < 32; q++) {
-        uint32_t word = 0;
-        for (uint32_t i = 0; i < 4; i++) {
-            const uint32_t slot = s0 + 4 * q + i;
-            while (slot >= nb) {
-                idx++;
-                s = list[idx] >> 16;
-                bs = nb;
-                nb = idx + 1 < npres ? list[idx + 1] & 0xFFFF : kM;
-            }
-            if constexpr (kL1) {
-                const uint32_t fm1 = nb - bs - 1;  // f - 1 of the owner
-                sh.tab[h][slot] = s | (fm1 << 8) | ((slot - bs) << 20);
-            } else {
-                word |= s << (8 * i);
+    } else {
+        // the wide entries the same way: mark each present symbol's first slot
+        // b with s | (f-1) << 8 | b << 20 (increasing in b), take the running
+        // maximum m from the mark of the owner of the lane's first slot, and
+        // turn it into the entry s | (f-1) << 8 | (slot-b) << 20 = m + (slot -
+        // 2b) << 20 (mod 2^32)
+        const uint32_t bs = list[idx] & 0xFFFF;
+        const uint32_t nb = idx + 1 < npres ? list[idx + 1] & 0xFFFF : kM;
+        u32x4 *row = reinterpret_cast<u32x4 *>(&sh.tab[h][s0]);
+#pragma unroll
+        for (int j = 0; j < 32; j++) row[j] = u32x4{0u, 0u, 0u, 0u};
+        wave_lds_order();
+        {
+            uint32_t b = b0;
+            for (int i = 0; i < 8; i++) {
+                if (f[i]) sh.tab[h][b] = (8 * lane + (uint32_t)i) | ((f[i] - 1) << 8) | (b << 20);
+                b += f[i];
             }
         }
-        if constexpr (!kL1) sh.sym[h][32 * lane + q] = word;
+        wave_lds_order();
+        uint32_t m = s | ((nb - bs - 1) << 8) | (bs << 20);
+        auto entry = [&](uint32_t mark, uint32_t slot) {
+            m = max(m, mark);
+            return m + ((slot - 2 * (m >> 20)) << 20);
+        };
+#pragma unroll
+        for (int j0 = 0; j0 < 32; j0 += 8) {
+            u32x4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) v[j] = row[j0 + j];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const uint32_t slot = s0 + 4 * (uint32_t)(j0 + j);
+                u32x4 o;
+                o.x = entry(v[j].x, slot);
+                o.y = entry(v[j].y, slot + 1);
+                o.z = entry(v[j].z, slot + 2);
+                o.w = entry(v[j].w, slot + 3);
+                v[j] = o;
+            }
+            // rows j0 .. j0+7 are read before they are written (and later
+            // rows hold no marks of these slots)
+#pragma unroll
+            for (int j = 0; j < 8; j++) row[j0 + j] = v[j];
+        }
     }
 }
 
