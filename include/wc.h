@@ -289,6 +289,32 @@ uint64_t wc_check_division(uint32_t samples_per_divisor);
 wc_status wc_decode_variant(wc_format format, uint64_t num_chunks, uint64_t n, uint64_t payload_bytes,
                             hipStream_t stream, int *one_chunk_per_wave, int *refill_dwords);
 
+/* How the encoder writes the coded words of a chunk; both forms write the
+ * same bytes and differ in speed only.  WC_ENC_WORDS_DIRECT: each step's
+ * words go straight to the chunk's scratch slot as 2-byte stores (fewest
+ * instructions per step: fastest where the grid does not fill the GPU).
+ * WC_ENC_WORDS_STAGED: they go to a 256-word LDS ring per chunk and reach
+ * the slot as whole dwords once per 256 symbols (fewer memory operations:
+ * fastest where the grid fills every SIMD).  WC_ENC_WORDS_AUTO (the
+ * default): staged when the encoder's grid has at least 16 wavefronts per
+ * compute unit of the stream's device (12 for FP32), else direct. */
+#define WC_ENC_WORDS_AUTO 0
+#define WC_ENC_WORDS_DIRECT 1
+#define WC_ENC_WORDS_STAGED 2
+
+/* Sets the encoder word-store form for every later encode call of the
+ * process (any thread, any device) and returns the previous setting, or -1
+ * (nothing changed) for a value that is not one of WC_ENC_WORDS_*.  Meant
+ * for tuning and tests; calls already enqueued are not affected. */
+int wc_set_encoder_words(int mode);
+
+/* Which form an encode of num_chunks chunks under `format` would take on
+ * the device that `stream` belongs to (the current device for the null
+ * stream), given the current setting: *staged = 1 for WC_ENC_WORDS_STAGED,
+ * 0 for direct.  Host function; WC_ERR_ARG for a bad format or null
+ * pointer, WC_ERR_HIP if the stream's device cannot be queried. */
+wc_status wc_encode_variant(wc_format format, uint64_t num_chunks, hipStream_t stream, int *staged);
+
 /* Size of the fixed device array wc_encode_noalloc takes its scratch from
  * (one per device the library runs on, held until the process ends). */
 #define WC_NOALLOC_SCRATCH_BYTES (128ull << 20)

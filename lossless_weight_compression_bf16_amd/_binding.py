@@ -38,7 +38,10 @@ WC_NOALLOC_SCRATCH_BYTES = 128 << 20  # the fixed device array of wc_encode_noal
 
 EXPORTS = ["wc_version", "wc_status_string", "wc_query_layout", "wc_plan_batch", "wc_encode",
            "wc_decode", "wc_encode_batch", "wc_decode_batch", "wc_check_division", "wc_tile_order",
-           "wc_decode_gemm_batch", "wc_decode_variant", "wc_encode_noalloc", "wc_noalloc_max_chunks"]
+           "wc_decode_gemm_batch", "wc_decode_variant", "wc_encode_noalloc", "wc_noalloc_max_chunks",
+           "wc_set_encoder_words", "wc_encode_variant"]
+# encoder word-store forms (wc_set_encoder_words)
+ENC_WORDS_AUTO, ENC_WORDS_DIRECT, ENC_WORDS_STAGED = 0, 1, 2
 
 
 class WcError(RuntimeError):
@@ -98,11 +101,14 @@ def lib() -> ctypes.CDLL:
     L.wc_decode_gemm_batch.argtypes = [I, P, P, U32, P, P, U32, ctypes.POINTER(wc_buffers), P, P]
     L.wc_decode_variant.argtypes = [I, U64, U64, U64, P, ctypes.POINTER(I), ctypes.POINTER(I)]
     L.wc_encode_noalloc.argtypes = [I, P, U64, ctypes.POINTER(wc_buffers), P, P]
+    L.wc_set_encoder_words.argtypes = [I]
+    L.wc_set_encoder_words.restype = I
+    L.wc_encode_variant.argtypes = [I, U64, P, ctypes.POINTER(I)]
     L.wc_noalloc_max_chunks.argtypes = [I]
     L.wc_noalloc_max_chunks.restype = U64
     for name in ("wc_query_layout", "wc_plan_batch", "wc_encode", "wc_decode", "wc_encode_batch",
                  "wc_decode_batch", "wc_tile_order", "wc_decode_gemm_batch", "wc_decode_variant",
-                 "wc_encode_noalloc"):
+                 "wc_encode_noalloc", "wc_encode_variant"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -239,6 +245,24 @@ def wc_decode_variant(dtype, num_chunks: int, n: int, payload_bytes: int, stream
                                  ctypes.byref(a), ctypes.byref(b))
     _check(rc, "wc_decode_variant")
     return bool(a.value), int(b.value)
+
+
+def wc_set_encoder_words(mode: int) -> int:
+    """Sets the encoder word-store form (ENC_WORDS_*) for the process;
+    returns the previous one."""
+    prev = int(lib().wc_set_encoder_words(int(mode)))
+    if prev < 0:
+        raise WcError(f"wc_set_encoder_words: bad mode {mode}")
+    return prev
+
+
+def wc_encode_variant(dtype, num_chunks: int, stream=None) -> bool:
+    """True if an encode of num_chunks chunks would stage its words in LDS
+    on the device of `stream`."""
+    a = ctypes.c_int(0)
+    rc = lib().wc_encode_variant(_code(dtype), int(num_chunks), _stream(stream), ctypes.byref(a))
+    _check(rc, "wc_encode_variant")
+    return bool(a.value)
 
 
 def wc_check_division(samples_per_divisor: int = 256) -> int:

@@ -21,6 +21,19 @@ constexpr uint32_t kM = 1u << kScaleBits;
 constexpr uint32_t kL = 1u << 16;
 constexpr uint32_t kMaxWords = kChunk;                  // at most one word per symbol
 constexpr uint64_t kSlotBytes = 128 + 2ull * kMaxWords;   // encoder scratch per chunk
+// Most words one group of 8 steps of one half consumes (decoder) or writes
+// (encoder).  The decoder checks that every stored state is at least
+// L = 2^16; then every state stays in [L, 2^32): a step gives
+// x' = f q + slot - b >= f q >= 16 f (q = x >> 12 >= 16), and a renormalised
+// state x' 2^16 + w is at least 16 f 2^16.  So a lane that renormalises at
+// steps t, t+1, ... has x'_t >= 16 f_t, q_(t+1) >= 256 f_t,
+// x'_(t+1) >= 256 f_t f_(t+1), ..., x'_(t+3) >= 2^16 f_t f_(t+1) f_(t+2)
+// f_(t+3) >= 2^16: four renormalisations in a row are impossible, and a
+// lane takes at most 6 words in 8 steps.  The encoder's states, read
+// backwards, are the decoder's states for the stream it writes (its final
+// states are in [L, 2^32)), so it writes a word exactly where the decoder
+// takes one and is held to the same bound.
+constexpr uint32_t kGroupMaxWords = 6 * kLanes;
 constexpr uint64_t kMaxElems = 1ull << 40;
 
 inline __host__ __device__ uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }

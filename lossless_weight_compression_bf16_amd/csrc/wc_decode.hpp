@@ -52,16 +52,6 @@ namespace wc {
 constexpr uint32_t kGroup = 8;                       // steps per group
 constexpr uint32_t kGroupWords = kLanes * kGroup;    // lane-steps of a group per half
 constexpr uint32_t kStageBytes = kLanes * kGroup;    // decoded bytes per group per half
-// Most words one group of one half consumes.  The decoder checks that every
-// stored state is at least L = 2^16; then every state stays in [L, 2^32):
-// a step gives x' = f q + slot - b >= f q >= 16 f (q = x >> 12 >= 16), and a
-// renormalised state x' 2^16 + w is at least 16 f 2^16.  So a lane that
-// renormalises at steps t, t+1, ... has x'_t >= 16 f_t, q_(t+1) >= 256 f_t,
-// x'_(t+1) >= 256 f_t f_(t+1), ..., x'_(t+3) >= 2^16 f_t f_(t+1) f_(t+2)
-// f_(t+3) >= 2^16: four renormalisations in a row are impossible, and a
-// lane takes at most 6 words in 8 steps.
-constexpr uint32_t kGroupMaxWords = 6 * kLanes;
-
 // Ring geometry for refills of kB dwords per lane.  A refill moves a block
 // of 64 kB words, at most one per group, issued while fewer than kAhead
 // words are issued and unconsumed, and lands two groups later; so about

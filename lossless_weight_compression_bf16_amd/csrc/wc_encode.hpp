@@ -404,13 +404,21 @@ using WideView = typename std::conditional<
 // One encode step for one lane: renormalise (the low 16 bits go to the word
 // list, which grows downwards from index p; the lane's rank among the half's
 // emitting lanes orders words within a step) and push the symbol.  Only
-// emitting lanes store (an exec-masked store: the instruction is issued every
-// step, so the compiler still counts memory operations exactly); stores go to
-// a wave-uniform base plus a 32-bit lane offset, woff being the half's word
-// area relative to that base.
-template <bool CHECK>
-__device__ __forceinline__ void enc_step(uint32_t &x, uint32_t &p, bool active, const EncSym &e,
-                                         WC_GLOBAL uint8_t *base, uint32_t woff, uint32_t h, uint32_t hs)
+// emitting lanes write their word (exec-masked).  Words go either straight
+// to the slot (STAGE false: a wave-uniform base plus a 32-bit lane offset,
+// woff being the half's word area relative to that base) or to the half's
+// LDS ring (STAGE true: 256 words per half, word w at w mod 256,
+// hsel = 256 h), from which whole dwords go to the slot once a group is done.
+struct WordDst {
+    WC_GLOBAL uint8_t *base;
+    uint32_t woff;
+    uint16_t *ring;
+    uint32_t hsel;
+};
+
+template <bool CHECK, bool STAGE>
+__device__ __forceinline__ void enc_step(uint32_t &x, uint32_t &p, bool active, const EncSym &e, const WordDst &d,
+                                         uint32_t h, uint32_t hs)
 {
     const bool emit = (!CHECK || active) && x > e.th;
     const uint64_t m = __ballot(emit);
@@ -421,9 +429,13 @@ __device__ __forceinline__ void enc_step(uint32_t &x, uint32_t &p, bool active, 
     const uint32_t lo = __builtin_amdgcn_mbcnt_lo(ml, p);
     const uint32_t hi = __builtin_amdgcn_mbcnt_hi(mh, p);
     const uint32_t slot = h ? hi : lo;
-    uint32_t off = woff + 2 * slot;
-    asm("" : "+v"(off));  // a 32-bit offset from the uniform base, not a per-lane pointer
-    if (emit) *reinterpret_cast<WC_GLOBAL uint16_t *>(base + off) = (uint16_t)(x & 0xFFFF);
+    if constexpr (STAGE) {
+        if (emit) d.ring[(slot & 255u) | d.hsel] = (uint16_t)(x & 0xFFFF);
+    } else {
+        uint32_t off = d.woff + 2 * slot;
+        asm("" : "+v"(off));  // a 32-bit offset from the uniform base, not a per-lane pointer
+        if (emit) *reinterpret_cast<WC_GLOBAL uint16_t *>(d.base + off) = (uint16_t)(x & 0xFFFF);
+    }
     const uint32_t xr = emit ? x >> 16 : x;
     const uint32_t q = div_exact(xr, e.mp, (e.fm_sh >> 16) & 0xFF, e.fm_sh >> 24);
     const uint32_t xn = xr + __umul24(q, e.fm_sh & 0xFFFF) + e.b;
@@ -434,13 +446,15 @@ __device__ __forceinline__ void enc_step(uint32_t &x, uint32_t &p, bool active, 
 // symbols from offset 0 and meta[k].x their padded size.
 constexpr uint32_t kRawMark = 0xFFFFFFFFu;
 
-template <int DT>
+template <int DT, bool STAGE>
 __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__restrict__ tables,
                                                uint8_t *__restrict__ slots, uint2 *__restrict__ meta,
                                                uint64_t total_chunks, Opts opts, uint8_t *__restrict__ raw)
 {
     __shared__ EncSym enc[2][256];
     __shared__ uint32_t estage[2][kEncBlk / 4];  // one full group's coded bytes per half
+    // per half: a ring of 256 words (word staging, below)
+    __shared__ uint32_t ewring[STAGE ? 2 * 128 : 1];
     const uint32_t lane = threadIdx.x & 31, h = threadIdx.x >> 5;
     // with an odd chunk count the last wavefront's second half shadows the
     // first half's chunk: it runs the same unchecked code but stores nothing
@@ -498,6 +512,47 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     uint32_t x = kL;
     uint32_t p_w = kMaxWords;  // words are written downwards from here
 
+    // Word staging (STAGE).  Steps write their words to the half's LDS
+    // ring; words [p_w, wf) are in the ring only.  At the end of a group,
+    // wt = p_w rounded up to even marks the dwords that are complete; the
+    // next group reads them from the ring before its steps (wflush_ld) and
+    // writes them to the slot after them (wflush_st), so LDS latency hides
+    // behind the steps.  A group writes at most kGroupMaxWords = 192 words
+    // per half, so the ring holds at most 193 words when it is read (three
+    // reads per lane cover the 96 dwords), and the reads come before (in LDS
+    // order) the writes that reuse their places.  Where the grid is too
+    // small to fill the machine, each wavefront's instruction count sets the
+    // time and the words go straight to the slot instead.
+    WordDst wd{wbase, woff, reinterpret_cast<uint16_t *>(&ewring[0]), h << 8};
+    asm volatile("" : "+v"(wd.hsel));
+    const uint32_t *const hring = &ewring[STAGE ? 128 * h : 0];
+    uint32_t wf = kMaxWords, wt = kMaxWords;
+    constexpr uint32_t kFlushRounds = kGroupMaxWords / 2 / kLanes;
+    uint32_t fv[kFlushRounds];
+    auto wflush_ld = [&]() {
+        if constexpr (STAGE) {
+            // dwords wt / 2 + lane + 32 r of the half; wt is even, so none
+            // straddles the ring's end
+            wave_lds_order();
+#pragma unroll
+            for (uint32_t r = 0; r < kFlushRounds; r++) fv[r] = hring[((wt >> 1) + lane + kLanes * r) & 127u];
+        }
+    };
+    auto wflush_st = [&]() {
+        if constexpr (STAGE) {
+            // the complete dwords, to the half's word area at a 32-bit offset
+            // from the uniform base
+            const uint32_t n = (wf - wt) >> 1;
+            const uint32_t off = woff + 2 * wt + 4 * lane;
+#pragma unroll
+            for (uint32_t r = 0; r < kFlushRounds; r++)
+                if (lane + kLanes * r < n)
+                    *reinterpret_cast<WC_GLOBAL uint32_t *>(wbase + (off + 4 * kLanes * r)) = fv[r];
+            wf = wt;
+            wt = (p_w + 1) & ~1u;
+        }
+    };
+
     // Groups of 8 steps run from the last to the first.  Groups where every
     // lane of both halves is active run unchecked; the partial last group of
     // a shorter chunk runs checked, first.
@@ -519,11 +574,13 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
         EncSym es[kEncGroup];
 #pragma unroll
         for (uint32_t i = 0; i < kEncGroup; i++) es[i] = enc[h][SymView<DT>::symbol(cur.e[i])];
+        wflush_ld();
 #pragma unroll
         for (int i = kEncGroup - 1; i >= 0; i--) {
             const bool active = !CHECK || kEncBlk * g + kLanes * i + lane < len;
-            enc_step<CHECK>(x, p_w, active, es[i], wbase, woff, h, hs);
+            enc_step<CHECK, STAGE>(x, p_w, active, es[i], wd, h, hs);
         }
+        wflush_st();
     };
     // Groups run from the last to the first.  The groups above the largest
     // multiple of D below the shorter chunk's full-group count run checked
@@ -580,8 +637,10 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
             for (uint32_t i = 0; i < kEncGroup; i++) es[i] = enc[h][sy[i]];
             uint32_t sn[kEncGroup];
             transpose(nx, sn, gs);
+            wflush_ld();
 #pragma unroll
-            for (int i = kEncGroup - 1; i >= 0; i--) enc_step<false>(x, p_w, true, es[i], wbase, woff, h, hs);
+            for (int i = kEncGroup - 1; i >= 0; i--) enc_step<false, STAGE>(x, p_w, true, es[i], wd, h, hs);
+            wflush_st();
 #pragma unroll
             for (uint32_t i = 0; i < kEncGroup; i++) sy[i] = sn[i];
         };
@@ -599,6 +658,16 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
                 fgroup(g >= j + D ? g - j - D : 0, s[(D - j) % D], s[(2 * D - j - 1) % D], g >= j + 1 ? g - j - 1 : 0);
             }
         }
+    }
+
+    // the words still in the ring (at most 193), from the dword holding
+    // word p_w (with an odd p_w its other half is not part of the stream)
+    if constexpr (STAGE) {
+        wt = p_w & ~1u;
+        const uint32_t n = (wf - wt) >> 1;
+        wave_lds_order();
+        for (uint32_t j = lane; j < n; j += kLanes)
+            *reinterpret_cast<WC_GLOBAL uint32_t *>(wbase + (woff + 2 * wt + 4 * j)) = hring[((wt >> 1) + j) & 127u];
     }
 
     if (real) {

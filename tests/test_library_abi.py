@@ -196,3 +196,27 @@ def test_decoder_variant_needs_a_device(L):
     assert L.wc_decode_variant(0, 100, 100 * 65536, 1 << 20, None, ctypes.byref(a), ctypes.byref(b)) == B.WC_ERR_HIP
     assert L.wc_decode_variant(0, 100, 100 * 65536, 1 << 20, None, None, ctypes.byref(b)) == B.WC_ERR_ARG
     assert L.wc_decode_variant(0x800, 100, 100 * 65536, 1 << 20, None, ctypes.byref(a), ctypes.byref(b)) == B.WC_ERR_ARG
+
+
+def test_encoder_words_setting(L):
+    """wc_set_encoder_words takes the three forms, returns the previous one
+    and refuses anything else without changing the setting; the variant
+    query checks its arguments and, with no device, says so."""
+    import torch
+    prev = L.wc_set_encoder_words(B.ENC_WORDS_STAGED)
+    try:
+        assert prev == B.ENC_WORDS_AUTO
+        assert L.wc_set_encoder_words(3) == -1
+        assert L.wc_set_encoder_words(-1) == -1
+        assert L.wc_set_encoder_words(B.ENC_WORDS_DIRECT) == B.ENC_WORDS_STAGED
+        assert L.wc_set_encoder_words(B.ENC_WORDS_AUTO) == B.ENC_WORDS_DIRECT
+        with pytest.raises(B.WcError):
+            B.wc_set_encoder_words(7)
+        assert L.wc_set_encoder_words(B.ENC_WORDS_AUTO) == B.ENC_WORDS_AUTO
+    finally:
+        L.wc_set_encoder_words(B.ENC_WORDS_AUTO)
+    a = ctypes.c_int(7)
+    assert L.wc_encode_variant(0, 100, None, None) == B.WC_ERR_ARG
+    assert L.wc_encode_variant(0x800, 100, None, ctypes.byref(a)) == B.WC_ERR_ARG
+    if not torch.cuda.is_available():
+        assert L.wc_encode_variant(0, 100, None, ctypes.byref(a)) == B.WC_ERR_HIP
