@@ -126,13 +126,16 @@ bool stream_device(hipStream_t stream, int *dev)
     return hipGetDevice(dev) == hipSuccess;
 }
 
-// Encoder word stores.  A grid that fills every SIMD's wavefront slots at
-// least once (k_encode holds 4 wavefronts per SIMD at the 16- and 8-bit
-// layouts' register counts, 3 for FP32) is bound by the memory pipeline,
-// and staging the words in LDS to write whole dwords once per group is
-// faster (MoE experts set: 8.66 -> 7.99 ms); a smaller grid is bound by each
-// wavefront's serial instruction stream, and the direct 2-byte stores, with
-// fewer instructions per step, are faster there (up to 24%).
+// Encoder word stores.  For the 16-bit layouts a grid that fills every
+// SIMD's wavefront slots at least once (k_encode holds 4 wavefronts per
+// SIMD, 16 per CU) is bound by the memory pipeline, and staging the words
+// in LDS to write whole dwords once per group is faster (MoE experts set:
+// BF16 8.66 -> 7.99 ms, FP16 9.49 -> 8.87 ms); a smaller grid is bound by
+// each wavefront's serial instruction stream, and the direct 2-byte stores,
+// with fewer instructions per step, are faster there (up to 24%).  FP8
+// (half the input bytes per symbol) is faster direct at any size (6.0
+// against 6.3 ms on the same set), FP32 within 3% either way: both store
+// directly.
 std::atomic<int> g_enc_words{WC_ENC_WORDS_AUTO};
 
 bool use_staged_words(int layout, uint64_t chunks, int dev, bool *staged)
@@ -144,8 +147,8 @@ bool use_staged_words(int layout, uint64_t chunks, int dev, bool *staged)
     }
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-    const uint64_t per_cu = layout == WC_FP32 ? 12 : 16;
-    *staged = (chunks + 1) / 2 >= per_cu * (uint64_t)cus;
+    const bool sixteen = layout != WC_FP32 && layout != WC_FP8_E4M3 && layout != WC_FP8_E5M2;
+    *staged = sixteen && (chunks + 1) / 2 >= 16 * (uint64_t)cus;
     return true;
 }
 

@@ -191,16 +191,17 @@ def test_forms_agree_on_a_large_set(dev):
 
 
 def test_encoder_variant_follows_the_streams_device(dev):
-    """Automatic choice: staged from 16 wavefronts (two chunks each) per CU
-    of the stream's device (12 for FP32), direct below; a forced form is
-    reported as such."""
+    """Automatic choice: for the 16-bit layouts staged from 16 wavefronts
+    (two chunks each) per CU of the stream's device, direct below; FP32 and
+    FP8 always direct; a forced form is reported as such."""
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     side = torch.cuda.Stream(device=dev)
+    c = 2 * 16 * cus
     for stream in (None, side):
-        for dtype, per_cu in (("bf16", 16), ("fp16", 16), ("fp8e4m3", 16), ("fp32", 12)):
-            c = 2 * per_cu * cus
-            for chunks, staged in ((c - 2, False), (c - 1, True), (c, True), (1, False)):
-                assert B.wc_encode_variant(dtype, chunks, stream) == staged, (dtype, chunks)
+        for dtype in ("bf16", "bf16r", "fp16", "fp16r", "fp32", "fp8e4m3", "fp8e5m2"):
+            sixteen = dtype in ("bf16", "bf16r", "fp16", "fp16r")
+            for chunks, staged in ((c - 2, False), (c - 1, True), (c, True), (1 << 20, True), (1, False)):
+                assert B.wc_encode_variant(dtype, chunks, stream) == (staged and sixteen), (dtype, chunks)
         for mode, staged in ((B.ENC_WORDS_STAGED, True), (B.ENC_WORDS_DIRECT, False)):
             B.wc_set_encoder_words(mode)
             try:
