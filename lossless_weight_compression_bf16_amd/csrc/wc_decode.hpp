@@ -118,16 +118,22 @@ struct alignas(16) DecSharedL2 {
 // takes its next symbol from the ring read that brings its word, a lane that
 // keeps x' reads the symbol of x' meanwhile, so a step waits for two
 // dependent LDS reads ((b, f) of the current symbol, then word and symbol)
-// instead of three.  12,672 B per wavefront: ten 1,280-byte LDS granules,
-// 12 wavefronts per CU like DecSharedL2<2, 1>.
+// instead of three.  Each half's ring symbols start a multiple of 256 bytes
+// from sym[0], so the ring cursor can carry that offset (kept by an and-or
+// when it is reduced) and serve as the symbol byte's address unchanged.
+// 12,800 B per wavefront: ten 1,280-byte LDS granules, 12 wavefronts per CU
+// like DecSharedL2<2, 1>.
 template <int H>
-struct alignas(16) DecSharedS {
+struct alignas(256) DecSharedS {
     using R = Ring<1, false, true>;
     static constexpr uint32_t kRingWords = R::kWords;
+    struct alignas(256) Half {
+        uint32_t rsym[R::kAlloc / 4];       // per ring word: sym[word & 4095]
+        uint32_t ring[R::kAlloc / 2];       // stream words, two per dword
+    };
     uint32_t sym[H][kM / 4];                // slot -> symbol, 4 slots per word
     uint32_t fb[H][256];                    // b | (f - 4096) << 16
-    uint32_t ring[H][R::kAlloc / 2];        // stream words, two per dword
-    uint32_t rsym[H][R::kAlloc / 4];        // per ring word: sym[word & 4095]
+    Half hr[H];                             // 1,024 B each (the table build's list scratch)
     uint32_t stage[H][kStageBytes / 4];
 };
 
@@ -542,13 +548,17 @@ __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, ui
 // the lane reads, in one batch, its ring word at its renormalisation rank
 // and one symbol byte: the ring's symbol of that word if it renormalises,
 // else the slot table's symbol of x' (an address select, so the byte is a
-// single zero-extending load).  The cursor is reduced modulo the ring
-// every second step (a step's reads end below kRingWords + 64).  sb = 4096
-// h and fbb = 1024 h are the half's table offsets, hs = 32 h, all opaque.
+// single zero-extending load).  The cursor rpos carries rb, the byte offset
+// of the half's ring symbols from sym[0] (a multiple of 256): it is the
+// symbol byte's address as it stands, and the ring word's address is
+// 2 rpos + radj (radj = the ring words' offset - 2 rb, modulo 2^32).  It is
+// reduced modulo the ring every second step, (rpos & 255) | rb (a step's
+// reads end below kRingWords + 64).  sb = 4096 h and fbb = 1024 h are the
+// half's table offsets, hs = 32 h, all opaque.
 template <bool CHECK, typename Sh>
 __device__ __forceinline__ void dec_step_sym(uint32_t &x, uint32_t &s, uint32_t &rpos, Sh &sh, uint32_t sb,
-                                             uint32_t fbb, uint32_t hs, uint32_t h, uint32_t lane, bool active,
-                                             uint32_t i)
+                                             uint32_t fbb, uint32_t hs, uint32_t rb, uint32_t radj, uint32_t h,
+                                             uint32_t lane, bool active, uint32_t i)
 {
     reinterpret_cast<uint8_t *>(&sh.stage[h][0])[kLanes * i + lane] = (uint8_t)s;
     const uint8_t *fbt = reinterpret_cast<const uint8_t *>(&sh.fb[0][0]);
@@ -560,21 +570,20 @@ __device__ __forceinline__ void dec_step_sym(uint32_t &x, uint32_t &s, uint32_t 
     // rank within the own half (see dec_step)
     const uint32_t lo = __builtin_amdgcn_mbcnt_lo(ml, rpos);
     const uint32_t hi = __builtin_amdgcn_mbcnt_hi(mh, rpos);
-    const uint32_t widx = h ? hi : lo;  // < Sh::kRingWords + 64
+    const uint32_t widx = h ? hi : lo;  // rb + (a ring index below Sh::kRingWords + 64)
     const uint32_t half = (uint32_t)(m >> hs);
-    const uint32_t w = reinterpret_cast<const uint16_t *>(&sh.ring[h][0])[widx];
     // byte offsets from the start of the slot tables (sym[0])
     const uint8_t *base = reinterpret_cast<const uint8_t *>(&sh.sym[0][0]);
-    const uint32_t at_ring = (uint32_t)(reinterpret_cast<const uint8_t *>(&sh.rsym[h][0]) - base) + widx;
+    const uint32_t w = *reinterpret_cast<const uint16_t *>(base + (2 * widx + radj));
     const uint32_t at_slot = (xd & (kM - 1)) | sb;
-    uint32_t sn = base[need ? at_ring : at_slot];
+    uint32_t sn = base[need ? widx : at_slot];
     // the next step's stage store must not see the byte itself: the load
     // would then be any-extending and the (b, f) address would need a mask
     asm("" : "+v"(sn));
     const uint32_t sel = need ? 0x05040100u : 0x07060504u;
     const uint32_t xn = __builtin_amdgcn_perm(xd, w, sel);
     rpos += __popc(half);
-    if (i % Sh::R::kWrap == Sh::R::kWrap - 1) rpos &= Sh::kRingWords - 1;
+    if (i % Sh::R::kWrap == Sh::R::kWrap - 1) rpos = (rpos & (Sh::kRingWords - 1)) | rb;
     asm volatile("" : "+v"(rpos));
     if (!CHECK || active) {
         x = xn;
@@ -855,37 +864,52 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         // scratch for the list of present symbols (256 dwords per half): the
         // ring's space, filled only after the table is built
         uint32_t *fbtmp, *list;
-        if constexpr (kL1) static_assert(sizeof(sh.ring2) >= 512 * 4, "list scratch");
-        else static_assert(sizeof(Sh) - offsetof(Sh, ring) >= 256 * 4 * kH, "list scratch");
         if constexpr (kL1) {
+            static_assert(sizeof(sh.ring2) >= 512 * 4, "list scratch");
             fbtmp = &sh.fbtmp[h][0];
             list = reinterpret_cast<uint32_t *>(&sh.ring2[0][0]) + 256;
+        } else if constexpr (kSym) {
+            static_assert(sizeof(typename Sh::Half) >= 256 * 4, "list scratch");
+            fbtmp = &sh.fb[h][0];
+            list = reinterpret_cast<uint32_t *>(&sh.hr[h]);
         } else {
+            static_assert(sizeof(Sh) - offsetof(Sh, ring) >= 256 * 4 * kH, "list scratch");
             fbtmp = &sh.fb[h][0];
             list = &sh.ring[0][0] + 256 * h;
         }
         build_table<kL1>(sh, h, lane, f, incl - local, fbtmp, list);
     }
-    // the halves' table offsets (4096 h, 1024 h) and 32 h, held opaque
-    uint32_t b0 = h, b1 = 0, hs = 32 * h;
+    // the halves' table offsets (4096 h, 1024 h) and 32 h, held opaque;
+    // symbol-carrying ring: the cursor's offset rb (the half's ring symbols
+    // from sym[0]) and the ring words' address adjustment
+    uint32_t b0 = h, b1 = 0, hs = 32 * h, rb = 0, radj = 0;
     if constexpr (!kL1) {
         b0 = h << 12;
         b1 = h << 10;
     }
-    asm volatile("" : "+v"(b0), "+v"(b1), "+v"(hs));
+    if constexpr (kSym) {
+        constexpr uint32_t rs0 = (uint32_t)(offsetof(Sh, hr) + offsetof(typename Sh::Half, rsym));
+        constexpr uint32_t rw0 = (uint32_t)(offsetof(Sh, hr) + offsetof(typename Sh::Half, ring));
+        constexpr uint32_t hstep = (uint32_t)sizeof(typename Sh::Half);
+        static_assert(offsetof(Sh, sym) == 0 && rs0 % 256 == 0 && hstep % 256 == 0, "ring symbol offsets");
+        rb = rs0 + hstep * h;
+        radj = rw0 + hstep * h - 2 * rb;  // modulo 2^32
+    }
+    asm volatile("" : "+v"(b0), "+v"(b1), "+v"(hs), "+v"(rb), "+v"(radj));
     // the wide table's refills also write the slot entries of the words they land
     // (and the symbol-carrying ring the symbols of theirs)
     auto commit = [&](Refill &r) {
         if constexpr (kL1) refill_commit<R>(cs, r, sh.ring2[0], sh.tab[0]);
         else if constexpr (kSym)
-            refill_commit<R>(cs, r, sh.ring[h], sh.rsym[h], reinterpret_cast<const uint8_t *>(&sh.sym[0][0]), b0);
+            refill_commit<R>(cs, r, sh.hr[h].ring, sh.hr[h].rsym, reinterpret_cast<const uint8_t *>(&sh.sym[0][0]),
+                             b0);
         else refill_commit<R>(cs, r, sh.ring[h]);
     };
     auto sync_fill = [&]() {
         if constexpr (kL1) refill_sync<R>(cs, lane, ok, sh.ring2[0], (const uint32_t *)sh.tab[0]);
         else if constexpr (kSym)
-            refill_sync<R>(cs, lane, ok, sh.ring[h], sh.rsym[h], reinterpret_cast<const uint8_t *>(&sh.sym[0][0]),
-                           b0);
+            refill_sync<R>(cs, lane, ok, sh.hr[h].ring, sh.hr[h].rsym,
+                           reinterpret_cast<const uint8_t *>(&sh.sym[0][0]), b0);
         else refill_sync<R>(cs, lane, ok, sh.ring[h]);
     };
     __syncthreads();
@@ -916,11 +940,11 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     const uint32_t ng = __builtin_amdgcn_readfirstlane((hi_len + kGroupWords - 1) / kGroupWords);
     const uint32_t nfull = __builtin_amdgcn_readfirstlane(lo_len / kGroupWords);
     using Pre = typename View::Pre;
-    uint32_t rpos = 0;  // cs.ptr modulo the ring size, advanced every step
+    uint32_t rpos = rb;  // cs.ptr modulo the ring size (plus rb), advanced every step
     auto step = [&](auto check_tag, bool active, uint32_t i) {
         constexpr bool CHECK = decltype(check_tag)::value;
         if constexpr (kL1) dec_step_wide<CHECK>(x, e, rpos, sh, b0, lane, active, i);
-        else if constexpr (kSym) dec_step_sym<CHECK>(x, e, rpos, sh, b0, b1, hs, h, lane, active, i);
+        else if constexpr (kSym) dec_step_sym<CHECK>(x, e, rpos, sh, b0, b1, hs, rb, radj, h, lane, active, i);
         else dec_step<CHECK, kH>(x, rpos, sh, b0, b1, hs, h, lane, active, i);
     };
     // Speculation: set when a group consumed a word that had not landed.
@@ -1053,7 +1077,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         commit(q[0]);
         cs.ptr = cs.fill = cs.land = 0;
         cs.fenc = fenc_start<R>(lane);
-        rpos = 0;
+        rpos = rb;
         if (ok) x = reinterpret_cast<const WC_GLOBAL uint32_t *>(cs.base)[lane];
         if constexpr (kL1) e = sh.tab[0][x & (kM - 1)];
         if constexpr (kSym) e = sym_of(sh, x);
