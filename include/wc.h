@@ -272,10 +272,12 @@ wc_status wc_decode_gemm_batch(wc_format format, const wc_segment *h_segs, const
                                const wc_gemm *h_gemm, const wc_gemm *d_gemm, uint32_t m, const wc_buffers *in,
                                uint32_t *d_err, hipStream_t stream);
 
-/* Host-side self check of the exact division by reciprocal that the encoder
- * kernel uses (same inline code, compiled for the CPU): every divisor
- * 1..4096 against boundary and sampled dividends below 2^32.  Returns the
- * number of wrong quotients (0 expected). */
+/* Host-side self check of the exact division by reciprocal and of the
+ * encoder's state update built on it (same inline code, compiled for the
+ * CPU): every divisor 1..4096 against boundary and sampled dividends below
+ * 2^32, and the update x' = 4096 floor(xr / f) + (xr mod f) + b for every
+ * f against boundary and sampled xr in [1, f 2^20).  Returns the number of
+ * wrong results (0 expected). */
 uint64_t wc_check_division(uint32_t samples_per_divisor);
 
 /* Which decoder wc_decode / wc_decode_batch would launch for num_chunks

@@ -244,6 +244,40 @@ inline __host__ __device__ uint32_t div_exact(uint32_t x, uint32_t mp, uint32_t 
     return (t1 + ((x - t1) >> sh1)) >> sh2;
 }
 
+// The encoder's state update for a symbol of frequency f and start b:
+// x' = 4096 floor(xr / f) + (xr mod f) + b = xr + q (4096 - f) + b, for
+// 1 <= xr < f 2^20 (a state is at least 2^16, so even a renormalised xr is
+// at least 1).  q comes from one multiply-high and two right shifts, the
+// first by the constant 1: for f >= 2 the round-up reciprocal's sh1 is 1 and
+// q is the exact quotient; for f = 1 the reciprocal 2^32 - 1 gives
+// q = xr - 1 (exact for xr >= 1), and a start raised by 4095 puts the
+// missing 4095 back.  Packed per symbol as {mp, fm = sh2 | (4096 - f) << 16,
+// bb}: the second shift takes fm's low 5 bits as they stand and the
+// multiply its high half.
+struct EncConst {
+    uint32_t mp, fm, bb;
+};
+
+inline __host__ __device__ EncConst enc_const(uint32_t mp, uint32_t l, uint32_t f, uint32_t b)
+{
+    EncConst c;
+    c.mp = f == 1 ? 0xFFFFFFFFu : mp;
+    c.fm = (l > 1 ? l - 1 : 0u) | (kM - f) << 16;
+    c.bb = f == 1 ? b + (kM - 1) : b;
+    return c;
+}
+
+inline __host__ __device__ uint32_t enc_update(uint32_t xr, uint32_t mp, uint32_t fm, uint32_t bb)
+{
+    const uint32_t t1 = mulhi32(mp, xr);
+    const uint32_t q = (t1 + ((xr - t1) >> 1)) >> (fm & 31u);  // below 2^20
+#if defined(__HIP_DEVICE_COMPILE__)
+    return xr + __umul24(q, fm >> 16) + bb;
+#else
+    return xr + q * (fm >> 16) + bb;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // Wavefront helpers (wave64).
 // ---------------------------------------------------------------------------

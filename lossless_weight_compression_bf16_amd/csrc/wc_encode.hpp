@@ -301,13 +301,13 @@ __global__ __launch_bounds__(256) void k_tensor_table(SegTable st, const unsigne
 
 // ------------------------------------------------------------------ encoder
 
-// Per-symbol encoder constants: reciprocal, renormalisation threshold,
-// (4096 - f) and the two shifts, cumulative start b.
+// Per-symbol encoder constants (enc_const): reciprocal, renormalisation
+// threshold, the second shift and (4096 - f), cumulative start.
 struct EncSym {
     uint32_t mp;
-    uint32_t th;     // x > th  <=>  x >= f * 2^20 (renormalise first)
-    uint32_t fm_sh;  // (4096 - f) | sh1 << 16 | sh2 << 24
-    uint32_t b;
+    uint32_t th;  // x > th  <=>  x >= f * 2^20 (renormalise first)
+    uint32_t fm;  // sh2 | (4096 - f) << 16
+    uint32_t b;   // b, plus 4095 for f = 1
 };
 
 constexpr uint32_t kEncGroup = 8;                  // steps per group: 256 symbols per half
@@ -437,8 +437,7 @@ __device__ __forceinline__ void enc_step(uint32_t &x, uint32_t &p, bool active, 
         if (emit) *reinterpret_cast<WC_GLOBAL uint16_t *>(d.base + off) = (uint16_t)(x & 0xFFFF);
     }
     const uint32_t xr = emit ? x >> 16 : x;
-    const uint32_t q = div_exact(xr, e.mp, (e.fm_sh >> 16) & 0xFF, e.fm_sh >> 24);
-    const uint32_t xn = xr + __umul24(q, e.fm_sh & 0xFFFF) + e.b;
+    const uint32_t xn = enc_update(xr, e.mp, e.fm, e.b);
     if (!CHECK || active) x = xn;
 }
 
@@ -485,11 +484,11 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
             // absent symbols are never encoded; f > 4096 only in a corrupt
             // table, which the normaliser never produces
             const uint32_t fi = f[i] ? (f[i] <= kM ? f[i] : kM) : 1u;
-            const uint32_t l = kDivTable.l[fi];
-            e.mp = kDivTable.mp[fi];
+            const EncConst c = enc_const(kDivTable.mp[fi], kDivTable.l[fi], fi, b);
+            e.mp = c.mp;
             e.th = (fi << 20) - 1u;  // wraps to 0xFFFFFFFF at f = 4096: never renormalise
-            e.fm_sh = (kM - fi) | ((l < 1 ? l : 1u) << 16) | ((l > 1 ? l - 1 : 0u) << 24);
-            e.b = b;
+            e.fm = c.fm;
+            e.b = c.bb;
             enc[h][8 * lane + i] = e;
             b += f[i];
         }

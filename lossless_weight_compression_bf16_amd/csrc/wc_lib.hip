@@ -580,6 +580,22 @@ uint64_t wc_check_division(uint32_t samples_per_divisor)
             check(q * d);
             if (q) check(q * d - 1);
         }
+        // the state update the kernel runs: every xr in [1, d 2^20) it can
+        // see, at the range's ends and sampled, with the start at both ends
+        const EncConst e0 = enc_const(table.mp[d], l, d, 0), e1 = enc_const(table.mp[d], l, d, kM - d);
+        auto check_update = [&](uint32_t xr) {
+            const uint32_t exact = kM * (xr / d) + xr % d;
+            if (enc_update(xr, e0.mp, e0.fm, e0.bb) != exact) bad++;
+            if (enc_update(xr, e1.mp, e1.fm, e1.bb) != exact + (kM - d)) bad++;
+        };
+        const uint32_t xmax = (uint32_t)(((uint64_t)d << 20) - 1);
+        const uint32_t ends[] = {1u, 2u, d - 1 ? d - 1 : 1u, d, d + 1, 65535u, 65536u, xmax, xmax - 1, xmax - d};
+        for (uint32_t x : ends)
+            if (x >= 1 && x <= xmax) check_update(x);
+        for (uint32_t i = 0; i < samples_per_divisor; i++) {
+            rng = rng * 6364136223846793005ull + 1442695040888963407ull;
+            check_update(1u + (uint32_t)((rng >> 24) % xmax));
+        }
     }
     return bad;
 }
