@@ -558,7 +558,7 @@ __device__ __forceinline__ void dec_step(uint32_t &x, uint32_t &rpos, Sh &sh, ui
 template <bool CHECK, typename Sh>
 __device__ __forceinline__ void dec_step_sym(uint32_t &x, uint32_t &s, uint32_t &rpos, Sh &sh, uint32_t sb,
                                              uint32_t fbb, uint32_t hs, uint32_t rb, uint32_t radj, uint32_t h,
-                                             uint32_t lane, bool active, uint32_t i)
+                                             uint32_t lane, uint32_t below, bool active, uint32_t i)
 {
     reinterpret_cast<uint8_t *>(&sh.stage[h][0])[kLanes * i + lane] = (uint8_t)s;
     const uint8_t *fbt = reinterpret_cast<const uint8_t *>(&sh.fb[0][0]);
@@ -566,12 +566,12 @@ __device__ __forceinline__ void dec_step_sym(uint32_t &x, uint32_t &s, uint32_t 
     const uint32_t xd = (uint32_t)__mul24((int32_t)fb >> 16, (int32_t)(x >> kScaleBits)) + (x - (fb & 0xFFFF));
     const bool need = (!CHECK || active) && xd < kL;
     const uint64_t m = __ballot(need);
-    const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
-    // rank within the own half (see dec_step)
-    const uint32_t lo = __builtin_amdgcn_mbcnt_lo(ml, rpos);
-    const uint32_t hi = __builtin_amdgcn_mbcnt_hi(mh, rpos);
-    const uint32_t widx = h ? hi : lo;  // rb + (a ring index below Sh::kRingWords + 64)
+    // the own half's mask (one 64-bit shift by 32 h); the lane's rank among
+    // the half's renormalising lanes is the count of its bits below the lane
+    // (below = 2^lane - 1, one AND and one bit count instead of two mbcnt
+    // and a per-half select), and the same mask's count advances the cursor
     const uint32_t half = (uint32_t)(m >> hs);
+    const uint32_t widx = __popc(half & below) + rpos;  // rb + (a ring index below Sh::kRingWords + 64)
     // byte offsets from the start of the slot tables (sym[0])
     const uint8_t *base = reinterpret_cast<const uint8_t *>(&sh.sym[0][0]);
     const uint32_t w = *reinterpret_cast<const uint16_t *>(base + (2 * widx + radj));
@@ -896,6 +896,8 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
         radj = rw0 + hstep * h - 2 * rb;  // modulo 2^32
     }
     asm volatile("" : "+v"(b0), "+v"(b1), "+v"(hs), "+v"(rb), "+v"(radj));
+    uint32_t below = (1u << lane) - 1;  // lanes of the own half below this one
+    if constexpr (kSym) asm volatile("" : "+v"(below));
     // the wide table's refills also write the slot entries of the words they land
     // (and the symbol-carrying ring the symbols of theirs)
     auto commit = [&](Refill &r) {
@@ -944,7 +946,7 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     auto step = [&](auto check_tag, bool active, uint32_t i) {
         constexpr bool CHECK = decltype(check_tag)::value;
         if constexpr (kL1) dec_step_wide<CHECK>(x, e, rpos, sh, b0, lane, active, i);
-        else if constexpr (kSym) dec_step_sym<CHECK>(x, e, rpos, sh, b0, b1, hs, rb, radj, h, lane, active, i);
+        else if constexpr (kSym) dec_step_sym<CHECK>(x, e, rpos, sh, b0, b1, hs, rb, radj, h, lane, below, active, i);
         else dec_step<CHECK, kH>(x, rpos, sh, b0, b1, hs, h, lane, active, i);
     };
     // Speculation: set when a group consumed a word that had not landed.
