@@ -359,7 +359,10 @@ struct RawView16 {  // the 16-bit layouts
         o.y = B::from_coded(__builtin_amdgcn_perm(sym.x, p.v.x, 0x07030602u));
         o.z = B::from_coded(__builtin_amdgcn_perm(sym.y, p.v.y, 0x05010400u));
         o.w = B::from_coded(__builtin_amdgcn_perm(sym.y, p.v.y, 0x07030602u));
-        *reinterpret_cast<WC_GLOBAL u32x4 *>(out + e) = o;
+        // a streaming store (nt): the output is written once and not read
+        // back here, so it need not displace the payload and raw lines in
+        // the caches (measured about 1% faster on multi-GB weight sets)
+        __builtin_nontemporal_store(o, reinterpret_cast<WC_GLOBAL u32x4 *>(out + e));
     }
     // tail chunks: only elements below len exist
     __device__ Pre fetch_checked(uint32_t e, uint32_t len) const

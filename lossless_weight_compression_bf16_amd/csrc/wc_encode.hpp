@@ -610,8 +610,12 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
                 using B = Bits16<DT>;
                 const uint32_t a0 = B::to_coded(d.v.x), a1 = B::to_coded(d.v.y);
                 const uint32_t a2 = B::to_coded(d.v.z), a3 = B::to_coded(d.v.w);
-                reinterpret_cast<WC_GLOBAL u32x2 *>(lo + kEncBlk * gs)[lane] =
-                    u32x2{__builtin_amdgcn_perm(a1, a0, 0x06040200u), __builtin_amdgcn_perm(a3, a2, 0x06040200u)};
+                // a streaming store (nt): the raw plane is not read again by
+                // the encode (the coded words' partial lines keep the default
+                // policy: written through as nt they cost far more)
+                __builtin_nontemporal_store(
+                    u32x2{__builtin_amdgcn_perm(a1, a0, 0x06040200u), __builtin_amdgcn_perm(a3, a2, 0x06040200u)},
+                    reinterpret_cast<WC_GLOBAL u32x2 *>(lo + kEncBlk * gs) + lane);
             }
             const uint2 b = WideView<DT>::bytes(d);
             wave_lds_order();
