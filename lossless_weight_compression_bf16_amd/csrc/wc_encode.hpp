@@ -513,13 +513,16 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
 
     // Word staging (STAGE).  Steps write their words to the half's LDS
     // ring; words [p_w, wf) are in the ring only.  At the end of a group,
-    // wt = p_w rounded up to even marks the dwords that are complete; the
-    // next group reads them from the ring before its steps (wflush_ld) and
-    // writes them to the slot after them (wflush_st), so LDS latency hides
-    // behind the steps.  A group writes at most kGroupMaxWords = 192 words
-    // per half, so the ring holds at most 193 words when it is read (three
-    // reads per lane cover the 96 dwords), and the reads come before (in LDS
-    // order) the writes that reuse their places.  Where the grid is too
+    // wt = p_w rounded up to a multiple of 64 marks the whole 128-byte lines
+    // of the slot that are complete (word w is at byte 128 + 2 w of the
+    // half's slot, and slots are multiples of 128 bytes); the next group
+    // reads them from the ring before its steps (wflush_ld) and writes them
+    // to the slot after them (wflush_st), so LDS latency hides behind the
+    // steps and every store covers whole lines.  A group writes at most
+    // kGroupMaxWords = 192 words per half and fewer than 64 wait below a
+    // line, so the ring holds at most 255 words, a flush moves at most 192
+    // (three reads per lane cover the 96 dwords), and the reads come before
+    // (in LDS order) the writes that reuse their places.  Where the grid is too
     // small to fill the machine, each wavefront's instruction count sets the
     // time and the words go straight to the slot instead.
     WordDst wd{wbase, woff, reinterpret_cast<uint16_t *>(&ewring[0]), h << 8};
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
                 if (lane + kLanes * r < n)
                     *reinterpret_cast<WC_GLOBAL uint32_t *>(wbase + (off + 4 * kLanes * r)) = fv[r];
             wf = wt;
-            wt = (p_w + 1) & ~1u;
+            wt = (p_w + 63) & ~63u;
         }
     };
 
@@ -663,7 +666,7 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
         }
     }
 
-    // the words still in the ring (at most 193), from the dword holding
+    // the words still in the ring (at most 255), from the dword holding
     // word p_w (with an odd p_w its other half is not part of the stream)
     if constexpr (STAGE) {
         wt = p_w & ~1u;
