@@ -453,7 +453,7 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     __shared__ EncSym enc[2][256];
     __shared__ uint32_t estage[2][kEncBlk / 4];  // one full group's coded bytes per half
     // per half: a ring of 256 words (word staging, below)
-    __shared__ uint32_t ewring[STAGE ? 2 * 128 : 1];
+    __shared__ alignas(16) uint32_t ewring[STAGE ? 2 * 128 : 4];
     const uint32_t lane = threadIdx.x & 31, h = threadIdx.x >> 5;
     // with an odd chunk count the last wavefront's second half shadows the
     // first half's chunk: it runs the same unchecked code but stores nothing
@@ -521,35 +521,32 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     // steps and every store covers whole lines.  A group writes at most
     // kGroupMaxWords = 192 words per half and fewer than 64 wait below a
     // line, so the ring holds at most 255 words, a flush moves at most 192
-    // (three reads per lane cover the 96 dwords), and the reads come before
-    // (in LDS order) the writes that reuse their places.  Where the grid is too
+    // (one 16-byte read per lane of the first 24 covers the 96 dwords), and
+    // the reads come before (in LDS order) the writes that reuse their places.  Where the grid is too
     // small to fill the machine, each wavefront's instruction count sets the
     // time and the words go straight to the slot instead.
     WordDst wd{wbase, woff, reinterpret_cast<uint16_t *>(&ewring[0]), h << 8};
     asm volatile("" : "+v"(wd.hsel));
     const uint32_t *const hring = &ewring[STAGE ? 128 * h : 0];
     uint32_t wf = kMaxWords, wt = kMaxWords;
-    constexpr uint32_t kFlushRounds = kGroupMaxWords / 2 / kLanes;
-    uint32_t fv[kFlushRounds];
+    // a flush moves at most kGroupMaxWords / 2 = 96 dwords: four per lane
+    // of the first 24 lanes, one 16-byte LDS read and one 16-byte store each
+    u32x4 fv = {0u, 0u, 0u, 0u};
     auto wflush_ld = [&]() {
         if constexpr (STAGE) {
-            // dwords wt / 2 + lane + 32 r of the half; wt is even, so none
-            // straddles the ring's end
+            // dwords wt / 2 + 4 lane .. + 3 of the half; wt is a multiple of
+            // 64, so no 16-byte read straddles the ring's end
             wave_lds_order();
-#pragma unroll
-            for (uint32_t r = 0; r < kFlushRounds; r++) fv[r] = hring[((wt >> 1) + lane + kLanes * r) & 127u];
+            fv = reinterpret_cast<const u32x4 *>(hring)[((wt >> 3) + lane) & 31u];
         }
     };
     auto wflush_st = [&]() {
         if constexpr (STAGE) {
-            // the complete dwords, to the half's word area at a 32-bit offset
+            // the complete lines, to the half's word area at a 32-bit offset
             // from the uniform base
             const uint32_t n = (wf - wt) >> 1;
-            const uint32_t off = woff + 2 * wt + 4 * lane;
-#pragma unroll
-            for (uint32_t r = 0; r < kFlushRounds; r++)
-                if (lane + kLanes * r < n)
-                    *reinterpret_cast<WC_GLOBAL uint32_t *>(wbase + (off + 4 * kLanes * r)) = fv[r];
+            const uint32_t off = woff + 2 * wt + 16 * lane;
+            if (4 * lane < n) *reinterpret_cast<WC_GLOBAL u32x4 *>(wbase + off) = fv;
             wf = wt;
             wt = (p_w + 63) & ~63u;
         }
