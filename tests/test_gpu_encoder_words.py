@@ -2,15 +2,17 @@
 
 WC_ENC_WORDS_DIRECT writes each step's renormalisation words straight to the
 chunk's scratch slot; WC_ENC_WORDS_STAGED collects them in a 256-word LDS
-ring per chunk and writes whole dwords once per 256 symbols.  Both must give
+ring per chunk and, once per 256 symbols, writes the whole 128-byte lines of
+the slot they complete (up to 63 words wait below a line).  Both must give
 the oracle's tables, seek table, payload and raw planes on: sizes with
 partial groups and ragged last chunks, odd chunk counts (a wavefront whose
 second half only shadows the first), every layout with and without options,
 ragged batches, uniform coded bytes (about 128 words per group and half:
 two flush rounds) and chunks at the most words a group can take (192 per
 half: every lane renormalising at 6 of its 8 steps, the three-in-a-row
-bound's maximum), where the ring is fullest and the flush takes all three
-rounds.  The automatic choice follows the CU count of the stream's device.
+bound's maximum), where a flush moves the most words, and dense groups among
+groups of weights, where up to 255 words are live in the ring.  The automatic
+choice follows the CU count of the stream's device.
 All calls go through the C ABI.
 """
 import sys
@@ -146,6 +148,23 @@ def test_most_words_per_group(dev, oracle_lib, form):
     _one("bf16", 0, x, dev, oracle_lib, f"{form} dense groups")
     # the same chunks with the tensor's table, raw storage allowed
     _one("bf16", TT | RF, x, dev, oracle_lib, f"{form} dense groups, tensor table + raw fallback")
+
+
+def test_dense_groups_among_weights(dev, oracle_lib, form):
+    """Groups of one of each coded byte (about 160 words per group and half
+    with their chunk's table) at random places among groups of weights (about
+    45 words), so the words left below a 128-byte line before a dense group
+    take many values and the staged ring holds up to 255 live words."""
+    g = np.random.default_rng(47)
+    parts = []
+    for c in range(6):
+        w = _bits16("bf16", 65536, 50 + c)
+        for q in g.choice(256, 24, replace=False):
+            lo = w[256 * q:256 * q + 256] & 0xFF
+            w[256 * q:256 * q + 256] = (g.permutation(np.arange(256, dtype=np.uint16)) << 8) | lo
+        parts.append(w)
+    x = np.concatenate(parts + [_bits16("bf16", 30001, 57)])
+    _one("bf16", 0, x, dev, oracle_lib, f"{form} dense groups among weights")
 
 
 def test_uniform_coded_bytes(dev, oracle_lib, form):
