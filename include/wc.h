@@ -296,8 +296,9 @@ wc_status wc_decode_variant(wc_format format, uint64_t num_chunks, uint64_t n, u
  * words go straight to the chunk's scratch slot as 2-byte stores (fewest
  * instructions per step: fastest where the grid does not fill the GPU).
  * WC_ENC_WORDS_STAGED: they go to a 256-word LDS ring per chunk and reach
- * the slot as whole dwords once per 256 symbols (fewer memory operations:
- * fastest where the grid fills every SIMD).  WC_ENC_WORDS_AUTO (the
+ * the slot as whole 128-byte lines, with 16-byte stores, once per 256
+ * symbols (fewer memory operations: fastest where the grid fills every
+ * SIMD).  WC_ENC_WORDS_AUTO (the
  * default): for the 16-bit layouts (BF16, FP16 and their reorders) staged
  * when the encoder's grid has at least 16 wavefronts (two chunks each) per
  * compute unit of the stream's device, else direct; FP32 and FP8 direct. */

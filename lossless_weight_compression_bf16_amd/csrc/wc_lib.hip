@@ -129,8 +129,9 @@ bool stream_device(hipStream_t stream, int *dev)
 // Encoder word stores.  For the 16-bit layouts a grid that fills every
 // SIMD's wavefront slots at least once (k_encode holds 4 wavefronts per
 // SIMD, 16 per CU) is bound by the memory pipeline, and staging the words
-// in LDS to write whole dwords once per group is faster (MoE experts set:
-// BF16 8.66 -> 7.99 ms, FP16 9.49 -> 8.87 ms); a smaller grid is bound by
+// in LDS to write them once per group is faster (MoE experts set, dword
+// flushes: BF16 8.66 -> 7.99 ms, FP16 9.49 -> 8.87 ms; now whole 128-byte
+// lines with 16-byte stores); a smaller grid is bound by
 // each wavefront's serial instruction stream, and the direct 2-byte stores,
 // with fewer instructions per step, are faster there (up to 24%).  FP8
 // (half the input bytes per symbol) is faster direct at any size (6.0
