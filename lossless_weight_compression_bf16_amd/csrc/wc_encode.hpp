@@ -408,7 +408,8 @@ using WideView = typename std::conditional<
 // to the slot (STAGE false: a wave-uniform base plus a 32-bit lane offset,
 // woff being the half's word area relative to that base) or to the half's
 // LDS ring (STAGE true: 256 words per half, word w at w mod 256,
-// hsel = 256 h), from which whole dwords go to the slot once a group is done.
+// hsel = 256 h), from which the completed 128-byte lines of the slot are
+// written once a group is done.
 struct WordDst {
     WC_GLOBAL uint8_t *base;
     uint32_t woff;
