@@ -422,7 +422,8 @@ struct RawView8 {
     }
     __device__ void flush(uint32_t e, uint2 sym, const Pre &p) const
     {
-        *reinterpret_cast<WC_GLOBAL u32x2 *>(out + e) = join(sym, p.v);
+        // a streaming store (nt), like the 16-bit layouts' output
+        __builtin_nontemporal_store(join(sym, p.v), reinterpret_cast<WC_GLOBAL u32x2 *>(out + e));
     }
     // tail chunks: only elements below len exist
     __device__ Pre fetch_checked(uint32_t e, uint32_t len) const
