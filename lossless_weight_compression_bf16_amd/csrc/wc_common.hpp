@@ -281,6 +281,17 @@ inline __host__ __device__ uint32_t enc_update(uint32_t xr, uint32_t mp, uint32_
 // ---------------------------------------------------------------------------
 // Wavefront helpers (wave64).
 // ---------------------------------------------------------------------------
+// The GPU hands consecutive workgroups to its 8 XCDs in turn; this maps
+// block b to slot start(b mod 8) + b / 8, where the grid's slots are cut
+// into 8 consecutive ranges (the first gridDim.x mod 8 one longer), so each
+// XCD works through one contiguous range.  A bijection on [0, gridDim.x) for
+// any grid size: results never depend on the dispatch order.
+__device__ inline uint32_t xcd_block()
+{
+    const uint32_t b = blockIdx.x, G = gridDim.x, per = G >> 3, rem = G & 7, xc = b & 7, i = b >> 3;
+    return (xc < rem ? xc * (per + 1) : rem * (per + 1) + (xc - rem) * per) + i;
+}
+
 __device__ inline uint32_t lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 __device__ inline uint32_t wave_sum(uint32_t v)

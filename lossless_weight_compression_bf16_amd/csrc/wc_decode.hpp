@@ -797,16 +797,8 @@ __device__ __forceinline__ void decode_wave(SegTable st, const uint16_t *__restr
     constexpr uint32_t D = R::kDepth;
     __shared__ Sh sh;
     const uint32_t lane = threadIdx.x & 31, h = kH == 1 ? 0u : threadIdx.x >> 5;
-    // The GPU hands consecutive workgroups to its 8 XCDs in turn; block b is
-    // given chunk-pair slot bid so that each XCD decodes one contiguous range
-    // of the set (a bijection on [0, gridDim.x) for any grid size, so the
-    // result never depends on the dispatch order; measured 0.5-0.9% faster
-    // on multi-GB sets than the plain order)
-    uint32_t bid;
-    {
-        const uint32_t b = blockIdx.x, G = gridDim.x, per = G >> 3, rem = G & 7, xc = b & 7, i = b >> 3;
-        bid = (xc < rem ? xc * (per + 1) : rem * (per + 1) + (xc - rem) * per) + i;
-    }
+    // each XCD decodes one contiguous range of chunk pairs (xcd_block)
+    const uint32_t bid = xcd_block();
     const uint64_t k_own = (uint64_t)kH * bid + h;
     const bool real = k_own < total_chunks;
     const uint64_t k = real ? k_own : k_own - 1;

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void k_split_hist(SegTable st, uint8_t *__rest
     __shared__ uint32_t keys[256];
     using B = Bits16<DT>;
 
-    const uint64_t k = blockIdx.x;
+    const uint64_t k = xcd_block();  // each XCD one contiguous range of chunks
     uint32_t sidx;
     const wc_segment sg = find_segment(st, k, &sidx);
     const uint64_t start = (k - sg.chunk_base) * kChunk;
@@ -458,7 +458,8 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     const uint32_t lane = threadIdx.x & 31, h = threadIdx.x >> 5;
     // with an odd chunk count the last wavefront's second half shadows the
     // first half's chunk: it runs the same unchecked code but stores nothing
-    const uint64_t k_own = 2ull * blockIdx.x + h;
+    const uint32_t bid = xcd_block();  // each XCD one contiguous range of chunk pairs
+    const uint64_t k_own = 2ull * bid + h;
     const bool real = k_own < total_chunks;
     const uint64_t k = real ? k_own : k_own - 1;
 
@@ -496,11 +497,11 @@ __global__ __launch_bounds__(64) void k_encode(SegTable st, const uint16_t *__re
     }
     __syncthreads();
 
-    // Half h writes slot 2 blockIdx + h, so a shadow half (only ever the
+    // Half h writes slot 2 bid + h, so a shadow half (only ever the
     // second half of the last wavefront) writes the spare slot after the
     // last chunk's.  Word stores address a wave-uniform base plus a lane
     // offset: the half's words start 128 bytes into its slot.
-    WC_GLOBAL uint8_t *const wbase = gptr(slots) + 2ull * blockIdx.x * kSlotBytes;
+    WC_GLOBAL uint8_t *const wbase = gptr(slots) + 2ull * bid * kSlotBytes;
     WC_GLOBAL uint8_t *slot = wbase + h * kSlotBytes;
     uint32_t woff = h * kSlotBytes + 128, hs = 32 * h;
     asm volatile("" : "+v"(woff), "+v"(hs));
@@ -839,7 +840,7 @@ __global__ __launch_bounds__(256) void k_compact(const uint8_t *__restrict__ slo
                                                  const uint64_t *__restrict__ seek,
                                                  uint8_t *__restrict__ payload, uint64_t capacity)
 {
-    const uint64_t k = blockIdx.x;
+    const uint64_t k = xcd_block();  // each XCD one contiguous range of chunks
     compact_chunk(slots, k, meta[k], seek[k], payload, capacity);
 }
 
